@@ -79,6 +79,7 @@ def lib():
             "cgo_tables_size": (SZ, [C.POINTER(cgo_params)]),
             "cgo_build_tables": (I, [C.POINTER(cgo_params), P, P, I, P, SZ, C.POINTER(SZ), P]),
             "cgo_fnv1a64": (U64, [P, SZ]),
+            "cgo_tables_id": (U64, [P, SZ]),
             "cgo_chunk_geometry": (I, [P, SZ, I, C.POINTER(C.c_int32), C.POINTER(C.c_int32),
                                        C.POINTER(C.c_int32)]),
             "cgo_encode_bound": (SZ, [P, SZ, I]),
@@ -220,6 +221,11 @@ def build_tables(p: cgo_params, k: np.ndarray, v: np.ndarray, threads: Optional[
 def fnv1a64(data: bytes) -> int:
     buf = np.frombuffer(data, np.uint8)
     return int(lib().cgo_fnv1a64(_ptr(buf), buf.size))
+
+
+def tables_id(data: bytes) -> int:
+    buf = np.frombuffer(data, np.uint8)
+    return int(lib().cgo_tables_id(_ptr(buf), buf.size))
 
 
 def chunk_geometry(tables: bytes, chunk: int):

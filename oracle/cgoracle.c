@@ -316,6 +316,22 @@ uint64_t cgo_fnv1a64(const uint8_t* data, size_t n) {
   return h;
 }
 
+/* Identity of a serialized table set, stamped into every blob: FNV-1a-64 of
+ * the little-endian FNV-1a-64 digests of its consecutive 64 KiB blocks (the
+ * last block may be shorter). */
+uint64_t cgo_tables_id(const uint8_t* data, size_t n) {
+  size_t nblk = (n + 65535) / 65536;
+  uint8_t* d = (uint8_t*)malloc(8 * (nblk ? nblk : 1));
+  for (size_t b = 0; b < nblk; b++) {
+    size_t len = (n - 65536 * b < 65536) ? n - 65536 * b : 65536;
+    uint64_t h = cgo_fnv1a64(data + 65536 * b, len);
+    for (int j = 0; j < 8; j++) d[8 * b + j] = (uint8_t)(h >> (8 * j));
+  }
+  uint64_t id = cgo_fnv1a64(d, 8 * nblk);
+  free(d);
+  return id;
+}
+
 static int nq_of(uint32_t mask) { return (mask & 1) + ((mask >> 1) & 1) + ((mask >> 2) & 1); }
 
 static int check_params(const cgo_params* p) {
@@ -390,7 +406,7 @@ static int parse_tables(const uint8_t* t, size_t len, tabview* tv) {
     tv->inv_step[k] = q; q += 4 * tv->n;
     tv->freq[k] = q; q += 2 * NSYM * tv->n;
   }
-  tv->id = cgo_fnv1a64(t, len);
+  tv->id = cgo_tables_id(t, len);
   return OK;
 }
 

@@ -62,6 +62,7 @@ int cgo_build_tables(const cgo_params* p, const uint16_t* k, const uint16_t* v,
                      int nthreads, uint8_t* out, size_t cap, size_t* len,
                      uint32_t* counts_out);
 uint64_t cgo_fnv1a64(const uint8_t* data, size_t n);
+uint64_t cgo_tables_id(const uint8_t* data, size_t n);
 
 /* chunks */
 int cgo_chunk_geometry(const uint8_t* tables, size_t tlen, int chunk, int32_t* t0,

@@ -178,7 +178,7 @@ def test_reencoding_the_decoded_tensor_is_idempotent(oracle_lib, coded):
 
 def test_blob_layout(oracle_lib, coded):
     w, k, v, t, blobs = coded
-    tid = oracle_lib.fnv1a64(t)
+    tid = oracle_lib.tables_id(t)
     for (ch, q), b in blobs.items():
         bv = oracle_lib.blob_view(b)
         h = bv.header

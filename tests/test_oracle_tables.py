@@ -159,3 +159,17 @@ def test_bad_params_are_rejected(oracle_lib):
         p = oracle_lib.make_params(**{**good, **bad})
         with pytest.raises(oracle_lib.OracleError):
             oracle_lib.build_tables(p, k, k)
+
+
+def test_fnv_and_tables_id(oracle_lib):
+    # FNV-1a-64 reference values: empty input is the offset basis; "a" and "foobar"
+    # are the published test vectors of the FNV specification
+    assert oracle_lib.fnv1a64(b"") == 0xcbf29ce484222325
+    assert oracle_lib.fnv1a64(b"a") == 0xaf63dc4c8601ec8c
+    assert oracle_lib.fnv1a64(b"foobar") == 0x85944171f73967e8
+    rng = np.random.default_rng(2)
+    for n in (1, 65535, 65536, 65537, 300000):
+        d = rng.integers(0, 256, n, dtype=np.uint8).tobytes()
+        blocks = [d[i:i + 65536] for i in range(0, n, 65536)]
+        digest = b"".join(oracle_lib.fnv1a64(b).to_bytes(8, "little") for b in blocks)
+        assert oracle_lib.tables_id(d) == oracle_lib.fnv1a64(digest)
