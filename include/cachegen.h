@@ -1,0 +1,166 @@
+/*
+ * cachegen.h — C ABI of the MI355X (gfx950) KV-cache codec library libcachegen.so.
+ *
+ * The codec follows CacheGen (arXiv 2310.07240):
+ *   - the encoder turns a KV cache into a compact bitstream
+ *     (gptget abstract; CacheGen blog, section 2.1 "compress_kv_cache(kv_tensor)
+ *     -> bitstream");
+ *   - tokens are coded as deltas against an 8-bit anchor token, one anchor per
+ *     group of ten (CacheGen blog, section 2.1 pseudocode; sciencestack TL;DR
+ *     "token-wise locality");
+ *   - the delta step depends on the layer group, 0.5 / 1.0 / 1.5 channel stds for
+ *     shallow / medium / deep layers (CacheGen blog, sections 1 and 2.1;
+ *     sciencestack "layer-sensitive quantization");
+ *   - the symbols are arithmetic-coded with probability tables kept per
+ *     (layer, channel) (CacheGen blog, section 1; sciencestack Figure 5);
+ *   - the context is cut into 1.5K-token chunks, each pre-encoded at quality
+ *     H, M or L, and decoded on the GPU, pipelined with its transfer
+ *     (CacheGen blog, section 2.2; gptget 方法详解).
+ *
+ * Tensors: K and V are each [layers][tokens][channels] IEEE binary16, contiguous,
+ * channels fastest, in device memory.
+ *
+ * Memory ownership: every pointer argument is owned by the caller, except the
+ * cg_tables handle, which the library allocates (device copies of the tables,
+ * encode scratch) and cg_tables_free releases.  Device buffers passed to an
+ * *_async / streamed call must stay valid until the stream has executed the work.
+ *
+ * Streams: a `void* stream` is a hipStream_t (NULL = the legacy default stream).
+ * A handle is used on the device that built or deserialized it; the library
+ * switches to that device for the call and restores the caller's device.
+ *
+ * Errors: every int-returning call returns CG_OK (0) or a negative CG_E_* code
+ * and never aborts; cg_last_error() gives the message of the calling thread's
+ * last failure.  Arguments are validated before any GPU work is enqueued.
+ */
+#ifndef CACHEGEN_H
+#define CACHEGEN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  CG_OK = 0,
+  CG_E_INVAL = -1,    /* bad argument, shape or parameter; non-finite input */
+  CG_E_NOMEM = -2,    /* device or host allocation failed */
+  CG_E_HIP = -3,      /* HIP runtime error (message in cg_last_error) */
+  CG_E_CORRUPT = -4,  /* a blob failed validation while decoding */
+  CG_E_CAPACITY = -5, /* output buffer too small */
+  CG_E_MISMATCH = -6  /* blob made for other tables, or quality not in the tables */
+};
+
+enum { CG_Q_H = 0, CG_Q_M = 1, CG_Q_L = 2 }; /* quality levels (CacheGen blog 2.2) */
+
+/* Codec parameters.  Groups restart at every chunk; the first token of a group
+ * is its anchor.  Layer l uses layer_step[g] where g is the first group with
+ * l < layer_group_end[g]; quality q multiplies the step by quality_mult[q]. */
+typedef struct {
+  int32_t layers, tokens, channels; /* each of K and V is [layers][tokens][channels] */
+  int32_t chunk_tokens;             /* 1 .. 65536 (1536 in the pages' setting) */
+  int32_t group_tokens;             /* 1 .. chunk_tokens (10 in the pages' setting) */
+  int32_t n_layer_groups;           /* 1 .. 3 */
+  int32_t layer_group_end[3];       /* exclusive ends, increasing, last == layers */
+  float layer_step[3];              /* delta step per layer group, channel-std units */
+  float quality_mult[3];            /* step multiplier of H, M, L */
+  uint32_t quality_mask;            /* bit q set: build tables for quality q */
+} cg_params;
+
+/* Header fields of one chunk blob, read from host memory by cg_chunk_info_parse. */
+typedef struct {
+  int32_t layers, channels, total_tokens;
+  int32_t token_offset;  /* first token of the chunk in the [tokens] axis */
+  int32_t chunk_tokens;  /* tokens in this chunk (the last chunk may be short) */
+  int32_t group_tokens, n_groups, quality;
+  uint32_t payload_words;
+  uint32_t reserved;
+  uint64_t tables_id;    /* identity of the tables the blob was coded with */
+  uint64_t blob_bytes;   /* total size of the blob */
+} cg_chunk_info;
+
+typedef struct cg_tables cg_tables; /* opaque, library-owned */
+
+/* Builds the per-(kv, layer, channel) tables from the K/V pair they will code:
+ * channel statistics (exact integer moments), anchor scales, delta steps, and,
+ * for each quality in quality_mask, the frequency table of the delta symbols
+ * over every chunk (CacheGen blog, section 1: symbol probabilities counted per
+ * layer-channel combination).  k_dev, v_dev: device fp16 [layers][tokens][channels].
+ * Runs on `stream`, then waits for it.  Non-finite input gives CG_E_INVAL.
+ * On success *out receives a new handle. */
+int cg_build_tables(const cg_params* params, const void* k_dev, const void* v_dev,
+                    void* stream, cg_tables** out);
+
+/* Releases a handle and its device memory (NULL is allowed).  The caller makes
+ * sure no enqueued work still uses it. */
+void cg_tables_free(cg_tables* tables);
+
+/* Serialized tables (the codebook shipped to a decoder).  cg_tables_serialize
+ * copies them into the host buffer `buf` of `cap` bytes; *len receives the size
+ * (call with buf == NULL to query it).  cg_tables_deserialize validates host
+ * bytes and uploads them to the current device. */
+int cg_tables_serialize(const cg_tables* tables, void* buf, size_t cap, size_t* len);
+int cg_tables_deserialize(const void* buf, size_t len, cg_tables** out);
+
+/* The tables' identity (stamped into blobs) and their parameters. */
+uint64_t cg_tables_id(const cg_tables* tables);
+int cg_tables_params(const cg_tables* tables, cg_params* out);
+
+/* Number of chunks, and the worst-case size of chunk `chunk`'s blob. */
+int cg_num_chunks(const cg_tables* tables, int32_t* n_chunks);
+int cg_encode_bound(const cg_tables* tables, int32_t chunk, size_t* max_bytes);
+
+/* Encodes chunk `chunk` of the K/V pair at `quality` into one blob written at
+ * the device address out_dev (`cap` bytes; the blob needs at most
+ * cg_encode_bound bytes, CG_E_CAPACITY if it does not fit).  The tensors must be
+ * the ones the tables were built from (same shape).  One stream per
+ * (kv, layer, channel): the group's first token as an int8 anchor, the others
+ * as range-coded delta symbols (CacheGen blog, section 2.1 stages 1-3).
+ * Runs on `stream` and waits for it; *out_len receives the blob size.
+ * A handle encodes on one stream at a time (it owns the encode scratch). */
+int cg_encode(const cg_tables* tables, const void* k_dev, const void* v_dev,
+              int32_t chunk, int32_t quality, void* out_dev, size_t cap,
+              size_t* out_len, void* stream);
+
+/* Parses and checks a blob header from host memory (len >= 64). Host only. */
+int cg_chunk_info_parse(const void* blob_host, size_t len, cg_chunk_info* out);
+
+/* Decodes n blobs (device addresses blobs_dev[i]) into K/V fp16
+ * [layers][total_tokens][channels] at k_out_dev / v_out_dev; each blob writes its
+ * own token range.  The blobs' headers are read back to the host first.  Runs on
+ * `stream`, waits for it, and returns CG_E_CORRUPT if a blob failed validation
+ * on the device. */
+int cg_decode(const cg_tables* tables, int32_t n, const void* const* blobs_dev,
+              const size_t* lens, void* k_out_dev, void* v_out_dev, void* stream);
+
+/* Enqueue-only decode (gptget 方法详解: GPU decoding of the received bitstream).
+ * infos[i] is the parsed header of blobs_dev[i] (cg_chunk_info_parse on a host
+ * copy); the device blob must hold the same bytes.  Bit 0 of *status_dev
+ * (caller-owned device uint32, never cleared by the library) is set if a
+ * stream of a blob is inconsistent (offsets past the payload, impossible code
+ * value).  Corrupt payloads never cause out-of-bounds accesses. */
+int cg_decode_async(const cg_tables* tables, int32_t n, const void* const* blobs_dev,
+                    const cg_chunk_info* infos, void* k_out_dev, void* v_out_dev,
+                    uint32_t* status_dev, void* stream);
+
+/* Chunk pipeline (gptget 方法详解: decoding pipelined with the transfer; CacheGen
+ * blog 2.2: chunk-by-chunk streaming).  blobs_host[i] are host blobs (pinned
+ * memory gives asynchronous copies); each is copied into a slot of the device
+ * staging buffer (staging_cap bytes; at least two blobs' worth overlaps copy and
+ * decode) on copy_stream and decoded on compute_stream once its copy has
+ * landed; a slot is reused only after its previous decode finished.  Enqueue
+ * only; the work is complete when compute_stream is. */
+int cg_decode_streamed(const cg_tables* tables, int32_t n, const void* const* blobs_host,
+                       const cg_chunk_info* infos, void* k_out_dev, void* v_out_dev,
+                       void* staging_dev, size_t staging_cap, uint32_t* status_dev,
+                       void* copy_stream, void* compute_stream);
+
+/* Message of the calling thread's last error ("" if none). */
+const char* cg_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CACHEGEN_H */

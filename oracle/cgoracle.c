@@ -317,14 +317,15 @@ uint64_t cgo_fnv1a64(const uint8_t* data, size_t n) {
 }
 
 /* Identity of a serialized table set, stamped into every blob: FNV-1a-64 of
- * the little-endian FNV-1a-64 digests of its consecutive 64 KiB blocks (the
+ * the little-endian FNV-1a-64 digests of its consecutive 16 KiB blocks (the
  * last block may be shorter). */
+#define ID_BLOCK 16384
 uint64_t cgo_tables_id(const uint8_t* data, size_t n) {
-  size_t nblk = (n + 65535) / 65536;
+  size_t nblk = (n + ID_BLOCK - 1) / ID_BLOCK;
   uint8_t* d = (uint8_t*)malloc(8 * (nblk ? nblk : 1));
   for (size_t b = 0; b < nblk; b++) {
-    size_t len = (n - 65536 * b < 65536) ? n - 65536 * b : 65536;
-    uint64_t h = cgo_fnv1a64(data + 65536 * b, len);
+    size_t len = (n - ID_BLOCK * b < ID_BLOCK) ? n - ID_BLOCK * b : ID_BLOCK;
+    uint64_t h = cgo_fnv1a64(data + ID_BLOCK * b, len);
     for (int j = 0; j < 8; j++) d[8 * b + j] = (uint8_t)(h >> (8 * j));
   }
   uint64_t id = cgo_fnv1a64(d, 8 * nblk);
