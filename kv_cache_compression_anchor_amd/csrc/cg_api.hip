@@ -1,0 +1,657 @@
+// Host side of the C ABI declared in include/cachegen.h: argument validation,
+// device memory, kernel launches, table (de)serialization and the chunk
+// pipeline.  Every step of the codec runs in the kernels of cg_*.hip.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "cg_internal.h"
+
+using namespace cg;
+
+struct cg_tables {
+  cg_params p{};
+  int dev = 0;
+  DevTables t;
+  uint64_t id = 0;
+  std::mutex mu;  // guards the encode scratch
+  uint32_t* scratch = nullptr;
+  size_t scratch_words = 0;
+  uint32_t* lens = nullptr;      // [2][L][C]
+  uint32_t* row_words = nullptr; // [2L]
+  uint32_t* status = nullptr;    // device words: W, flags, decode status
+  uint32_t* host_status = nullptr;  // pinned mirror
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(CG_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define HIP_TRY(expr, what)               \
+  do {                                    \
+    hipError_t e_ = (expr);               \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) ok = hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+int check_params(const cg_params* p) {
+  if (!p) return fail(CG_E_INVAL, "params is NULL");
+  if (p->layers < 1 || p->tokens < 1 || p->channels < 1)
+    return fail(CG_E_INVAL, "layers, tokens and channels must be positive");
+  if (p->layers > 4096 || p->channels > 65536 || p->tokens > kMaxTokens)
+    return fail(CG_E_INVAL, "shape too large (layers <= 4096, channels <= 65536, tokens <= 2^21)");
+  if (p->chunk_tokens < 1 || p->chunk_tokens > kMaxChunk)
+    return fail(CG_E_INVAL, "chunk_tokens must be in 1..65536");
+  if (p->group_tokens < 1 || p->group_tokens > p->chunk_tokens)
+    return fail(CG_E_INVAL, "group_tokens must be in 1..chunk_tokens");
+  if (p->n_layer_groups < 1 || p->n_layer_groups > 3)
+    return fail(CG_E_INVAL, "n_layer_groups must be 1..3");
+  int prev = 0;
+  for (int i = 0; i < p->n_layer_groups; i++) {
+    if (p->layer_group_end[i] <= prev) return fail(CG_E_INVAL, "layer_group_end must increase");
+    prev = p->layer_group_end[i];
+    if (!(p->layer_step[i] > 0.0f) || !isfinite(p->layer_step[i]))
+      return fail(CG_E_INVAL, "layer_step must be positive and finite");
+  }
+  if (prev != p->layers) return fail(CG_E_INVAL, "last layer_group_end must equal layers");
+  if ((p->quality_mask & ~7u) || !p->quality_mask)
+    return fail(CG_E_INVAL, "quality_mask must be a non-empty subset of {H,M,L}");
+  for (int q = 0; q < 3; q++)
+    if ((p->quality_mask >> q) & 1)
+      if (!(p->quality_mult[q] > 0.0f) || !isfinite(p->quality_mult[q]))
+        return fail(CG_E_INVAL, "quality_mult must be positive and finite");
+  const size_t n = (size_t)2 * p->layers * p->channels;
+  const TabLayout lay = tab_layout(p->layers, p->channels, p->quality_mask);
+  if (lay.total > 0x7FFFFFFFull || n > 0x7FFFFFFFull)
+    return fail(CG_E_INVAL, "tables larger than 2 GiB");
+  return CG_OK;
+}
+
+void init_dev_tables(DevTables& t, const cg_params& p) {
+  t.L = p.layers;
+  t.T = p.tokens;
+  t.C = p.channels;
+  t.CH = p.chunk_tokens;
+  t.G = p.group_tokens;
+  t.nblk = (p.channels + kLanes - 1) / kLanes;
+  t.mask = p.quality_mask;
+  t.lay = tab_layout(p.layers, p.channels, p.quality_mask);
+}
+
+size_t img_bytes(const DevTables& t) { return (size_t)2 * t.L * t.nblk * kImgRows * kLanes * 2; }
+
+void write_header(uint8_t* h, const cg_params& p) {
+  memset(h, 0, kTabHdr);
+  uint32_t u[20] = {0};
+  u[0] = kTabMagic;
+  u[1] = 1;
+  u[2] = (uint32_t)p.layers;
+  u[3] = (uint32_t)p.channels;
+  u[4] = (uint32_t)p.tokens;
+  u[5] = (uint32_t)p.chunk_tokens;
+  u[6] = (uint32_t)p.group_tokens;
+  u[7] = (uint32_t)p.n_layer_groups;
+  for (int i = 0; i < 3; i++) {
+    u[8 + i] = i < p.n_layer_groups ? (uint32_t)p.layer_group_end[i] : 0u;
+    const float ls = i < p.n_layer_groups ? p.layer_step[i] : 0.0f;
+    const float qm = ((p.quality_mask >> i) & 1) ? p.quality_mult[i] : 0.0f;
+    memcpy(&u[11 + i], &ls, 4);
+    memcpy(&u[14 + i], &qm, 4);
+  }
+  u[17] = p.quality_mask;
+  u[18] = kProbBits;
+  u[19] = kNSym;
+  memcpy(h, u, kTabHdr);
+}
+
+void free_tables(cg_tables* t) {
+  if (!t) return;
+  DeviceGuard g(t->dev);
+  if (t->t.ser) (void)hipFree(t->t.ser);
+  for (int q = 0; q < 3; q++)
+    if (t->t.img[q]) (void)hipFree(t->t.img[q]);
+  if (t->scratch) (void)hipFree(t->scratch);
+  if (t->lens) (void)hipFree(t->lens);
+  if (t->row_words) (void)hipFree(t->row_words);
+  if (t->status) (void)hipFree(t->status);
+  if (t->host_status) (void)hipHostFree(t->host_status);
+  delete t;
+}
+
+// Allocates the device copies of a table set whose params are already checked.
+int alloc_tables(cg_tables* h) {
+  DevTables& t = h->t;
+  HIP_TRY(hipMalloc(&t.ser, t.lay.total), "hipMalloc(tables)");
+  for (int q = 0; q < 3; q++)
+    if ((t.mask >> q) & 1u) HIP_TRY(hipMalloc(&t.img[q], img_bytes(t)), "hipMalloc(images)");
+  HIP_TRY(hipMalloc(&h->status, 64), "hipMalloc(status)");
+  HIP_TRY(hipHostMalloc(&h->host_status, 64, hipHostMallocDefault), "hipHostMalloc(status)");
+  return CG_OK;
+}
+
+// Tables id of the device copy, computed on the GPU; syncs the stream.
+int compute_id(cg_tables* h, hipStream_t st) {
+  const size_t nblk = (h->t.lay.total + kIdBlock - 1) / kIdBlock;
+  uint64_t* dig = nullptr;
+  HIP_TRY(hipMalloc(&dig, 8 * (nblk + 1)), "hipMalloc(id)");
+  hipError_t e = launch_tables_id(h->t, dig, dig + nblk, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(h->host_status, dig + nblk, 8, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  (void)hipFree(dig);
+  if (e != hipSuccess) return hip_fail(e, "tables id");
+  memcpy(&h->id, h->host_status, 8);
+  return CG_OK;
+}
+
+struct ChunkGeo {
+  int t0, tc, ng;
+};
+
+ChunkGeo chunk_geo(const DevTables& t, int chunk) {
+  ChunkGeo g;
+  g.t0 = chunk * t.CH;
+  g.tc = std::min(t.CH, t.T - g.t0);
+  g.ng = (g.tc + t.G - 1) / t.G;
+  return g;
+}
+
+int n_chunks_of(const DevTables& t) { return (t.T + t.CH - 1) / t.CH; }
+
+int parse_info(const uint8_t* b, size_t len, cg_chunk_info* o) {
+  if (!b || !o) return fail(CG_E_INVAL, "NULL argument");
+  if (len < (size_t)kBlobHdr) return fail(CG_E_INVAL, "blob shorter than its header");
+  uint32_t u[16];
+  memcpy(u, b, 64);
+  if (u[0] != kBlobMagic || u[1] != 1) return fail(CG_E_INVAL, "not a CGK1 v1 blob");
+  if (u[11] != (uint32_t)kProbBits) return fail(CG_E_INVAL, "unsupported probability precision");
+  o->layers = (int32_t)u[2];
+  o->channels = (int32_t)u[3];
+  o->total_tokens = (int32_t)u[4];
+  o->token_offset = (int32_t)u[5];
+  o->chunk_tokens = (int32_t)u[6];
+  o->group_tokens = (int32_t)u[7];
+  o->n_groups = (int32_t)u[8];
+  o->quality = (int32_t)u[9];
+  o->payload_words = u[10];
+  o->reserved = 0;
+  memcpy(&o->tables_id, &u[12], 8);
+  if (o->layers < 1 || o->layers > 4096 || o->channels < 1 || o->channels > 65536 ||
+      o->total_tokens < 1 || o->total_tokens > kMaxTokens || o->chunk_tokens < 1 ||
+      o->chunk_tokens > kMaxChunk || o->group_tokens < 1 || o->token_offset < 0 ||
+      o->token_offset >= o->total_tokens ||
+      o->chunk_tokens > o->total_tokens - o->token_offset || o->quality < 0 || o->quality > 2 ||
+      o->n_groups != (o->chunk_tokens + o->group_tokens - 1) / o->group_tokens ||
+      o->payload_words > 0x3FFFFFFFu)
+    return fail(CG_E_INVAL, "inconsistent blob header");
+  const BlobLayout bl = blob_layout(o->layers, o->channels, o->n_groups);
+  o->blob_bytes = blob_bytes(bl, o->payload_words);
+  if (o->blob_bytes > 0xFFFFFFFFull) return fail(CG_E_INVAL, "blob larger than 4 GiB");
+  return CG_OK;
+}
+
+int check_info_against(const cg_tables* h, const cg_chunk_info& in) {
+  const DevTables& t = h->t;
+  if (in.layers != t.L || in.channels != t.C || in.total_tokens != t.T || in.group_tokens != t.G)
+    return fail(CG_E_MISMATCH, "blob shape differs from the tables");
+  if (in.tables_id != h->id) return fail(CG_E_MISMATCH, "blob was coded with other tables");
+  if (!((t.mask >> in.quality) & 1u)) return fail(CG_E_MISMATCH, "quality not in the tables");
+  if (in.token_offset % t.CH) return fail(CG_E_INVAL, "token_offset is not a chunk start");
+  const ChunkGeo g = chunk_geo(t, in.token_offset / t.CH);
+  if (g.tc != in.chunk_tokens) return fail(CG_E_INVAL, "chunk_tokens differs from the geometry");
+  return CG_OK;
+}
+
+// Enqueues the decode of n blobs whose headers are already checked.
+int enqueue_decode(const cg_tables* h, int n, const void* const* blobs, const cg_chunk_info* infos,
+                   void* k_out, void* v_out, uint32_t* status, hipStream_t st) {
+  const DevTables& t = h->t;
+  // chunks grouped by quality, up to 4 per workgroup (one wave each)
+  std::vector<int> byq[3];
+  for (int i = 0; i < n; i++) byq[infos[i].quality].push_back(i);
+  std::vector<std::vector<int>> groups;
+  for (int q = 0; q < 3; q++)
+    for (size_t j = 0; j < byq[q].size(); j += 4) {
+      std::vector<int> g(byq[q].begin() + j, byq[q].begin() + std::min(byq[q].size(), j + 4));
+      groups.push_back(g);
+    }
+  size_t gi = 0;
+  while (gi < groups.size()) {
+    DecodeArgs a;
+    memset(&a, 0, sizeof(a));
+    a.L = t.L;
+    a.T = t.T;
+    a.C = t.C;
+    a.G = t.G;
+    a.nblk = t.nblk;
+    for (int q = 0; q < 3; q++) {
+      a.img[q] = t.img[q];
+      a.step[q] = ((t.mask >> q) & 1u) ? reinterpret_cast<const float*>(t.ser + t.lay.off_step[q])
+                                       : nullptr;
+    }
+    a.scale_a = reinterpret_cast<const float*>(t.ser + t.lay.off_scale_a);
+    a.k_out = static_cast<uint16_t*>(k_out);
+    a.v_out = static_cast<uint16_t*>(v_out);
+    a.status = status;
+    int nc = 0, ngrp = 0, waves = 1;
+    while (gi < groups.size() && ngrp < kDecMaxChunks &&
+           nc + (int)groups[gi].size() <= kDecMaxChunks) {
+      DecGroup dg;
+      for (int w = 0; w < 4; w++) dg.chunk[w] = -1;
+      for (size_t w = 0; w < groups[gi].size(); w++) {
+        const int i = groups[gi][w];
+        const cg_chunk_info& in = infos[i];
+        const BlobLayout bl = blob_layout(t.L, t.C, in.n_groups);
+        DecChunk& dc = a.chunks[nc];
+        dc.blob = static_cast<const uint8_t*>(blobs[i]);
+        dc.blob_bytes = (uint32_t)in.blob_bytes;
+        dc.t0 = in.token_offset;
+        dc.tc = in.chunk_tokens;
+        dc.ng = in.n_groups;
+        dc.q = in.quality;
+        dc.off_anchor = (uint32_t)bl.off_anchor;
+        dc.off_len = (uint32_t)bl.off_len;
+        dc.off_pay = (uint32_t)bl.off_pay;
+        dc.W = in.payload_words;
+        dg.chunk[w] = (int8_t)nc++;
+      }
+      waves = std::max(waves, (int)groups[gi].size());
+      a.groups[ngrp++] = dg;
+      gi++;
+    }
+    a.n_groups = ngrp;
+    a.waves = waves;
+    HIP_TRY(launch_decode(a, st), "decode launch");
+  }
+  return CG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* cg_last_error(void) { return g_err.c_str(); }
+
+int cg_build_tables(const cg_params* params, const void* k_dev, const void* v_dev, void* stream,
+                    cg_tables** out) {
+  int rc = check_params(params);
+  if (rc) return rc;
+  if (!k_dev || !v_dev || !out) return fail(CG_E_INVAL, "NULL argument");
+  *out = nullptr;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  cg_tables* h = new (std::nothrow) cg_tables();
+  if (!h) return fail(CG_E_NOMEM, "host allocation");
+  h->p = *params;
+  if (hipGetDevice(&h->dev) != hipSuccess) {
+    delete h;
+    return fail(CG_E_HIP, "no HIP device");
+  }
+  init_dev_tables(h->t, *params);
+  DevTables& t = h->t;
+  if ((rc = alloc_tables(h))) {
+    free_tables(h);
+    return rc;
+  }
+  const size_t n = t.lay.n;
+  const size_t counts_words = (size_t)n * t.lay.nq * kNSym;
+  const size_t tmp_bytes = 4 * 8 * n + 4 * n + 16 + 4 * counts_words;
+  uint8_t* tmp = nullptr;
+  hipError_t e = hipMalloc(&tmp, tmp_bytes);
+  if (e != hipSuccess) {
+    free_tables(h);
+    return fail(CG_E_NOMEM, "device allocation for table statistics");
+  }
+  StatsBuf sb;
+  sb.s1 = reinterpret_cast<uint64_t*>(tmp);
+  sb.sa = sb.s1 + n;
+  sb.sb = sb.sa + n;
+  sb.sc = sb.sb + n;
+  sb.amax = reinterpret_cast<uint32_t*>(sb.sc + n);
+  sb.flags = sb.amax + n;
+  uint32_t* counts = sb.flags + 4;
+  uint8_t hdr[kTabHdr];
+  write_header(hdr, *params);
+  const uint16_t* k = static_cast<const uint16_t*>(k_dev);
+  const uint16_t* v = static_cast<const uint16_t*>(v_dev);
+  e = hipMemsetAsync(tmp, 0, tmp_bytes, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(t.ser, hdr, kTabHdr, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = launch_stats(k, 0, t.L, t.T, t.C, sb, st);
+  if (e == hipSuccess) e = launch_stats(v, 1, t.L, t.T, t.C, sb, st);
+  if (e == hipSuccess) e = launch_finalize(*params, sb, t, st);
+  if (e == hipSuccess) e = launch_histogram(k, 0, t, counts, st);
+  if (e == hipSuccess) e = launch_histogram(v, 1, t, counts, st);
+  if (e == hipSuccess) e = launch_normalize(t, counts, st);
+  if (e == hipSuccess) e = launch_images(t, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(h->host_status, sb.flags, 8, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  (void)hipFree(tmp);
+  if (e != hipSuccess) {
+    free_tables(h);
+    return hip_fail(e, "build tables");
+  }
+  if (h->host_status[0]) {
+    free_tables(h);
+    return fail(CG_E_INVAL, "K/V hold a non-finite value");
+  }
+  if (h->host_status[1]) {
+    free_tables(h);
+    return fail(CG_E_INVAL, "a delta step is not a normal binary32 value");
+  }
+  if ((rc = compute_id(h, st))) {
+    free_tables(h);
+    return rc;
+  }
+  *out = h;
+  return CG_OK;
+}
+
+void cg_tables_free(cg_tables* tables) { free_tables(tables); }
+
+int cg_tables_serialize(const cg_tables* h, void* buf, size_t cap, size_t* len) {
+  if (!h || !len) return fail(CG_E_INVAL, "NULL argument");
+  *len = h->t.lay.total;
+  if (!buf) return CG_OK;
+  if (cap < h->t.lay.total) return fail(CG_E_CAPACITY, "buffer smaller than the tables");
+  DeviceGuard g(h->dev);
+  HIP_TRY(hipMemcpy(buf, h->t.ser, h->t.lay.total, hipMemcpyDeviceToHost), "copy tables");
+  return CG_OK;
+}
+
+int cg_tables_deserialize(const void* buf, size_t len, cg_tables** out) {
+  if (!buf || !out) return fail(CG_E_INVAL, "NULL argument");
+  *out = nullptr;
+  const uint8_t* b = static_cast<const uint8_t*>(buf);
+  if (len < (size_t)kTabHdr) return fail(CG_E_INVAL, "tables shorter than their header");
+  uint32_t u[20];
+  memcpy(u, b, kTabHdr);
+  if (u[0] != kTabMagic || u[1] != 1 || u[18] != (uint32_t)kProbBits || u[19] != (uint32_t)kNSym)
+    return fail(CG_E_INVAL, "not CGT1 v1 tables");
+  cg_params p;
+  memset(&p, 0, sizeof(p));
+  p.layers = (int32_t)u[2];
+  p.channels = (int32_t)u[3];
+  p.tokens = (int32_t)u[4];
+  p.chunk_tokens = (int32_t)u[5];
+  p.group_tokens = (int32_t)u[6];
+  p.n_layer_groups = (int32_t)u[7];
+  for (int i = 0; i < 3; i++) {
+    p.layer_group_end[i] = (int32_t)u[8 + i];
+    memcpy(&p.layer_step[i], &u[11 + i], 4);
+    memcpy(&p.quality_mult[i], &u[14 + i], 4);
+  }
+  p.quality_mask = u[17];
+  int rc = check_params(&p);
+  if (rc) return rc;
+  const TabLayout lay = tab_layout(p.layers, p.channels, p.quality_mask);
+  if (len != lay.total) return fail(CG_E_INVAL, "tables size does not match their header");
+  // every value the kernels rely on: positive normal steps, finite inverses,
+  // frequency tables of 64 positive entries summing to 2^15
+  for (size_t i = 0; i < lay.n; i++) {
+    float sa, ia;
+    memcpy(&sa, b + lay.off_scale_a + 4 * i, 4);
+    memcpy(&ia, b + lay.off_inv_a + 4 * i, 4);
+    if (!(sa > 0.0f) || !isfinite(sa) || !isfinite(ia)) return fail(CG_E_INVAL, "bad anchor scale");
+  }
+  for (int q = 0; q < 3; q++) {
+    if (!((p.quality_mask >> q) & 1)) continue;
+    for (size_t i = 0; i < lay.n; i++) {
+      float s, is;
+      memcpy(&s, b + lay.off_step[q] + 4 * i, 4);
+      memcpy(&is, b + lay.off_inv_step[q] + 4 * i, 4);
+      if (!(s >= 1.17549435e-38f) || !isfinite(s) || !isfinite(is))
+        return fail(CG_E_INVAL, "bad delta step");
+      uint16_t f[kNSym];
+      memcpy(f, b + lay.off_freq[q] + 2 * kNSym * i, sizeof(f));
+      uint32_t sum = 0;
+      for (int k = 0; k < kNSym; k++) {
+        if (!f[k]) return fail(CG_E_INVAL, "zero frequency");
+        sum += f[k];
+      }
+      if (sum != kProbTotal) return fail(CG_E_INVAL, "frequencies do not sum to 2^15");
+    }
+  }
+  cg_tables* h = new (std::nothrow) cg_tables();
+  if (!h) return fail(CG_E_NOMEM, "host allocation");
+  h->p = p;
+  if (hipGetDevice(&h->dev) != hipSuccess) {
+    delete h;
+    return fail(CG_E_HIP, "no HIP device");
+  }
+  init_dev_tables(h->t, p);
+  if ((rc = alloc_tables(h))) {
+    free_tables(h);
+    return rc;
+  }
+  hipError_t e = hipMemcpy(h->t.ser, b, len, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = launch_images(h->t, nullptr);
+  if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+  if (e != hipSuccess) {
+    free_tables(h);
+    return hip_fail(e, "upload tables");
+  }
+  if ((rc = compute_id(h, nullptr))) {
+    free_tables(h);
+    return rc;
+  }
+  *out = h;
+  return CG_OK;
+}
+
+uint64_t cg_tables_id(const cg_tables* h) { return h ? h->id : 0; }
+
+int cg_tables_params(const cg_tables* h, cg_params* out) {
+  if (!h || !out) return fail(CG_E_INVAL, "NULL argument");
+  *out = h->p;
+  return CG_OK;
+}
+
+int cg_num_chunks(const cg_tables* h, int32_t* n) {
+  if (!h || !n) return fail(CG_E_INVAL, "NULL argument");
+  *n = n_chunks_of(h->t);
+  return CG_OK;
+}
+
+int cg_encode_bound(const cg_tables* h, int32_t chunk, size_t* max_bytes) {
+  if (!h || !max_bytes) return fail(CG_E_INVAL, "NULL argument");
+  if (chunk < 0 || chunk >= n_chunks_of(h->t)) return fail(CG_E_INVAL, "chunk out of range");
+  const ChunkGeo g = chunk_geo(h->t, chunk);
+  const BlobLayout bl = blob_layout(h->t.L, h->t.C, g.ng);
+  *max_bytes = blob_bytes(bl, h->t.lay.n * stream_words_bound(g.tc - g.ng));
+  return CG_OK;
+}
+
+int cg_encode(const cg_tables* ch, const void* k_dev, const void* v_dev, int32_t chunk,
+              int32_t quality, void* out_dev, size_t cap, size_t* out_len, void* stream) {
+  if (!ch || !k_dev || !v_dev || !out_dev || !out_len) return fail(CG_E_INVAL, "NULL argument");
+  cg_tables* h = const_cast<cg_tables*>(ch);
+  const DevTables& t = h->t;
+  if (chunk < 0 || chunk >= n_chunks_of(t)) return fail(CG_E_INVAL, "chunk out of range");
+  if (quality < 0 || quality > 2 || !((t.mask >> quality) & 1u))
+    return fail(CG_E_MISMATCH, "quality not in the tables");
+  const ChunkGeo g = chunk_geo(t, chunk);
+  const BlobLayout bl = blob_layout(t.L, t.C, g.ng);
+  if (cap < bl.off_pay + 16) return fail(CG_E_CAPACITY, "output smaller than the blob's fixed part");
+  DeviceGuard dg(h->dev);
+  if (!dg.ok) return fail(CG_E_HIP, "cannot select the tables' device");
+  std::lock_guard<std::mutex> lk(h->mu);
+  const size_t swb = stream_words_bound(t.CH - (t.CH + t.G - 1) / t.G);
+  const size_t need = t.lay.n * std::max<size_t>(swb, 1);
+  if (h->scratch_words < need) {
+    if (h->scratch) (void)hipFree(h->scratch);
+    h->scratch = nullptr;
+    h->scratch_words = 0;
+    if (hipMalloc(&h->scratch, need * 4) != hipSuccess) return fail(CG_E_NOMEM, "encode scratch");
+    h->scratch_words = need;
+  }
+  if (!h->lens) {
+    HIP_TRY(hipMalloc(&h->lens, 4 * t.lay.n), "hipMalloc(lens)");
+    HIP_TRY(hipMalloc(&h->row_words, 8 * (size_t)t.L), "hipMalloc(rows)");
+  }
+  EncodeArgs a;
+  a.k = static_cast<const uint16_t*>(k_dev);
+  a.v = static_cast<const uint16_t*>(v_dev);
+  a.L = t.L;
+  a.T = t.T;
+  a.C = t.C;
+  a.G = t.G;
+  a.nblk = t.nblk;
+  a.t0 = g.t0;
+  a.tc = g.tc;
+  a.ng = g.ng;
+  a.q = quality;
+  a.scale_a = reinterpret_cast<const float*>(t.ser + t.lay.off_scale_a);
+  a.inv_a = reinterpret_cast<const float*>(t.ser + t.lay.off_inv_a);
+  a.inv_step = reinterpret_cast<const float*>(t.ser + t.lay.off_inv_step[quality]);
+  a.img = t.img[quality];
+  a.scratch = h->scratch;
+  a.swb = std::max<size_t>(swb, 1);
+  a.lens = h->lens;
+  a.blob = static_cast<uint8_t*>(out_dev);
+  a.lay = bl;
+  a.row_words = h->row_words;
+  a.status = h->status;
+  a.cap = cap;
+  a.tables_id = h->id;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  HIP_TRY(hipMemsetAsync(h->status, 0, 12, st), "clear status");
+  HIP_TRY(launch_encode(a, st), "encode launch");
+  HIP_TRY(hipMemcpyAsync(h->host_status, h->status, 12, hipMemcpyDeviceToHost, st), "encode status");
+  HIP_TRY(hipStreamSynchronize(st), "encode");
+  if (h->host_status[2]) return fail(CG_E_INVAL, "K/V hold a non-finite value");
+  if (h->host_status[1]) return fail(CG_E_CAPACITY, "blob larger than the output buffer");
+  *out_len = blob_bytes(bl, h->host_status[0]);
+  return CG_OK;
+}
+
+int cg_chunk_info_parse(const void* blob_host, size_t len, cg_chunk_info* out) {
+  return parse_info(static_cast<const uint8_t*>(blob_host), len, out);
+}
+
+int cg_decode_async(const cg_tables* h, int32_t n, const void* const* blobs_dev,
+                    const cg_chunk_info* infos, void* k_out_dev, void* v_out_dev,
+                    uint32_t* status_dev, void* stream) {
+  if (!h || n < 0 || (n > 0 && (!blobs_dev || !infos)) || !k_out_dev || !v_out_dev || !status_dev)
+    return fail(CG_E_INVAL, "NULL argument");
+  for (int i = 0; i < n; i++) {
+    if (!blobs_dev[i]) return fail(CG_E_INVAL, "NULL blob");
+    int rc = check_info_against(h, infos[i]);
+    if (rc) return rc;
+  }
+  if (n == 0) return CG_OK;
+  DeviceGuard dg(h->dev);
+  if (!dg.ok) return fail(CG_E_HIP, "cannot select the tables' device");
+  return enqueue_decode(h, n, blobs_dev, infos, k_out_dev, v_out_dev, status_dev,
+                        static_cast<hipStream_t>(stream));
+}
+
+int cg_decode(const cg_tables* ch, int32_t n, const void* const* blobs_dev, const size_t* lens,
+              void* k_out_dev, void* v_out_dev, void* stream) {
+  if (!ch || n < 0 || (n > 0 && (!blobs_dev || !lens)) || !k_out_dev || !v_out_dev)
+    return fail(CG_E_INVAL, "NULL argument");
+  cg_tables* h = const_cast<cg_tables*>(ch);
+  DeviceGuard dg(h->dev);
+  if (!dg.ok) return fail(CG_E_HIP, "cannot select the tables' device");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  std::vector<cg_chunk_info> infos(n);
+  for (int i = 0; i < n; i++) {
+    if (!blobs_dev[i]) return fail(CG_E_INVAL, "NULL blob");
+    uint8_t hdr[kBlobHdr];
+    if (lens[i] < (size_t)kBlobHdr) return fail(CG_E_INVAL, "blob shorter than its header");
+    HIP_TRY(hipMemcpyAsync(hdr, blobs_dev[i], kBlobHdr, hipMemcpyDeviceToHost, st), "read header");
+    HIP_TRY(hipStreamSynchronize(st), "read header");
+    int rc = parse_info(hdr, kBlobHdr, &infos[i]);
+    if (rc) return rc;
+    if (infos[i].blob_bytes > lens[i]) return fail(CG_E_INVAL, "blob shorter than its header says");
+    if ((rc = check_info_against(h, infos[i]))) return rc;
+  }
+  if (n == 0) return CG_OK;
+  std::lock_guard<std::mutex> lk(h->mu);
+  uint32_t* status = h->status + 8;
+  HIP_TRY(hipMemsetAsync(status, 0, 4, st), "clear status");
+  int rc = enqueue_decode(h, n, blobs_dev, infos.data(), k_out_dev, v_out_dev, status, st);
+  if (rc) return rc;
+  HIP_TRY(hipMemcpyAsync(h->host_status + 8, status, 4, hipMemcpyDeviceToHost, st), "status");
+  HIP_TRY(hipStreamSynchronize(st), "decode");
+  if (h->host_status[8]) return fail(CG_E_CORRUPT, "a blob failed validation while decoding");
+  return CG_OK;
+}
+
+int cg_decode_streamed(const cg_tables* h, int32_t n, const void* const* blobs_host,
+                       const cg_chunk_info* infos, void* k_out_dev, void* v_out_dev,
+                       void* staging_dev, size_t staging_cap, uint32_t* status_dev,
+                       void* copy_stream, void* compute_stream) {
+  if (!h || n < 0 || (n > 0 && (!blobs_host || !infos)) || !k_out_dev || !v_out_dev ||
+      !status_dev || !staging_dev)
+    return fail(CG_E_INVAL, "NULL argument");
+  size_t slot = 0;
+  for (int i = 0; i < n; i++) {
+    if (!blobs_host[i]) return fail(CG_E_INVAL, "NULL blob");
+    int rc = check_info_against(h, infos[i]);
+    if (rc) return rc;
+    slot = std::max<size_t>(slot, (infos[i].blob_bytes + 255) & ~(size_t)255);
+  }
+  if (n == 0) return CG_OK;
+  if (staging_cap < slot) return fail(CG_E_CAPACITY, "staging buffer smaller than a blob");
+  const int nslots = (int)std::min<size_t>((size_t)n, staging_cap / slot);
+  DeviceGuard dg(h->dev);
+  if (!dg.ok) return fail(CG_E_HIP, "cannot select the tables' device");
+  hipStream_t cs = static_cast<hipStream_t>(copy_stream);
+  hipStream_t ks = static_cast<hipStream_t>(compute_stream);
+  std::vector<hipEvent_t> copied(nslots, nullptr), done(nslots, nullptr);
+  int rc = CG_OK;
+  for (int s = 0; s < nslots && rc == CG_OK; s++) {
+    if (hipEventCreateWithFlags(&copied[s], hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&done[s], hipEventDisableTiming) != hipSuccess)
+      rc = fail(CG_E_HIP, "event creation");
+  }
+  uint8_t* stage = static_cast<uint8_t*>(staging_dev);
+  for (int i = 0; i < n && rc == CG_OK; i++) {
+    const int s = i % nslots;
+    uint8_t* dst = stage + (size_t)s * slot;
+    hipError_t e = hipSuccess;
+    if (i >= nslots) e = hipStreamWaitEvent(cs, done[s], 0);  // slot's last decode finished
+    if (e == hipSuccess) e = hipMemcpyAsync(dst, blobs_host[i], infos[i].blob_bytes,
+                                            hipMemcpyHostToDevice, cs);
+    if (e == hipSuccess) e = hipEventRecord(copied[s], cs);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ks, copied[s], 0);
+    if (e != hipSuccess) {
+      rc = hip_fail(e, "pipeline copy");
+      break;
+    }
+    const void* b = dst;
+    rc = enqueue_decode(h, 1, &b, &infos[i], k_out_dev, v_out_dev, status_dev, ks);
+    if (rc == CG_OK && (e = hipEventRecord(done[s], ks)) != hipSuccess)
+      rc = hip_fail(e, "pipeline event");
+  }
+  for (int s = 0; s < nslots; s++) {
+    if (copied[s]) (void)hipEventDestroy(copied[s]);
+    if (done[s]) (void)hipEventDestroy(done[s]);
+  }
+  return rc;
+}
+
+}  // extern "C"

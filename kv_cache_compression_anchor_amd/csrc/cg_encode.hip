@@ -1,0 +1,233 @@
+// Chunk encoder (CacheGen blog, section 2.1: anchor quantised to 8 bits, deltas
+// of the other tokens of the group against it, layer-group step, arithmetic
+// coding).  One lane per stream (kv, layer, channel): a wave codes 64 channels
+// of one (kv, layer) row in lockstep, so every input row it reads is one
+// coalesced 128-byte segment.  Streams land in per-stream scratch, then a
+// wavefront prefix sum over the stream lengths packs them into the blob.
+#include "cg_internal.h"
+
+namespace cg {
+namespace {
+
+constexpr int kEncWaves = 4;
+
+// Range coder state of one lane.  Output bytes are final when emitted: a
+// possible carry is held back in `cache` plus a run of `pending` 0xFF bytes.
+struct RcEnc {
+  uint64_t low;     // < 2^33; bit 32 is a carry into the bytes held back
+  uint32_t range;
+  uint32_t cache;   // last byte not yet emitted
+  uint32_t pending; // 0xFF bytes after the cache
+  uint32_t have;    // cache holds a byte
+  uint32_t acc;     // bytes of the current output word, first byte highest
+  uint32_t nacc;
+  uint32_t nw;      // words written
+};
+
+__device__ __forceinline__ void put_byte(RcEnc& e, uint32_t b, uint32_t* out) {
+  e.acc = (e.acc << 8) | (b & 0xFFu);
+  if (++e.nacc == 4) {
+    out[e.nw++] = e.acc;
+    e.acc = 0;
+    e.nacc = 0;
+  }
+}
+
+__device__ __forceinline__ void shift_low(RcEnc& e, uint32_t* out) {
+  const uint32_t carry = (uint32_t)(e.low >> 32);
+  const uint32_t byte = (uint32_t)(e.low >> 24) & 0xFFu;
+  if (!e.have) {
+    e.cache = byte;  // the first byte can still take a carry, never overflow
+    e.have = 1;
+  } else if (byte != 0xFFu || carry) {
+    put_byte(e, e.cache + carry, out);
+    for (; e.pending; e.pending--) put_byte(e, 0xFFu + carry, out);
+    e.cache = byte;
+  } else {
+    e.pending++;
+  }
+  e.low = (e.low & 0x00FFFFFFull) << 8;
+}
+
+__device__ __forceinline__ void rc_put(RcEnc& e, uint32_t c0, uint32_t freq, uint32_t* out) {
+  const uint32_t r = e.range >> kProbBits;
+  e.low += (uint64_t)mul24(r, c0);
+  e.range = mul24(r, freq);
+  while (e.range < kTop) {
+    shift_low(e, out);
+    e.range <<= 8;
+  }
+}
+
+// Flush: the fewest bytes (one or two) that name an aligned block inside
+// [low, low + range), so the stream decodes whatever bytes follow it.
+__device__ __forceinline__ void rc_finish(RcEnc& e, uint32_t* out) {
+  int k = 1;
+  uint64_t V = (e.low + 0xFFFFFFull) & ~0xFFFFFFull;
+  if (V + 0x1000000ull > e.low + e.range) {
+    k = 2;
+    V = (e.low + 0xFFFFull) & ~0xFFFFull;
+  }
+  e.low = V;
+  for (int j = 0; j < k; j++) shift_low(e, out);
+  if (e.have) {
+    put_byte(e, e.cache, out);
+    for (; e.pending; e.pending--) put_byte(e, 0xFFu, out);
+  }
+  if (e.nacc) out[e.nw++] = e.acc << (8 * (4 - e.nacc));
+}
+
+__global__ __launch_bounds__(kLanes * kEncWaves) void k_encode(EncodeArgs a) {
+  __shared__ uint16_t tab[kEncWaves][kImgRows * kLanes];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int units = 2 * a.L * a.nblk;
+  const int unit = blockIdx.x * kEncWaves + wave;
+  if (unit < units) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.img + (size_t)unit * kImgRows * kLanes);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(tab[wave]);
+    for (int j = lane; j < kImgRows * kLanes / 2; j += kLanes) dst[j] = src[j];
+  }
+  __syncthreads();
+  if (unit >= units) return;
+  const int kv = unit / (a.L * a.nblk);
+  const int l = (unit / a.nblk) % a.L;
+  const int cb = unit % a.nblk;
+  const int c = cb * kLanes + lane;
+  if (c >= a.C) return;
+  const size_t pi = ((size_t)kv * a.L + l) * a.C + c;
+  const float scale_a = a.scale_a[pi], inv_a = a.inv_a[pi], inv_step = a.inv_step[pi];
+  const uint16_t* x = (kv ? a.v : a.k) + ((size_t)l * a.T + a.t0) * a.C + c;
+  const uint8_t* tb = reinterpret_cast<const uint8_t*>(tab[wave]) + 2 * lane_slot(lane);
+  uint32_t* out = a.scratch + pi * a.swb;
+  int8_t* anchors = reinterpret_cast<int8_t*>(a.blob + a.lay.off_anchor) +
+                    ((size_t)kv * a.L + l) * a.ng * a.C + c;
+  RcEnc e = {0, 0xFFFFFFFFu, 0, 0, 0, 0, 0, 0};
+  uint32_t nonfinite = 0;
+  for (int g = 0; g < a.ng; g++) {
+    const int ta = g * a.G, te = min(ta + a.G, a.tc);
+    const uint16_t ha = x[(size_t)ta * a.C];
+    nonfinite |= (ha & 0x7C00u) == 0x7C00u;
+    const int av = quant_anchor(half_bits_to_float(ha), inv_a);
+    anchors[(size_t)g * a.C] = (int8_t)av;
+    const float ahat = anchor_value(av, scale_a);
+    for (int t = ta + 1; t < te; t++) {
+      const uint16_t hx = x[(size_t)t * a.C];
+      nonfinite |= (hx & 0x7C00u) == 0x7C00u;
+      const uint32_t s = quant_delta(half_bits_to_float(hx), ahat, inv_step);
+      const uint32_t c0 = *reinterpret_cast<const uint16_t*>(tb + s * (2 * kLanes));
+      const uint32_t c1 = *reinterpret_cast<const uint16_t*>(tb + (s + 1) * (2 * kLanes));
+      rc_put(e, c0, c1 - c0, out);
+    }
+  }
+  if (a.tc > a.ng) rc_finish(e, out);  // a stream without symbols stays empty
+  if (nonfinite) atomicOr(&a.status[2], 1u);
+  a.lens[pi] = e.nw;
+  reinterpret_cast<uint16_t*>(a.blob + a.lay.off_len)[pi] = (uint16_t)e.nw;
+}
+
+// words of every (kv, layer) row
+__global__ __launch_bounds__(256) void k_row_totals(const uint32_t* lens, int C, uint32_t* row_words) {
+  __shared__ uint32_t part[4];
+  const uint32_t* r = lens + (size_t)blockIdx.x * C;
+  uint32_t s = 0;
+  for (int j = threadIdx.x; j < C; j += 256) s += r[j];
+  for (int o = 32; o; o >>= 1) s += __shfl_xor(s, o);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) row_words[blockIdx.x] = part[0] + part[1] + part[2] + part[3];
+}
+
+// row offsets, payload size, header, zero padding; flags a blob larger than cap
+__global__ void k_row_scan(EncodeArgs a) {
+  if (threadIdx.x != 0) return;
+  const int rows = 2 * a.L;
+  uint32_t* row_off = reinterpret_cast<uint32_t*>(a.blob + a.lay.off_rows);
+  uint64_t w = 0;
+  for (int r = 0; r < rows; r++) {
+    row_off[r] = (uint32_t)w;
+    w += a.row_words[r];
+  }
+  const size_t total = blob_bytes(a.lay, w);
+  a.status[0] = (uint32_t)w;
+  a.status[1] = (total > a.cap || w > 0x3FFFFFFFull) ? 1u : 0u;
+  uint32_t* h = reinterpret_cast<uint32_t*>(a.blob);
+  h[0] = kBlobMagic;
+  h[1] = 1;
+  h[2] = (uint32_t)a.L;
+  h[3] = (uint32_t)a.C;
+  h[4] = (uint32_t)a.T;
+  h[5] = (uint32_t)a.t0;
+  h[6] = (uint32_t)a.tc;
+  h[7] = (uint32_t)a.G;
+  h[8] = (uint32_t)a.ng;
+  h[9] = (uint32_t)a.q;
+  h[10] = (uint32_t)w;
+  h[11] = kProbBits;
+  h[12] = (uint32_t)a.tables_id;
+  h[13] = (uint32_t)(a.tables_id >> 32);
+  h[14] = 0;
+  h[15] = 0;
+}
+
+// zero the gap before the payload and the tail after it
+__global__ __launch_bounds__(256) void k_pad(EncodeArgs a) {
+  if (a.status[1]) return;
+  const size_t W = a.status[0];
+  const size_t gap0 = a.lay.off_len + 4 * (size_t)a.L * a.C, gap1 = a.lay.off_pay;
+  const size_t tail0 = a.lay.off_pay + 4 * W, tail1 = blob_bytes(a.lay, W);
+  for (size_t j = gap0 + threadIdx.x; j < gap1; j += 256) a.blob[j] = 0;
+  for (size_t j = tail0 + threadIdx.x; j < tail1; j += 256) a.blob[j] = 0;
+}
+
+// Pack one row: block-wide exclusive prefix sum of the stream lengths (wave
+// scans plus the wave totals), then each wave copies whole streams with
+// coalesced 64-word moves.
+__global__ __launch_bounds__(256) void k_pack(EncodeArgs a) {
+  if (a.status[1]) return;
+  __shared__ uint32_t wsum[4];
+  __shared__ uint32_t soff[256];
+  __shared__ uint32_t slen[256];
+  const int row = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const uint32_t* lens = a.lens + (size_t)row * a.C;
+  uint32_t* pay = reinterpret_cast<uint32_t*>(a.blob + a.lay.off_pay);
+  uint32_t base = reinterpret_cast<const uint32_t*>(a.blob + a.lay.off_rows)[row];
+  for (int c0 = 0; c0 < a.C; c0 += 256) {
+    const int c = c0 + tid;
+    const uint32_t len = c < a.C ? lens[c] : 0u;
+    uint32_t incl = len;
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    uint32_t before = base;
+    for (int w = 0; w < wave; w++) before += wsum[w];
+    soff[tid] = before + incl - len;
+    slen[tid] = len;
+    const uint32_t chunk_total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+    const int n = min(256, a.C - c0);
+    for (int j = wave; j < n; j += 4) {
+      const uint32_t* src = a.scratch + ((size_t)row * a.C + c0 + j) * a.swb;
+      uint32_t* dst = pay + soff[j];
+      for (uint32_t k = lane; k < slen[j]; k += 64) dst[k] = src[k];
+    }
+    base += chunk_total;
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_encode(const EncodeArgs& a, hipStream_t st) {
+  const int units = 2 * a.L * a.nblk;
+  k_encode<<<(units + kEncWaves - 1) / kEncWaves, kLanes * kEncWaves, 0, st>>>(a);
+  k_row_totals<<<2 * a.L, 256, 0, st>>>(a.lens, a.C, a.row_words);
+  k_row_scan<<<1, 64, 0, st>>>(a);
+  k_pad<<<1, 256, 0, st>>>(a);
+  k_pack<<<2 * a.L, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace cg

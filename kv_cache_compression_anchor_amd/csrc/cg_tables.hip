@@ -1,0 +1,425 @@
+// Table building on the GPU (CacheGen blog, section 1: symbol probabilities
+// counted per layer-channel combination; section 2.1: step sizes 0.5/1.0/1.5 per
+// layer group).  All reductions are exact integer sums, so the result does not
+// depend on the order in which workgroups run.
+#include <float.h>
+
+#include "cg_internal.h"
+
+namespace cg {
+namespace {
+
+constexpr int kStatsRows = 1024;  // tokens per stats workgroup
+
+struct Acc {
+  uint64_t s1, sa, sb, sc;
+  uint32_t amax, nf;
+};
+
+// |X| = |x| * 2^24 = M << E for a finite binary16 x; split as A*2^20 + B so that
+// the squares fit 64-bit partial sums: X^2 = A^2 2^40 + 2AB 2^20 + B^2.
+__device__ __forceinline__ void accumulate(Acc& a, uint32_t h) {
+  const uint32_t e = (h >> 10) & 31u, m = h & 1023u;
+  if (e == 31u) {
+    a.nf = 1;
+    return;
+  }
+  const uint32_t M = e ? (m | 1024u) : m;
+  const uint32_t E = e ? e - 1u : 0u;
+  uint32_t A, B;
+  if (E < 20u) {
+    const uint32_t v = M << E;
+    A = v >> 20;
+    B = v & 0xFFFFFu;
+  } else {
+    A = M << (E - 20u);
+    B = 0;
+  }
+  a.sa += (uint64_t)A * A;
+  a.sb += (uint64_t)A * B;
+  a.sc += (uint64_t)B * B;
+  const uint64_t mag = ((uint64_t)A << 20) | B;
+  a.s1 += (h & 0x8000u) ? (0ull - mag) : mag;
+  a.amax = max(a.amax, h & 0x7FFFu);
+}
+
+__global__ __launch_bounds__(256) void k_stats(const uint16_t* __restrict__ x, int kv, int L,
+                                               int T, int C, StatsBuf sb) {
+  __shared__ Acc part[128][2];
+  const int tid = threadIdx.x;
+  const int cp = tid & 127, ph = tid >> 7;
+  const int c0 = blockIdx.x * 256 + 2 * cp;
+  const int l = blockIdx.z;
+  const int tbeg = blockIdx.y * kStatsRows;
+  const int tend = min(tbeg + kStatsRows, T);
+  const bool has0 = c0 < C, has1 = c0 + 1 < C;
+  const bool paired = has1 && ((C & 1) == 0);
+  Acc a0 = {0, 0, 0, 0, 0, 0}, a1 = {0, 0, 0, 0, 0, 0};
+  const uint16_t* base = x + (size_t)l * T * C + c0;
+  for (int t = tbeg + ph; t < tend; t += 2) {
+    const uint16_t* p = base + (size_t)t * C;
+    if (paired) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+      accumulate(a0, w & 0xFFFFu);
+      accumulate(a1, w >> 16);
+    } else {
+      if (has0) accumulate(a0, p[0]);
+      if (has1) accumulate(a1, p[1]);
+    }
+  }
+  if (ph) {
+    part[cp][0] = a0;
+    part[cp][1] = a1;
+  }
+  __syncthreads();
+  if (ph) return;
+  const Acc o0 = part[cp][0], o1 = part[cp][1];
+  a0.s1 += o0.s1; a0.sa += o0.sa; a0.sb += o0.sb; a0.sc += o0.sc;
+  a0.amax = max(a0.amax, o0.amax); a0.nf |= o0.nf;
+  a1.s1 += o1.s1; a1.sa += o1.sa; a1.sb += o1.sb; a1.sc += o1.sc;
+  a1.amax = max(a1.amax, o1.amax); a1.nf |= o1.nf;
+  const size_t i0 = ((size_t)kv * L + l) * C + c0;
+  if (has0) {
+    atomicAdd((unsigned long long*)&sb.s1[i0], (unsigned long long)a0.s1);
+    atomicAdd((unsigned long long*)&sb.sa[i0], (unsigned long long)a0.sa);
+    atomicAdd((unsigned long long*)&sb.sb[i0], (unsigned long long)a0.sb);
+    atomicAdd((unsigned long long*)&sb.sc[i0], (unsigned long long)a0.sc);
+    atomicMax(&sb.amax[i0], a0.amax);
+  }
+  if (has1) {
+    atomicAdd((unsigned long long*)&sb.s1[i0 + 1], (unsigned long long)a1.s1);
+    atomicAdd((unsigned long long*)&sb.sa[i0 + 1], (unsigned long long)a1.sa);
+    atomicAdd((unsigned long long*)&sb.sb[i0 + 1], (unsigned long long)a1.sb);
+    atomicAdd((unsigned long long*)&sb.sc[i0 + 1], (unsigned long long)a1.sc);
+    atomicMax(&sb.amax[i0 + 1], a1.amax);
+  }
+  if (a0.nf | a1.nf) atomicOr(&sb.flags[0], 1u);
+}
+
+// Correctly rounded (to nearest, ties to even) conversion of a 128-bit integer:
+// keep the top 64 bits with the lost bits folded into a sticky bit, convert once.
+__device__ double u128_to_f64(unsigned __int128 v) {
+  const uint64_t hi = (uint64_t)(v >> 64);
+  if (hi == 0) return (double)(uint64_t)v;
+  const int shift = 64 - __clzll(hi);
+  uint64_t top = (uint64_t)(v >> shift);
+  const unsigned __int128 lost = v & (((unsigned __int128)1 << shift) - 1);
+  top |= (lost != 0) ? 1ull : 0ull;
+  return ldexp((double)top, shift);
+}
+
+struct FinArgs {
+  StatsBuf sb;
+  uint8_t* ser;
+  int L, T, C;
+  uint32_t mask;
+  int lg_end[3];
+  float layer_step[3];
+  float mult[3];
+  size_t off_scale_a, off_inv_a, off_step[3], off_inv_step[3];
+};
+
+// Population std over all tokens from the exact moments, anchor scale and the
+// per-quality delta step of every (kv, layer, channel).
+__global__ __launch_bounds__(256) void k_finalize(FinArgs a) {
+  const size_t n = (size_t)2 * a.L * a.C;
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int l = (int)((i / a.C) % a.L);
+  const int64_t S1 = (int64_t)a.sb.s1[i];
+  const unsigned __int128 S2 = ((unsigned __int128)a.sb.sa[i] << 40) +
+                               ((unsigned __int128)a.sb.sb[i] << 21) +
+                               (unsigned __int128)a.sb.sc[i];
+  const unsigned __int128 num =
+      (unsigned __int128)a.T * S2 - (unsigned __int128)((__int128)S1 * S1);
+  const double sigma = num ? sqrt(u128_to_f64(num)) / ((double)a.T * 16777216.0) : 1.0;
+  const float amax = half_bits_to_float((uint16_t)a.sb.amax[i]);
+  const float scale_a = amax > 0.0f ? (float)((double)amax / 127.0) : 1.0f;
+  const float inv_a = (float)(1.0 / (double)scale_a);
+  reinterpret_cast<float*>(a.ser + a.off_scale_a)[i] = scale_a;
+  reinterpret_cast<float*>(a.ser + a.off_inv_a)[i] = inv_a;
+  int g = 0;
+  while (g < 2 && l >= a.lg_end[g]) g++;
+  const double ls = (double)a.layer_step[g];
+  for (int q = 0; q < 3; q++) {
+    if (!((a.mask >> q) & 1u)) continue;
+    const float step = (float)((double)a.mult[q] * ls * sigma);
+    const float inv_step = (float)(1.0 / (double)step);
+    if (!(step >= FLT_MIN) || !isfinite(inv_step)) atomicOr(&a.sb.flags[1], 1u);
+    reinterpret_cast<float*>(a.ser + a.off_step[q])[i] = step;
+    reinterpret_cast<float*>(a.ser + a.off_inv_step[q])[i] = inv_step;
+  }
+}
+
+struct HistArgs {
+  const uint16_t* x;
+  int kv, L, T, C, CH, G, nq;
+  const float* scale_a;
+  const float* inv_a;
+  const float* inv_step[3];  // by slot
+  uint32_t* counts;          // [2][nq][L][C][64]
+};
+
+// Delta-symbol histogram of one (kv, layer, 64-channel block, chunk): each lane
+// owns a channel, the four waves take interleaved groups; counts go to LDS with
+// atomics ([slot][symbol][lane] keeps the 64 lanes in distinct banks), then to
+// global memory with one atomic per non-zero bin.
+__global__ __launch_bounds__(256) void k_histogram(HistArgs a) {
+  __shared__ uint32_t hist[3 * kNSym * kLanes];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int j = tid; j < a.nq * kNSym * kLanes; j += 256) hist[j] = 0;
+  __syncthreads();
+  const int c = blockIdx.x * kLanes + lane;
+  const int chunk = blockIdx.y, l = blockIdx.z;
+  const int t0 = chunk * a.CH;
+  const int tc = min(a.CH, a.T - t0);
+  const int ng = (tc + a.G - 1) / a.G;
+  if (c < a.C) {
+    const size_t pi = ((size_t)a.kv * a.L + l) * a.C + c;
+    const float scale_a = a.scale_a[pi], inv_a = a.inv_a[pi];
+    const float is0 = a.inv_step[0][pi];
+    const float is1 = a.nq > 1 ? a.inv_step[1][pi] : 1.0f;
+    const float is2 = a.nq > 2 ? a.inv_step[2][pi] : 1.0f;
+    const uint16_t* xc = a.x + ((size_t)l * a.T + t0) * a.C + c;
+    for (int g = wave; g < ng; g += 4) {
+      const int ta = g * a.G, te = min(ta + a.G, tc);
+      const float ahat = anchor_value(quant_anchor(half_bits_to_float(xc[(size_t)ta * a.C]), inv_a),
+                                      scale_a);
+      for (int t = ta + 1; t < te; t++) {
+        const float xv = half_bits_to_float(xc[(size_t)t * a.C]);
+        atomicAdd(&hist[(0 * kNSym + quant_delta(xv, ahat, is0)) * kLanes + lane], 1u);
+        if (a.nq > 1) atomicAdd(&hist[(1 * kNSym + quant_delta(xv, ahat, is1)) * kLanes + lane], 1u);
+        if (a.nq > 2) atomicAdd(&hist[(2 * kNSym + quant_delta(xv, ahat, is2)) * kLanes + lane], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  for (int j = tid; j < a.nq * kNSym * kLanes; j += 256) {
+    const uint32_t v = hist[j];
+    if (!v) continue;
+    const int s = j / (kNSym * kLanes), sym = (j / kLanes) % kNSym, ln = j % kLanes;
+    const int cc = blockIdx.x * kLanes + ln;
+    const size_t ti = (((size_t)a.kv * a.nq + s) * a.L + l) * a.C + cc;
+    atomicAdd(&a.counts[ti * kNSym + sym], v);
+  }
+}
+
+struct NormArgs {
+  const uint32_t* counts;
+  uint8_t* ser;
+  int L, C, nq;
+  int q_of_slot[3];
+  size_t off_freq[3];
+};
+
+// counts -> frequencies summing to 2^15: one slot each, the rest in proportion
+// (rounded down), the remainder to the most counted symbol (lowest on ties).
+__global__ __launch_bounds__(256) void k_normalize(NormArgs a) {
+  const size_t ntab = (size_t)2 * a.nq * a.L * a.C;
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= ntab) return;
+  const size_t lc = (size_t)a.L * a.C;
+  const int kv = (int)(i / (a.nq * lc));
+  const int s = (int)((i / lc) % a.nq);
+  const size_t rest = i % lc;  // l * C + c
+  const uint32_t* cnt = a.counts + i * kNSym;
+  uint64_t N = 0;
+  for (int k = 0; k < kNSym; k++) N += cnt[k];
+  const double spare = (double)(kProbTotal - kNSym);
+  const double den = N ? (double)N : (double)kNSym;
+  // floor of an exact quotient of integers below 2^36 and 2^22: the correctly
+  // rounded binary64 quotient never crosses an integer
+  uint32_t total = 0, bestc = 0;
+  int best = -1;
+  for (int k = 0; k < kNSym; k++) {
+    const uint32_t ck = N ? cnt[k] : 1u;
+    total += 1u + (uint32_t)floor((double)ck * spare / den);
+    if (best < 0 || ck > bestc) {
+      bestc = ck;
+      best = k;
+    }
+  }
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.ser + a.off_freq[a.q_of_slot[s]]) +
+                  ((size_t)kv * lc + rest) * kNSym;
+  for (int k = 0; k < kNSym; k++) {
+    const uint32_t ck = N ? cnt[k] : 1u;
+    uint32_t f = 1u + (uint32_t)floor((double)ck * spare / den);
+    if (k == best) f += kProbTotal - total;
+    out[k] = (uint16_t)f;
+  }
+}
+
+struct ImgArgs {
+  const uint8_t* ser;
+  uint16_t* img[3];
+  int L, C, nblk;
+  size_t off_freq[3];
+  uint32_t mask;
+};
+
+// Frequencies -> cumulative tables laid out as LDS images: per (kv, layer,
+// 64-channel block) 65 rows of 64 16-bit entries, entry of lane j at
+// lane_slot(j).  Channels past C get a uniform table.
+__global__ __launch_bounds__(256) void k_images(ImgArgs a) {
+  const size_t per_q = (size_t)2 * a.L * a.nblk * kLanes;
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= 3 * per_q) return;
+  const int q = (int)(i / per_q);
+  if (!((a.mask >> q) & 1u)) return;
+  const size_t r = i % per_q;
+  const int lane = (int)(r % kLanes);
+  const size_t blk = r / kLanes;  // (kv * L + l) * nblk + cb
+  const int cb = (int)(blk % a.nblk);
+  const size_t row = blk / a.nblk;  // kv * L + l
+  const int c = cb * kLanes + lane;
+  uint16_t* out = a.img[q] + blk * (kImgRows * kLanes) + lane_slot(lane);
+  uint32_t cum = 0;
+  if (c < a.C) {
+    const uint16_t* f =
+        reinterpret_cast<const uint16_t*>(a.ser + a.off_freq[q]) + (row * a.C + c) * kNSym;
+    for (int k = 0; k < kNSym; k++) {
+      out[k * kLanes] = (uint16_t)cum;
+      cum += f[k];
+    }
+  } else {
+    for (int k = 0; k < kNSym; k++) {
+      out[k * kLanes] = (uint16_t)cum;
+      cum += kProbTotal / kNSym;
+    }
+  }
+  out[kNSym * kLanes] = (uint16_t)cum;  // 2^15 does not fit 15 bits but fits 16
+}
+
+constexpr uint64_t kFnvBasis = 0xcbf29ce484222325ull;
+constexpr uint64_t kFnvPrime = 0x100000001b3ull;
+
+__device__ __forceinline__ uint64_t fnv_byte(uint64_t h, uint32_t b) {
+  return (h ^ b) * kFnvPrime;
+}
+
+__global__ __launch_bounds__(256) void k_id_blocks(const uint8_t* ser, size_t n,
+                                                   uint64_t* digests) {
+  const size_t nblk = (n + kIdBlock - 1) / kIdBlock;
+  const size_t b = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblk) return;
+  const size_t start = b * kIdBlock;
+  const size_t len = min((size_t)kIdBlock, n - start);
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(ser + start);
+  uint64_t h = kFnvBasis;
+  size_t k = 0;
+  for (; k + 4 <= len; k += 4) {
+    const uint32_t v = w[k / 4];
+    h = fnv_byte(h, v & 0xFF);
+    h = fnv_byte(h, (v >> 8) & 0xFF);
+    h = fnv_byte(h, (v >> 16) & 0xFF);
+    h = fnv_byte(h, v >> 24);
+  }
+  for (; k < len; k++) h = fnv_byte(h, ser[start + k]);
+  digests[b] = h;
+}
+
+__global__ void k_id_final(const uint64_t* digests, size_t nblk, uint64_t* out) {
+  uint64_t h = kFnvBasis;
+  for (size_t b = 0; b < nblk; b++) {
+    const uint64_t d = digests[b];
+    for (int j = 0; j < 8; j++) h = fnv_byte(h, (uint32_t)(d >> (8 * j)) & 0xFF);
+  }
+  *out = h;
+}
+
+inline unsigned blocks_for(size_t n, unsigned per) { return (unsigned)((n + per - 1) / per); }
+
+}  // namespace
+
+hipError_t launch_stats(const uint16_t* x, int kv, int L, int T, int C, const StatsBuf& sb,
+                        hipStream_t st) {
+  dim3 grid((unsigned)((C + 255) / 256), (unsigned)((T + kStatsRows - 1) / kStatsRows),
+            (unsigned)L);
+  k_stats<<<grid, 256, 0, st>>>(x, kv, L, T, C, sb);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const cg_params& p, const StatsBuf& sb, DevTables& t, hipStream_t st) {
+  FinArgs a;
+  a.sb = sb;
+  a.ser = t.ser;
+  a.L = t.L;
+  a.T = t.T;
+  a.C = t.C;
+  a.mask = t.mask;
+  for (int g = 0; g < 3; g++) {
+    a.lg_end[g] = g < p.n_layer_groups ? p.layer_group_end[g] : t.L;
+    a.layer_step[g] = g < p.n_layer_groups ? p.layer_step[g] : p.layer_step[p.n_layer_groups - 1];
+    a.mult[g] = p.quality_mult[g];
+    a.off_step[g] = t.lay.off_step[g];
+    a.off_inv_step[g] = t.lay.off_inv_step[g];
+  }
+  a.off_scale_a = t.lay.off_scale_a;
+  a.off_inv_a = t.lay.off_inv_a;
+  k_finalize<<<blocks_for(t.lay.n, 256), 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_histogram(const uint16_t* x, int kv, const DevTables& t, uint32_t* counts,
+                            hipStream_t st) {
+  HistArgs a;
+  a.x = x;
+  a.kv = kv;
+  a.L = t.L;
+  a.T = t.T;
+  a.C = t.C;
+  a.CH = t.CH;
+  a.G = t.G;
+  a.nq = t.lay.nq;
+  a.scale_a = reinterpret_cast<const float*>(t.ser + t.lay.off_scale_a);
+  a.inv_a = reinterpret_cast<const float*>(t.ser + t.lay.off_inv_a);
+  for (int q = 0, s = 0; q < 3; q++)
+    if ((t.mask >> q) & 1u) a.inv_step[s++] = reinterpret_cast<const float*>(t.ser + t.lay.off_inv_step[q]);
+  a.counts = counts;
+  const int nchunks = (t.T + t.CH - 1) / t.CH;
+  dim3 grid((unsigned)t.nblk, (unsigned)nchunks, (unsigned)t.L);
+  k_histogram<<<grid, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_normalize(const DevTables& t, const uint32_t* counts, hipStream_t st) {
+  NormArgs a;
+  a.counts = counts;
+  a.ser = t.ser;
+  a.L = t.L;
+  a.C = t.C;
+  a.nq = t.lay.nq;
+  for (int q = 0, s = 0; q < 3; q++) {
+    a.off_freq[q] = t.lay.off_freq[q];
+    if ((t.mask >> q) & 1u) a.q_of_slot[s++] = q;
+  }
+  const size_t ntab = (size_t)2 * a.nq * t.L * t.C;
+  k_normalize<<<blocks_for(ntab, 256), 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_images(DevTables& t, hipStream_t st) {
+  ImgArgs a;
+  a.ser = t.ser;
+  for (int q = 0; q < 3; q++) {
+    a.img[q] = t.img[q];
+    a.off_freq[q] = t.lay.off_freq[q];
+  }
+  a.L = t.L;
+  a.C = t.C;
+  a.nblk = t.nblk;
+  a.mask = t.mask;
+  const size_t n = (size_t)3 * 2 * t.L * t.nblk * kLanes;
+  k_images<<<blocks_for(n, 256), 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tables_id(const DevTables& t, uint64_t* digests, uint64_t* id_out,
+                            hipStream_t st) {
+  const size_t nblk = (t.lay.total + kIdBlock - 1) / kIdBlock;
+  k_id_blocks<<<blocks_for(nblk, 64), 64, 0, st>>>(t.ser, t.lay.total, digests);
+  k_id_final<<<1, 1, 0, st>>>(digests, nblk, id_out);
+  return hipGetLastError();
+}
+
+}  // namespace cg

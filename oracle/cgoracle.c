@@ -583,6 +583,13 @@ size_t cgo_encode_bound(const uint8_t* tables, size_t tlen, int chunk) {
   return align16(align16(body) + 4 * 2 * L * C * stream_words_bound(tc, ng) + 16);
 }
 
+/* a binary16 value whose exponent field is all ones is infinite or NaN */
+static int any_nonfinite(const uint16_t* x, size_t stride, int n) {
+  for (int t = 0; t < n; t++)
+    if ((x[(size_t)t * stride] & 0x7C00) == 0x7C00) return 1;
+  return 0;
+}
+
 /* symbols of one channel of one chunk: anchors[g] and delta symbols in token
  * order (the group's first token is the anchor, the others are deltas) */
 static void channel_symbols(const uint16_t* x, size_t stride, int tc, int G, float scale_a,
@@ -657,6 +664,10 @@ int cgo_encode_chunk(const uint8_t* tables, size_t tlen, const uint16_t* k,
     size_t used = 0;
     for (int c = 0; c < C; c++) {
       size_t i = kv * lc + (size_t)l * C + c;
+      if (any_nonfinite(x + c, C, tc)) {
+#pragma omp critical
+        rc = E_INVAL; /* non-finite input cannot be coded */
+      }
       uint16_t f[NSYM];
       tv_freq(tv.freq[q], i, f);
       channel_symbols(x + c, C, tc, G, tv_f(tv.scale_a, i), tv_f(tv.inv_a, i),
@@ -883,6 +894,7 @@ int cgo_stream_encode(const uint8_t* tables, size_t tlen, int kv, int l, int c, 
     return E_INVAL;
   const int G = tv.p.group_tokens, ng = (tc + G - 1) / G;
   size_t i = (size_t)kv * tv.p.layers * tv.p.channels + (size_t)l * tv.p.channels + c;
+  if (any_nonfinite(x, 1, tc)) return E_INVAL;
   uint8_t* sym = (uint8_t*)malloc(tc);
   channel_symbols(x, 1, tc, G, tv_f(tv.scale_a, i), tv_f(tv.inv_a, i),
                   tv_f(tv.inv_step[q], i), anchors, sym, NULL);

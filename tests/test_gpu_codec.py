@@ -1,0 +1,146 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle on the same
+seeded inputs.  Integer and byte results (tables, blobs) must be identical; the
+fp16 reconstruction must be bit-identical (within 1 ulp is the stated bar, 0
+is what the shared binary32 op sequence gives)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def run_all(w, check_cross=True):
+    k, v = synth.gen_kv(w)
+    kd, vd = gu.to_dev(k), gu.to_dev(v)
+    tab = gu.gpu_tables(w, kd, vd)
+    import kv_cache_compression_anchor_amd as cg
+    gt = cg.cg_tables_serialize(tab)
+    ot = oracle.build_tables(oracle.params_for(w), k, v)
+    assert gt == ot, ("tables differ", gu.first_difference(gt, ot))
+    assert tab.id == oracle.tables_id(ot)
+    for ch in range(w.n_chunks):
+        for q in w.qualities:
+            dblob, gb = gu.gpu_encode(tab, kd, vd, ch, q)
+            ob = oracle.encode_chunk(ot, k, v, ch, q)
+            assert gb == ob, ("blob differs", ch, q, gu.first_difference(gb, ob))
+            kg, vg, st = gu.gpu_decode(tab, [dblob], k.shape)
+            ko, vo, bad = gu.oracle_decode(ot, [ob], k.shape)
+            assert st == 0 and not bad
+            assert gu.same_bits(kg, ko) and gu.same_bits(vg, vo), ("decode differs", ch, q)
+    return k, v, kd, vd, tab, ot
+
+
+def test_tiny_workload():
+    run_all(synth.workload("tiny"))
+
+
+def test_multi_chunk_ragged_three_qualities():
+    # 3 chunks (last one ragged), ragged last group, channels not a multiple of 64
+    run_all(gu.workload())
+
+
+@pytest.mark.parametrize("shape", [
+    dict(tokens=1, chunk_tokens=1, group_tokens=1, channels=3),
+    dict(tokens=37, chunk_tokens=16, group_tokens=5, channels=7),
+    dict(tokens=23, chunk_tokens=23, group_tokens=1, channels=65),
+    dict(tokens=50, chunk_tokens=21, group_tokens=10, channels=1),
+    dict(tokens=300, chunk_tokens=300, group_tokens=300, channels=130),
+    dict(tokens=129, chunk_tokens=64, group_tokens=3, channels=64),
+])
+def test_edge_geometries(shape):
+    run_all(gu.workload(layers=2, layer_group_end=(1, 2), layer_step=(0.5, 1.5), **shape))
+
+
+def test_selection_of_mixed_qualities_in_one_call():
+    """Several chunks at different qualities decoded by one cg_decode_async call
+    (chunks of one quality share a workgroup's LDS tables)."""
+    w = gu.workload(tokens=2000, chunk_tokens=256, channels=192)
+    k, v = synth.gen_kv(w)
+    kd, vd = gu.to_dev(k), gu.to_dev(v)
+    tab = gu.gpu_tables(w, kd, vd)
+    import kv_cache_compression_anchor_amd as cg
+    ot = cg.cg_tables_serialize(tab)
+    sel = [(ch, (ch * 7) % 3) for ch in range(w.n_chunks)]
+    dblobs, hblobs = zip(*[gu.gpu_encode(tab, kd, vd, ch, q) for ch, q in sel])
+    kg, vg, st = gu.gpu_decode(tab, list(dblobs), k.shape)
+    ko, vo, bad = gu.oracle_decode(ot, hblobs, k.shape)
+    assert st == 0 and not bad
+    assert gu.same_bits(kg, ko) and gu.same_bits(vg, vo)
+    # and the synchronous entry point gives the same
+    t = gu.torch()
+    k2 = t.zeros_like(kd)
+    v2 = t.zeros_like(vd)
+    cg.cg_decode(tab, list(dblobs), k2, v2)
+    assert gu.same_bits(k2.cpu().numpy(), ko) and gu.same_bits(v2.cpu().numpy(), vo)
+
+
+def test_cross_decoding_both_ways():
+    w = gu.workload(tokens=700, channels=70, seed=9)
+    k, v = synth.gen_kv(w)
+    kd, vd = gu.to_dev(k), gu.to_dev(v)
+    tab = gu.gpu_tables(w, kd, vd)
+    ot = oracle.build_tables(oracle.params_for(w), k, v)
+    import kv_cache_compression_anchor_amd as cg
+    # tables made by the oracle, uploaded: the GPU decodes oracle blobs
+    tab2 = cg.cg_tables_deserialize(ot)
+    assert tab2.id == tab.id
+    for q in w.qualities:
+        obs = [oracle.encode_chunk(ot, k, v, ch, q) for ch in range(w.n_chunks)]
+        dev = [gu.to_dev(np.frombuffer(b, np.uint8).copy()) for b in obs]
+        kg, vg, st = gu.gpu_decode(tab2, dev, k.shape)
+        ko, vo, _ = gu.oracle_decode(ot, obs, k.shape)
+        assert st == 0 and gu.same_bits(kg, ko) and gu.same_bits(vg, vo)
+        # GPU blobs decoded by the oracle
+        gbs = [gu.gpu_encode(tab, kd, vd, ch, q)[1] for ch in range(w.n_chunks)]
+        ko2, vo2, bad = gu.oracle_decode(ot, gbs, k.shape)
+        assert not bad and gu.same_bits(ko2, ko) and gu.same_bits(vo2, vo)
+
+
+def test_degenerate_channels():
+    w = gu.workload(layers=1, tokens=64, channels=6, chunk_tokens=64, layer_group_end=(1,),
+                    layer_step=(0.5,), qualities=(0,))
+    k = np.zeros((1, 64, 6), np.float16)
+    v = np.zeros((1, 64, 6), np.float16)
+    k[0, :, 1] = 3.25
+    k[0, :, 2] = np.float16(-65504)
+    k[0, ::7, 3] = np.float16(1e-7)
+    k[0, :, 4] = np.float16(6e-8) * np.arange(64) % 3
+    k[0, :, 5] = np.float16(60000) * (np.arange(64) % 2)
+    kd, vd = gu.to_dev(k), gu.to_dev(v)
+    tab = gu.gpu_tables(w, kd, vd)
+    import kv_cache_compression_anchor_amd as cg
+    ot = oracle.build_tables(oracle.params_for(w), k, v)
+    assert cg.cg_tables_serialize(tab) == ot
+    dblob, gb = gu.gpu_encode(tab, kd, vd, 0, 0)
+    assert gb == oracle.encode_chunk(ot, k, v, 0, 0)
+    kg, vg, st = gu.gpu_decode(tab, [dblob], k.shape)
+    ko, vo, _ = gu.oracle_decode(ot, [gb], k.shape)
+    assert st == 0 and gu.same_bits(kg, ko) and gu.same_bits(vg, vo)
+
+
+def test_nonfinite_input_is_rejected():
+    import kv_cache_compression_anchor_amd as cg
+    w = gu.workload(layers=1, tokens=40, channels=8, chunk_tokens=40, layer_group_end=(1,),
+                    layer_step=(0.5,), qualities=(0,))
+    k, v = synth.gen_kv(w)
+    v[0, 5, 5] = np.nan
+    with pytest.raises(cg.CgError) as e:
+        gu.gpu_tables(w, gu.to_dev(k), gu.to_dev(v))
+    assert e.value.code == cg.CG_E_INVAL
+
+
+def test_nonfinite_input_is_not_encoded():
+    import kv_cache_compression_anchor_amd as cg
+    w = gu.workload(layers=1, tokens=80, channels=8, chunk_tokens=40, layer_group_end=(1,),
+                    layer_step=(0.5,), qualities=(0,))
+    k, v = synth.gen_kv(w)
+    kd, vd = gu.to_dev(k), gu.to_dev(v)
+    tab = gu.gpu_tables(w, kd, vd)
+    kd[0, 45, 2] = float("inf")
+    gu.gpu_encode(tab, kd, vd, 0, 0)
+    with pytest.raises(cg.CgError) as e:
+        gu.gpu_encode(tab, kd, vd, 1, 0)
+    assert e.value.code == cg.CG_E_INVAL

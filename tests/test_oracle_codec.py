@@ -274,3 +274,13 @@ def test_corrupt_payload_is_flagged_not_crashing(oracle_lib, coded):
     with pytest.raises(oracle_lib.OracleError) as e:
         oracle_lib.decode_blob(bytes(t2), blobs[(0, 0)], ko, vo)
     assert e.value.code == -6
+
+
+def test_nonfinite_input_is_not_encoded(oracle_lib, coded):
+    w, k, v, t, blobs = coded
+    k2 = k.copy()
+    k2[1, 500, 3] = np.inf
+    with pytest.raises(oracle_lib.OracleError) as e:
+        oracle_lib.encode_chunk(t, k2, v, 1, 0)
+    assert e.value.code == -1
+    oracle_lib.encode_chunk(t, k2, v, 0, 0)  # other chunks are unaffected
