@@ -1,0 +1,241 @@
+"""Benchmark of the KV-cache codec hot path on one MI355X.
+
+One step = the whole hot path over one synthetic context (Mistral-7B-shape GQA,
+K and V each [32 layers, 9216 tokens, 1024 channels] fp16, 6 chunks of 1536
+tokens): build the per-(kv, layer, channel) tables, encode every chunk at H, M
+and L, and decode one mixed-quality selection H,M,L,H,M,L with one
+cg_decode_async call.  Inputs are resident in HBM when the timed region starts.
+
+`value` is the decode throughput in GB/s of fp16 KV written; the roofline entry
+counts the decode kernel's algorithmic bytes (blob bytes read + fp16 written)
+per launch against MI355X's 8 TB/s HBM peak, with the kernel's duration taken
+from HIP events on the stream it runs on.  The CPU baseline is the oracle's
+decode of a bounded sample of the same selection on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="mistral7b_9k")
+    ap.add_argument("--decode-reps", type=int, default=1,
+                    help="timed decode launches per step (the selection is decoded this many times)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-seconds", type=float, default=10.0,
+                    help="the oracle decodes the selection repeatedly for about this long")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES (for HBM counter scaling)")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "decode_traffic.json"))
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the codec's streams are independent, sharding is described in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    if args.copy_calibration:
+        a = torch.empty(args.copy_calibration // 4, dtype=torch.int32, device="cuda:0")
+        b = torch.empty_like(a)
+        a.fill_(1)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": a.numel() * 4}), flush=True)
+        return
+
+    import kv_cache_compression_anchor_amd as cg
+    import synth
+
+    w = synth.workload(args.workload)
+    t_gen = time.time()
+    k, v = synth.gen_kv(w)
+    t_gen = time.time() - t_gen
+    dev = torch.device("cuda:0")
+    kd = torch.from_numpy(k).to(dev)
+    vd = torch.from_numpy(v).to(dev)
+    p = cg.make_params(w.layers, w.tokens, w.channels, w.chunk_tokens, w.group_tokens,
+                       w.layer_group_end, w.layer_step, w.quality_mult, w.quality_mask)
+    sel = w.selection()
+    nch = w.n_chunks
+    elements = w.elements
+    fp16_bytes = 2 * elements
+    stream = torch.cuda.current_stream()
+
+    # output buffers, allocated once: one blob buffer per (chunk, quality)
+    tab0 = cg.cg_build_tables(p, kd, vd)
+    bufs = {(c, q): torch.empty(cg.cg_encode_bound(tab0, c), dtype=torch.uint8, device=dev)
+            for c in range(nch) for q in w.qualities}
+    del tab0
+    ko = torch.empty_like(kd)
+    vo = torch.empty_like(vd)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def step(timed: bool):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4 + 2 * args.decode_reps)]
+        t0 = time.perf_counter()
+        ev[0].record(stream)
+        tab = cg.cg_build_tables(p, kd, vd)
+        ev[1].record(stream)
+        sizes = {}
+        for c in range(nch):
+            for q in w.qualities:
+                sizes[(c, q)] = cg.cg_encode(tab, kd, vd, c, q, bufs[(c, q)])
+        ev[2].record(stream)
+        blobs = [bufs[(c, q)][: sizes[(c, q)]] for c, q in enumerate(sel)]
+        infos = [cg.cg_chunk_info_parse(b[:64].cpu()) for b in blobs]
+        dec = []
+        for r in range(args.decode_reps):
+            ev[3 + 2 * r].record(stream)
+            cg.cg_decode_async(tab, blobs, infos, ko, vo, status)
+            ev[4 + 2 * r].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        dec = [ev[3 + 2 * r].elapsed_time(ev[4 + 2 * r]) for r in range(args.decode_reps)]
+        return dict(wall_ms=wall * 1e3, build_ms=ev[0].elapsed_time(ev[1]),
+                    encode_ms=ev[1].elapsed_time(ev[2]), decode_ms=dec, sizes=sizes, tab=tab)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    results = []
+    t_all = time.perf_counter()
+    for _ in range(args.steps):
+        results.append(step(True))
+    torch.cuda.synchronize()
+    t_all = time.perf_counter() - t_all
+    if int(status.item()) != 0:
+        raise SystemExit("decode reported a corrupt stream")
+
+    sizes = results[-1]["sizes"]
+    sel_blob_bytes = sum(sizes[(c, q)] for c, q in enumerate(sel))
+    dec_ms = [d for r in results for d in r["decode_ms"]]
+    dec_avg_ms = sum(dec_ms) / len(dec_ms)
+    value = fp16_bytes / (dec_avg_ms * 1e-3) / 1e9
+    achieved = (fp16_bytes + sel_blob_bytes) / (dec_avg_ms * 1e-3) / 1e9
+    enc_ms = sum(r["encode_ms"] for r in results) / len(results)
+    build_ms = sum(r["build_ms"] for r in results) / len(results)
+    step_ms = t_all * 1e3 / args.steps
+    all_blob_bytes = sum(sizes.values())
+    nq = len(w.qualities)
+    tables_bytes = len(cg.cg_tables_serialize(results[-1]["tab"]))
+    eight_bit = elements  # one byte per element
+    ratio = eight_bit / sel_blob_bytes
+    ratio_q = {("HML"[q]): eight_bit / sum(sizes[(c, q)] for c in range(nch)) for q in w.qualities}
+
+    traffic = decode_traffic(args.traffic_json, w.name)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, k, v, results[-1]["tab"], bufs, sizes, sel, args.cpu_sample_seconds)
+
+    line = {
+        "metric": "decode GB/s (fp16 KV out) + compress ratio vs 8-bit, Mistral-7B-shape 9K tok",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic (seeded AR(1) K/V with lognormal channel scales)",
+        "config": {"workload": w.name, "layers": w.layers, "tokens": w.tokens,
+                   "channels": w.channels, "chunk_tokens": w.chunk_tokens,
+                   "group_tokens": w.group_tokens, "chunks": nch,
+                   "decode_selection": ",".join("HML"[q] for q in sel)},
+        "compress_ratio_vs_8bit": round(ratio, 4),
+        "compress_ratio_vs_8bit_with_tables": round(eight_bit / (sel_blob_bytes + tables_bytes), 4),
+        "compress_ratio_by_quality": {q: round(r, 4) for q, r in ratio_q.items()},
+        "selection_blob_bytes": sel_blob_bytes,
+        "decode_ms": round(dec_avg_ms, 4),
+        "decode_GBps_algorithmic": round(achieved, 2),
+        "encode_ms_all_chunks_all_qualities": round(enc_ms, 3),
+        "encode_GBps_fp16_in": round(nq * fp16_bytes / (enc_ms * 1e-3) / 1e9, 2),
+        "build_tables_ms": round(build_ms, 3),
+        "build_tables_GBps_fp16_in": round(fp16_bytes / (build_ms * 1e-3) / 1e9, 2),
+        "roofline": {"bound": "hbm", "kernel": "k_decode", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+        "input_generation_s": round(t_gen, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
+DECODE_SOURCES = ["kv_cache_compression_anchor_amd/csrc/cg_decode.hip",
+                  "kv_cache_compression_anchor_amd/csrc/cg_internal.h"]
+
+
+def decode_traffic(path, workload):
+    """HBM bytes per decode launch from the committed FETCH_SIZE / WRITE_SIZE
+    counter runs (scaled by the same counters on a plain copy of known size);
+    None when the record is for another workload or the decoder changed since."""
+    import hashlib
+    try:
+        rec = json.load(open(path))
+        src = b"".join(open(os.path.join(ROOT, p), "rb").read() for p in DECODE_SOURCES)
+        if rec.get("workload") != workload:
+            return None
+        if rec.get("kernel_source_sha256") != hashlib.sha256(src).hexdigest():
+            return None
+        return int(rec["bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        return None
+
+
+def cpu_baseline(w, k, v, tab, bufs, sizes, sel, seconds):
+    """The oracle decoding the selection (the same blobs the GPU decodes) on this
+    host's cores, chunk after chunk, until about `seconds` have passed; GB/s of
+    fp16 written."""
+    import numpy as np
+
+    import kv_cache_compression_anchor_amd as cg
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    t = cg.cg_tables_serialize(tab)
+    ko = np.zeros_like(k)
+    vo = np.zeros_like(v)
+    blobs = [bufs[(c, q)][: sizes[(c, q)]].cpu().numpy().tobytes() for c, q in enumerate(sel)]
+    n = 0
+    tok = 0
+    t0 = time.perf_counter()
+    while True:
+        c = n % len(blobs)
+        oracle.decode_blob(t, blobs[c], ko, vo, threads=threads)
+        tok += min(w.chunk_tokens, w.tokens - c * w.chunk_tokens)
+        n += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds and n >= len(blobs):
+            break
+    out_bytes = 2 * 2 * w.layers * tok * w.channels
+    return {"value": round(out_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"oracle decode of {n} chunk blobs of the selection "
+                      f"({n // len(blobs)}+ passes, {2 * w.layers * tok * w.channels} elements, "
+                      f"{dt:.1f} s)"}
+
+
+if __name__ == "__main__":
+    main()
