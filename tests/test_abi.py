@@ -1,0 +1,133 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/cachegen.h declares, and its host-only logic (blob header parsing,
+argument validation before any GPU work) behaves as documented."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cachegen.h")
+
+
+@pytest.fixture(scope="module")
+def cg():
+    import kv_cache_compression_anchor_amd as pkg
+    if not os.path.exists(pkg.LIB_PATH):
+        from kv_cache_compression_anchor_amd import build
+        build.build()
+    pkg.lib()
+    return pkg
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cg_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports(cg):
+    assert declared_functions() == sorted(cg.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(cg):
+    out = subprocess.run(["nm", "-D", "--defined-only", cg.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [f for f in declared_functions() if f not in exported]
+    assert not missing, missing
+    for f in declared_functions():
+        assert hasattr(cg.lib(), f)
+
+
+def test_struct_layouts_match_the_header(cg, tmp_path):
+    """sizeof and offsetof of the ABI structs, as the C compiler lays them out,
+    equal the binding's ctypes layouts."""
+    fields = {"cg_params": [f for f, _ in cg.cg_params._fields_],
+              "cg_chunk_info": [f for f, _ in cg.cg_chunk_info._fields_]}
+    src = ["#include <stdio.h>", "#include <stddef.h>", '#include "cachegen.h"', "int main(void){"]
+    for st, fs in fields.items():
+        src.append(f'printf("{st} %zu\\n", sizeof({st}));')
+        for f in fs:
+            src.append(f'printf("{st}.{f} %zu\\n", offsetof({st}, {f}));')
+    src.append("return 0;}")
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(src))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(c), "-o", str(exe)], check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                        check=True).stdout.splitlines())
+    for st, cls in (("cg_params", cg.cg_params), ("cg_chunk_info", cg.cg_chunk_info)):
+        assert int(got[st]) == ctypes.sizeof(cls)
+        for f in fields[st]:
+            assert int(got[f"{st}.{f}"]) == getattr(cls, f).offset, (st, f)
+
+
+def test_chunk_info_parse_reads_oracle_blobs(cg):
+    w = synth.workload("tiny", tokens=150, chunk_tokens=64)
+    k, v = synth.gen_kv(w)
+    t = oracle.build_tables(oracle.params_for(w), k, v)
+    for ch in range(w.n_chunks):
+        b = oracle.encode_chunk(t, k, v, ch, 0)
+        info = cg.cg_chunk_info_parse(b)
+        h = oracle.parse_blob_header(b)
+        assert (info.layers, info.channels, info.total_tokens) == (2, 128, 150)
+        assert info.token_offset == h["token_offset"] and info.chunk_tokens == h["chunk_tokens"]
+        assert info.n_groups == h["n_groups"] and info.quality == 0
+        assert info.payload_words == h["payload_words"]
+        assert info.tables_id == oracle.tables_id(t)
+        assert info.blob_bytes == len(b)
+
+
+def test_chunk_info_parse_rejects_bad_headers(cg):
+    w = synth.workload("tiny")
+    k, v = synth.gen_kv(w)
+    t = oracle.build_tables(oracle.params_for(w), k, v)
+    b = bytearray(oracle.encode_chunk(t, k, v, 0, 0))
+    for off, val in ((0, 0x58), (4, 2), (44, 14), (32, 99), (36, 3), (8, 0)):
+        bad = bytearray(b)
+        bad[off] = val
+        with pytest.raises(cg.CgError) as e:
+            cg.cg_chunk_info_parse(bytes(bad))
+        assert e.value.code == cg.CG_E_INVAL
+    with pytest.raises(cg.CgError):
+        cg.cg_chunk_info_parse(bytes(b[:63]))
+
+
+def test_invalid_params_fail_before_any_gpu_work(cg):
+    lib = cg.lib()
+    out = ctypes.c_void_p()
+    good = dict(layers=2, tokens=64, channels=128, chunk_tokens=64, group_tokens=10,
+                layer_group_end=(2,), layer_step=(0.5,))
+    bad_cases = [dict(layers=0), dict(group_tokens=0), dict(group_tokens=65),
+                 dict(chunk_tokens=70000), dict(layer_group_end=(1,)),
+                 dict(layer_step=(float("nan"),)), dict(quality_mask=0),
+                 dict(quality_mask=8), dict(tokens=1 << 22)]
+    for bad in bad_cases:
+        p = cg.make_params(**{**good, **bad})
+        rc = lib.cg_build_tables(ctypes.byref(p), ctypes.c_void_p(1), ctypes.c_void_p(1), None,
+                                 ctypes.byref(out))
+        assert rc == cg.CG_E_INVAL, (bad, rc, cg.cg_last_error())
+        assert cg.cg_last_error()
+    p = cg.make_params(**good)
+    assert lib.cg_build_tables(ctypes.byref(p), None, None, None, ctypes.byref(out)) == cg.CG_E_INVAL
+
+
+def test_tables_deserialize_validates_host_bytes(cg):
+    lib = cg.lib()
+    out = ctypes.c_void_p()
+    w = synth.workload("tiny")
+    k, v = synth.gen_kv(w)
+    t = bytearray(oracle.build_tables(oracle.params_for(w), k, v))
+    for mutate in (lambda b: b.__setitem__(0, 0), lambda b: b.__delitem__(slice(-4, None)),
+                   lambda b: b.__setitem__(slice(len(b) - 128, len(b) - 126), b"\0\0")):
+        bad = bytearray(t)
+        mutate(bad)
+        buf = ctypes.create_string_buffer(bytes(bad), len(bad))
+        assert lib.cg_tables_deserialize(buf, len(bad), ctypes.byref(out)) == cg.CG_E_INVAL
