@@ -25,6 +25,13 @@ __device__ __forceinline__ int ld8s(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return (int)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
 }
 
+__device__ __forceinline__ uint32_t lds16(const uint8_t* base, uint32_t byte_off) {
+  return *reinterpret_cast<const uint16_t*>(base + byte_off);
+}
+
+// Row stride of an LDS table image: entry k of every lane lives in row k.
+constexpr uint32_t kRow = 2 * kLanes;
+
 __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
   __shared__ uint16_t tab[kImgRows * kLanes];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -49,11 +56,9 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
 
   const int c = cb * kLanes + lane;
   const bool active = c < a.C;
-  const size_t pi = (size_t)row * a.C + (active ? c : 0);
-  const float scale_a = a.scale_a[pi];
-  const float step = a.step[q][pi];
 
   // start of this lane's stream: row offset + lengths of the streams before it
+  // (the whole wave takes part in the prefix sums)
   const uint32_t len_base = ch.off_len + 2u * (uint32_t)row * (uint32_t)a.C;
   uint32_t before = 0;
   for (int j = lane; j < cb * kLanes; j += kLanes) before += ld16(rs, len_base + 2u * j);
@@ -64,61 +69,92 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
     const uint32_t y = __shfl_up(incl, o);
     if (lane >= o) incl += y;
   }
+  if (!active) return;  // no cross-lane work below
   const uint32_t start = ld32(rs, 64u + 4u * row) + before + incl - my_len;
-  uint32_t bad = (active && (uint64_t)start + my_len > ch.W) ? 1u : 0u;
+  uint32_t bad = ((uint64_t)start + my_len > ch.W) ? 1u : 0u;
 
-  // bit reader: `code` is the 32-bit window, `buf` the next 32..64 bits (most
-  // significant first), `nxt` the word after them, already in flight
+  const size_t pi = (size_t)row * a.C + c;
+  const float scale_a = a.scale_a[pi];
+  const float step = a.step[q][pi];
+  const float step_row = step * (1.0f / kRow);  // exact: a power-of-two scaling
+
+  const uint8_t* tb = reinterpret_cast<const uint8_t*>(tab);
+  const uint32_t lane_addr = 2u * lane_slot(lane);      // LDS byte address of cum[0]
+  const uint32_t key32 = lds16(tb, lane_addr + 32u * kRow);  // root of the search, kept in a register
+
+  // bit reader: `code` is the 32-bit window, b1:b0 the next nb bits (most
+  // significant first; 32..64 before every pair of symbols), `nxt` the word
+  // after them, already in flight
   uint32_t wof = ch.off_pay + 4u * start;
   uint32_t code = ld32(rs, wof);
-  uint64_t buf = ((uint64_t)ld32(rs, wof + 4u) << 32) | ld32(rs, wof + 8u);
+  uint32_t b1 = ld32(rs, wof + 4u), b0 = ld32(rs, wof + 8u);
   uint32_t nxt = ld32(rs, wof + 12u);
   wof += 16u;
   int nb = 64;
   uint32_t range = 0xFFFFFFFFu;
 
-  const uint8_t* tb = reinterpret_cast<const uint8_t*>(tab) + 2 * lane_slot(lane);
-  uint16_t* out = (kv ? a.v_out : a.k_out) + ((size_t)l * a.T + ch.t0) * a.C + c;
+  // output rows of this (kv, layer, chunk) through a buffer resource: the lane's
+  // channel is the vector offset, the token row a wave-uniform scalar offset
+  uint16_t* const out_base = (kv ? a.v_out : a.k_out) + ((size_t)l * a.T + ch.t0) * a.C;
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+      out_base, 0, (int)((uint32_t)ch.tc * (uint32_t)a.C * 2u), kBufRsrcWord3);
+  const uint32_t row_bytes = 2u * (uint32_t)a.C;
+  const uint32_t lane_off = 2u * (uint32_t)c;
   const uint32_t anc_base = ch.off_anchor + (uint32_t)row * (uint32_t)ch.ng * (uint32_t)a.C + c;
+  int anc_next = ld8s(rs, anc_base);
+
+  // one symbol: search, interval update, renormalisation, reconstruction
+  auto symbol = [&](uint32_t soff, float base) {
+    const uint32_t r = range >> kProbBits;
+    // largest s with r * cum[s] <= code; `ad` is the LDS address of cum[s]
+    uint32_t ad = (mul24(r, key32) <= code) ? lane_addr + 32u * kRow : lane_addr;
+#pragma unroll
+    for (uint32_t stp = 16; stp; stp >>= 1) {
+      if (mul24(r, lds16(tb, ad + stp * kRow)) <= code) ad += stp * kRow;
+    }
+    const uint32_t lo = mul24(r, lds16(tb, ad));
+    const uint32_t hi = mul24(r, lds16(tb, ad + kRow));
+    code -= lo;
+    range = hi - lo;
+    // shift in whole bytes until range >= 2^24 (0, 1 or 2 bytes; range > 0)
+    const uint32_t sh = (uint32_t)__builtin_clz(range) & 24u;
+    const uint64_t w_hi = ((uint64_t)code << 32) | b1;
+    const uint64_t w_lo = (((uint64_t)b1 << 32) | b0) << sh;
+    code = (uint32_t)((w_hi << sh) >> 32);
+    b1 = (uint32_t)(w_lo >> 32);
+    b0 = (uint32_t)w_lo;
+    nb -= (int)sh;
+    range <<= sh;
+    // (ad - lane_addr) = s * kRow, so this is fma(s, step, base) exactly
+    const float y = __builtin_fmaf((float)(ad - lane_addr), step_row, base);
+    __builtin_amdgcn_raw_buffer_store_b16(float_to_half_bits(y), ro, lane_off, soff, 0);
+  };
 
   for (int g = 0; g < ch.ng; g++) {
     const int ta = g * a.G, te = min(ta + a.G, ch.tc);
-    const float ahat = anchor_value(ld8s(rs, anc_base + (uint32_t)g * a.C), scale_a);
-    if (active) out[(size_t)ta * a.C] = float_to_half_bits(ahat);
+    const int anc = anc_next;
+    if (g + 1 < ch.ng) anc_next = ld8s(rs, anc_base + (uint32_t)(g + 1) * a.C);
+    const float ahat = anchor_value(anc, scale_a);
+    __builtin_amdgcn_raw_buffer_store_b16(float_to_half_bits(ahat), ro, lane_off,
+                                          (uint32_t)ta * row_bytes, 0);
     const float base = __builtin_fmaf(-32.0f, step, ahat);
-    for (int t = ta + 1; t < te; t++) {
-      const uint32_t r = range >> kProbBits;
-      bad |= ((r << kProbBits) <= code) ? 1u : 0u;
-      // largest s with r * cum[s] <= code, by bisection over the LDS column
-      uint32_t s = 0;
-#pragma unroll
-      for (uint32_t stp = 32; stp; stp >>= 1) {
-        const uint32_t key = *reinterpret_cast<const uint16_t*>(tb + (s + stp) * (2 * kLanes));
-        if (mul24(r, key) <= code) s += stp;
-      }
-      const uint32_t c0 = *reinterpret_cast<const uint16_t*>(tb + s * (2 * kLanes));
-      const uint32_t c1 = *reinterpret_cast<const uint16_t*>(tb + (s + 1) * (2 * kLanes));
-      code -= mul24(r, c0);
-      range = mul24(r, c1 - c0);
-      // shift in whole bytes until range >= 2^24 (0, 1 or 2 bytes)
-      const uint32_t sh = __clz(range) & 24u;
-      const uint64_t win = ((uint64_t)code << 32) | (uint32_t)(buf >> 32);
-      code = (uint32_t)((win << sh) >> 32);
-      buf <<= sh;
-      nb -= (int)sh;
-      range <<= sh;
-      if (nb <= 32) {
-        buf |= (uint64_t)nxt << (32 - nb);
+    for (int t = ta + 1; t < te; t += 2) {
+      // at least 32 buffered bits cover the next two symbols (16 bits each at most)
+      if (nb < 32) {
+        const uint64_t add = (uint64_t)nxt << (32 - nb);
+        b1 |= (uint32_t)(add >> 32);
+        b0 |= (uint32_t)add;
         nb += 32;
         nxt = ld32(rs, wof);
         wof += 4u;
       }
-      if (active) out[(size_t)t * a.C] = float_to_half_bits(__builtin_fmaf((float)s, step, base));
+      symbol((uint32_t)t * row_bytes, base);
+      if (t + 1 < te) symbol((uint32_t)(t + 1) * row_bytes, base);
     }
   }
-  if (__any(bad & (active ? 1u : 0u))) {
-    if (lane == 0) atomicOr(a.status, 1u);
-  }
+  // a valid stream keeps code < range throughout; a corrupt one breaks it for good
+  bad |= (code >= range) ? 1u : 0u;
+  if (bad) atomicOr(a.status, 1u);
 }
 
 }  // namespace
