@@ -124,6 +124,16 @@ int cg_encode(const cg_tables* tables, const void* k_dev, const void* v_dev,
               int32_t chunk, int32_t quality, void* out_dev, size_t cap,
               size_t* out_len, void* stream);
 
+/* Encodes n (chunk, quality) blobs of the same K/V as cg_encode does, in as few
+ * kernel launches as the encode scratch allows (all streams of up to 16 blobs in
+ * flight together), waiting for the stream once at the end.  outs_dev[i] (caps[i]
+ * bytes) receives blob i and out_lens[i] its size (0 for a blob that failed).
+ * Every argument is checked before any launch; on a per-blob failure (capacity,
+ * non-finite input) the first such error is returned after the others finished. */
+int cg_encode_batch(const cg_tables* tables, const void* k_dev, const void* v_dev, int32_t n,
+                    const int32_t* chunks, const int32_t* qualities, void* const* outs_dev,
+                    const size_t* caps, size_t* out_lens, void* stream);
+
 /* Parses and checks a blob header from host memory (len >= 64). Host only. */
 int cg_chunk_info_parse(const void* blob_host, size_t len, cg_chunk_info* out);
 

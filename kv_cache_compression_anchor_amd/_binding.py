@@ -22,7 +22,7 @@ _NAMES = {0: "CG_OK", -1: "CG_E_INVAL", -2: "CG_E_NOMEM", -3: "CG_E_HIP", -4: "C
 
 EXPORTS = ["cg_build_tables", "cg_tables_free", "cg_tables_serialize", "cg_tables_deserialize",
            "cg_tables_id", "cg_tables_params", "cg_num_chunks", "cg_encode_bound", "cg_encode",
-           "cg_chunk_info_parse", "cg_decode", "cg_decode_async", "cg_decode_streamed",
+           "cg_encode_batch", "cg_chunk_info_parse", "cg_decode", "cg_decode_async", "cg_decode_streamed",
            "cg_last_error"]
 
 
@@ -70,6 +70,8 @@ def lib():
             "cg_num_chunks": (I, [P, C.POINTER(I32)]),
             "cg_encode_bound": (I, [P, I32, C.POINTER(SZ)]),
             "cg_encode": (I, [P, P, P, I32, I32, P, SZ, C.POINTER(SZ), P]),
+            "cg_encode_batch": (I, [P, P, P, I32, C.POINTER(I32), C.POINTER(I32), C.POINTER(P),
+                                    C.POINTER(SZ), C.POINTER(SZ), P]),
             "cg_chunk_info_parse": (I, [P, SZ, C.POINTER(cg_chunk_info)]),
             "cg_decode": (I, [P, I32, C.POINTER(P), C.POINTER(SZ), P, P, P]),
             "cg_decode_async": (I, [P, I32, C.POINTER(P), C.POINTER(cg_chunk_info), P, P, P, P]),
@@ -219,6 +221,25 @@ def cg_encode(t: Tables, k, v, chunk: int, quality: int, out, stream=None) -> in
     _check(lib().cg_encode(t.handle, kp, vp, chunk, quality, op, out.numel(), C.byref(n),
                            _stream(stream)))
     return n.value
+
+
+def cg_encode_batch(t: Tables, k, v, chunks, qualities, outs, stream=None):
+    """Encodes blob i = (chunks[i], qualities[i]) into the uint8 device tensor outs[i];
+    returns the blob sizes."""
+    import torch
+    n = len(chunks)
+    if len(qualities) != n or len(outs) != n:
+        raise ValueError("one quality and one output per chunk")
+    kp = _dev_ptr(k, torch.float16, "k")
+    vp = _dev_ptr(v, torch.float16, "v")
+    ops = [_dev_ptr(o, torch.uint8, "out") for o in outs]
+    carr = (C.c_int32 * max(1, n))(*chunks)
+    qarr = (C.c_int32 * max(1, n))(*qualities)
+    caps = (C.c_size_t * max(1, n))(*[o.numel() for o in outs])
+    lens = (C.c_size_t * max(1, n))()
+    _check(lib().cg_encode_batch(t.handle, kp, vp, n, carr, qarr, _ptr_array(ops), caps, lens,
+                                 _stream(stream)))
+    return [int(x) for x in lens[:n]]
 
 
 def cg_chunk_info_parse(blob_host) -> cg_chunk_info:

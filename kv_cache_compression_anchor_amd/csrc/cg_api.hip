@@ -18,12 +18,16 @@ struct cg_tables {
   int dev = 0;
   DevTables t;
   uint64_t id = 0;
-  std::mutex mu;  // guards the encode scratch
-  uint32_t* scratch = nullptr;
+  std::mutex mu;  // guards the encode buffers and the status words
+  uint32_t* scratch = nullptr;   // per launch slot: [2][L][C] streams of swb words
   size_t scratch_words = 0;
-  uint32_t* lens = nullptr;      // [2][L][C]
-  uint32_t* row_words = nullptr; // [2L]
-  uint32_t* status = nullptr;    // device words: W, flags, decode status
+  uint32_t* lens = nullptr;      // per launch slot: [2][L][C]
+  uint32_t* row_words = nullptr; // per launch slot: [2L]
+  int enc_slots = 0;             // blobs one encode launch can hold
+  uint32_t* enc_status = nullptr;   // per blob of a batch: W, too large, non-finite, pad
+  uint32_t* enc_host = nullptr;     // pinned mirror
+  int enc_status_cap = 0;
+  uint32_t* status = nullptr;    // device words: id scratch, decode status
   uint32_t* host_status = nullptr;  // pinned mirror
 };
 
@@ -138,6 +142,8 @@ void free_tables(cg_tables* t) {
   if (t->scratch) (void)hipFree(t->scratch);
   if (t->lens) (void)hipFree(t->lens);
   if (t->row_words) (void)hipFree(t->row_words);
+  if (t->enc_status) (void)hipFree(t->enc_status);
+  if (t->enc_host) (void)hipHostFree(t->enc_host);
   if (t->status) (void)hipFree(t->status);
   if (t->host_status) (void)hipHostFree(t->host_status);
   delete t;
@@ -484,67 +490,117 @@ int cg_encode_bound(const cg_tables* h, int32_t chunk, size_t* max_bytes) {
   return CG_OK;
 }
 
-int cg_encode(const cg_tables* ch, const void* k_dev, const void* v_dev, int32_t chunk,
-              int32_t quality, void* out_dev, size_t cap, size_t* out_len, void* stream) {
-  if (!ch || !k_dev || !v_dev || !out_dev || !out_len) return fail(CG_E_INVAL, "NULL argument");
+// Scratch memory the encoder may hold: the blobs of one launch share it.
+constexpr size_t kEncScratchBudget = (size_t)3 << 30;
+
+int cg_encode_batch(const cg_tables* ch, const void* k_dev, const void* v_dev, int32_t n,
+                    const int32_t* chunks, const int32_t* qualities, void* const* outs_dev,
+                    const size_t* caps, size_t* out_lens, void* stream) {
+  if (!ch || !k_dev || !v_dev || n < 0 || (n > 0 && (!chunks || !qualities || !outs_dev ||
+                                                      !caps || !out_lens)))
+    return fail(CG_E_INVAL, "NULL argument");
   cg_tables* h = const_cast<cg_tables*>(ch);
   const DevTables& t = h->t;
-  if (chunk < 0 || chunk >= n_chunks_of(t)) return fail(CG_E_INVAL, "chunk out of range");
-  if (quality < 0 || quality > 2 || !((t.mask >> quality) & 1u))
-    return fail(CG_E_MISMATCH, "quality not in the tables");
-  const ChunkGeo g = chunk_geo(t, chunk);
-  const BlobLayout bl = blob_layout(t.L, t.C, g.ng);
-  if (cap < bl.off_pay + 16) return fail(CG_E_CAPACITY, "output smaller than the blob's fixed part");
+  for (int i = 0; i < n; i++) {
+    if (!outs_dev[i]) return fail(CG_E_INVAL, "NULL output");
+    if (chunks[i] < 0 || chunks[i] >= n_chunks_of(t)) return fail(CG_E_INVAL, "chunk out of range");
+    if (qualities[i] < 0 || qualities[i] > 2 || !((t.mask >> qualities[i]) & 1u))
+      return fail(CG_E_MISMATCH, "quality not in the tables");
+    const ChunkGeo g = chunk_geo(t, chunks[i]);
+    if (caps[i] < blob_layout(t.L, t.C, g.ng).off_pay + 16)
+      return fail(CG_E_CAPACITY, "output smaller than the blob's fixed part");
+  }
+  if (n == 0) return CG_OK;
   DeviceGuard dg(h->dev);
   if (!dg.ok) return fail(CG_E_HIP, "cannot select the tables' device");
   std::lock_guard<std::mutex> lk(h->mu);
-  const size_t swb = stream_words_bound(t.CH - (t.CH + t.G - 1) / t.G);
-  const size_t need = t.lay.n * std::max<size_t>(swb, 1);
-  if (h->scratch_words < need) {
+  const size_t swb = std::max<size_t>(stream_words_bound(t.CH - (t.CH + t.G - 1) / t.G), 1);
+  const size_t slot_words = t.lay.n * swb;
+  const int slots = (int)std::max<size_t>(
+      1, std::min<size_t>({(size_t)kEncMaxBlobs, (size_t)n, kEncScratchBudget / (4 * slot_words)}));
+  if (h->enc_slots < slots) {
     if (h->scratch) (void)hipFree(h->scratch);
+    if (h->lens) (void)hipFree(h->lens);
+    if (h->row_words) (void)hipFree(h->row_words);
     h->scratch = nullptr;
-    h->scratch_words = 0;
-    if (hipMalloc(&h->scratch, need * 4) != hipSuccess) return fail(CG_E_NOMEM, "encode scratch");
-    h->scratch_words = need;
+    h->lens = h->row_words = nullptr;
+    h->enc_slots = 0;
+    if (hipMalloc(&h->scratch, 4 * slot_words * slots) != hipSuccess ||
+        hipMalloc(&h->lens, 4 * t.lay.n * slots) != hipSuccess ||
+        hipMalloc(&h->row_words, 8 * (size_t)t.L * slots) != hipSuccess)
+      return fail(CG_E_NOMEM, "encode scratch");
+    h->enc_slots = slots;
   }
-  if (!h->lens) {
-    HIP_TRY(hipMalloc(&h->lens, 4 * t.lay.n), "hipMalloc(lens)");
-    HIP_TRY(hipMalloc(&h->row_words, 8 * (size_t)t.L), "hipMalloc(rows)");
+  if (h->enc_status_cap < n) {
+    if (h->enc_status) (void)hipFree(h->enc_status);
+    if (h->enc_host) (void)hipHostFree(h->enc_host);
+    h->enc_status = h->enc_host = nullptr;
+    h->enc_status_cap = 0;
+    if (hipMalloc(&h->enc_status, 16 * (size_t)n) != hipSuccess ||
+        hipHostMalloc(&h->enc_host, 16 * (size_t)n, hipHostMallocDefault) != hipSuccess)
+      return fail(CG_E_NOMEM, "encode status");
+    h->enc_status_cap = n;
   }
-  EncodeArgs a;
-  a.k = static_cast<const uint16_t*>(k_dev);
-  a.v = static_cast<const uint16_t*>(v_dev);
-  a.L = t.L;
-  a.T = t.T;
-  a.C = t.C;
-  a.G = t.G;
-  a.nblk = t.nblk;
-  a.t0 = g.t0;
-  a.tc = g.tc;
-  a.ng = g.ng;
-  a.q = quality;
-  a.scale_a = reinterpret_cast<const float*>(t.ser + t.lay.off_scale_a);
-  a.inv_a = reinterpret_cast<const float*>(t.ser + t.lay.off_inv_a);
-  a.inv_step = reinterpret_cast<const float*>(t.ser + t.lay.off_inv_step[quality]);
-  a.img = t.img[quality];
-  a.scratch = h->scratch;
-  a.swb = std::max<size_t>(swb, 1);
-  a.lens = h->lens;
-  a.blob = static_cast<uint8_t*>(out_dev);
-  a.lay = bl;
-  a.row_words = h->row_words;
-  a.status = h->status;
-  a.cap = cap;
-  a.tables_id = h->id;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  HIP_TRY(hipMemsetAsync(h->status, 0, 12, st), "clear status");
-  HIP_TRY(launch_encode(a, st), "encode launch");
-  HIP_TRY(hipMemcpyAsync(h->host_status, h->status, 12, hipMemcpyDeviceToHost, st), "encode status");
+  HIP_TRY(hipMemsetAsync(h->enc_status, 0, 16 * (size_t)n, st), "clear status");
+  for (int i0 = 0; i0 < n; i0 += slots) {
+    EncodeArgs a;
+    memset(&a, 0, sizeof(a));
+    a.k = static_cast<const uint16_t*>(k_dev);
+    a.v = static_cast<const uint16_t*>(v_dev);
+    a.L = t.L;
+    a.T = t.T;
+    a.C = t.C;
+    a.G = t.G;
+    a.nblk = t.nblk;
+    a.nblobs = std::min(slots, n - i0);
+    a.unit_blocks = (uint32_t)((2 * t.L * t.nblk + 3) / 4);
+    a.swb = swb;
+    a.scale_a = reinterpret_cast<const float*>(t.ser + t.lay.off_scale_a);
+    a.inv_a = reinterpret_cast<const float*>(t.ser + t.lay.off_inv_a);
+    a.tables_id = h->id;
+    for (int j = 0; j < a.nblobs; j++) {
+      const int i = i0 + j;
+      const ChunkGeo g = chunk_geo(t, chunks[i]);
+      EncBlob& B = a.b[j];
+      B.blob = static_cast<uint8_t*>(outs_dev[i]);
+      B.cap = caps[i];
+      B.t0 = g.t0;
+      B.tc = g.tc;
+      B.ng = g.ng;
+      B.q = qualities[i];
+      B.lay = blob_layout(t.L, t.C, g.ng);
+      B.img = t.img[qualities[i]];
+      B.inv_step = reinterpret_cast<const float*>(t.ser + t.lay.off_inv_step[qualities[i]]);
+      B.scratch = h->scratch + (size_t)j * slot_words;
+      B.lens = h->lens + (size_t)j * t.lay.n;
+      B.row_words = h->row_words + (size_t)j * 2 * t.L;
+      B.status = h->enc_status + 4 * (size_t)i;
+    }
+    HIP_TRY(launch_encode(a, st), "encode launch");
+  }
+  HIP_TRY(hipMemcpyAsync(h->enc_host, h->enc_status, 16 * (size_t)n, hipMemcpyDeviceToHost, st),
+          "encode status");
   HIP_TRY(hipStreamSynchronize(st), "encode");
-  if (h->host_status[2]) return fail(CG_E_INVAL, "K/V hold a non-finite value");
-  if (h->host_status[1]) return fail(CG_E_CAPACITY, "blob larger than the output buffer");
-  *out_len = blob_bytes(bl, h->host_status[0]);
-  return CG_OK;
+  int rc = CG_OK;
+  for (int i = 0; i < n; i++) {
+    const uint32_t* sw = h->enc_host + 4 * (size_t)i;
+    out_lens[i] = 0;
+    if (sw[2]) {
+      if (rc == CG_OK) rc = fail(CG_E_INVAL, "K/V hold a non-finite value");
+    } else if (sw[1]) {
+      if (rc == CG_OK) rc = fail(CG_E_CAPACITY, "blob larger than the output buffer");
+    } else {
+      out_lens[i] = blob_bytes(blob_layout(t.L, t.C, chunk_geo(t, chunks[i]).ng), sw[0]);
+    }
+  }
+  return rc;
+}
+
+int cg_encode(const cg_tables* h, const void* k_dev, const void* v_dev, int32_t chunk,
+              int32_t quality, void* out_dev, size_t cap, size_t* out_len, void* stream) {
+  if (!out_len) return fail(CG_E_INVAL, "NULL argument");
+  return cg_encode_batch(h, k_dev, v_dev, 1, &chunk, &quality, &out_dev, &cap, out_len, stream);
 }
 
 int cg_chunk_info_parse(const void* blob_host, size_t len, cg_chunk_info* out) {

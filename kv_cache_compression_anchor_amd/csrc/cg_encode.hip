@@ -77,13 +77,18 @@ __device__ __forceinline__ void rc_finish(RcEnc& e, uint32_t* out) {
   if (e.nacc) out[e.nw++] = e.acc << (8 * (4 - e.nacc));
 }
 
+// One wave per (blob, kv, layer, 64-channel block); a launch covers up to
+// kEncMaxBlobs (chunk, quality) blobs of the same tensors so that enough waves are
+// in flight to hide the latency of each lane's serial coder.
 __global__ __launch_bounds__(kLanes * kEncWaves) void k_encode(EncodeArgs a) {
   __shared__ uint16_t tab[kEncWaves][kImgRows * kLanes];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int bi = blockIdx.x / a.unit_blocks;
+  const EncBlob& B = a.b[bi];
   const int units = 2 * a.L * a.nblk;
-  const int unit = blockIdx.x * kEncWaves + wave;
+  const int unit = (blockIdx.x % a.unit_blocks) * kEncWaves + wave;
   if (unit < units) {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.img + (size_t)unit * kImgRows * kLanes);
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(B.img + (size_t)unit * kImgRows * kLanes);
     uint32_t* dst = reinterpret_cast<uint32_t*>(tab[wave]);
     for (int j = lane; j < kImgRows * kLanes / 2; j += kLanes) dst[j] = src[j];
   }
@@ -95,16 +100,16 @@ __global__ __launch_bounds__(kLanes * kEncWaves) void k_encode(EncodeArgs a) {
   const int c = cb * kLanes + lane;
   if (c >= a.C) return;
   const size_t pi = ((size_t)kv * a.L + l) * a.C + c;
-  const float scale_a = a.scale_a[pi], inv_a = a.inv_a[pi], inv_step = a.inv_step[pi];
-  const uint16_t* x = (kv ? a.v : a.k) + ((size_t)l * a.T + a.t0) * a.C + c;
+  const float scale_a = a.scale_a[pi], inv_a = a.inv_a[pi], inv_step = B.inv_step[pi];
+  const uint16_t* x = (kv ? a.v : a.k) + ((size_t)l * a.T + B.t0) * a.C + c;
   const uint8_t* tb = reinterpret_cast<const uint8_t*>(tab[wave]) + 2 * lane_slot(lane);
-  uint32_t* out = a.scratch + pi * a.swb;
-  int8_t* anchors = reinterpret_cast<int8_t*>(a.blob + a.lay.off_anchor) +
-                    ((size_t)kv * a.L + l) * a.ng * a.C + c;
+  uint32_t* out = B.scratch + pi * a.swb;
+  int8_t* anchors = reinterpret_cast<int8_t*>(B.blob + B.lay.off_anchor) +
+                    ((size_t)kv * a.L + l) * B.ng * a.C + c;
   RcEnc e = {0, 0xFFFFFFFFu, 0, 0, 0, 0, 0, 0};
   uint32_t nonfinite = 0;
-  for (int g = 0; g < a.ng; g++) {
-    const int ta = g * a.G, te = min(ta + a.G, a.tc);
+  for (int g = 0; g < B.ng; g++) {
+    const int ta = g * a.G, te = min(ta + a.G, B.tc);
     const uint16_t ha = x[(size_t)ta * a.C];
     nonfinite |= (ha & 0x7C00u) == 0x7C00u;
     const int av = quant_anchor(half_bits_to_float(ha), inv_a);
@@ -119,48 +124,50 @@ __global__ __launch_bounds__(kLanes * kEncWaves) void k_encode(EncodeArgs a) {
       rc_put(e, c0, c1 - c0, out);
     }
   }
-  if (a.tc > a.ng) rc_finish(e, out);  // a stream without symbols stays empty
-  if (nonfinite) atomicOr(&a.status[2], 1u);
-  a.lens[pi] = e.nw;
-  reinterpret_cast<uint16_t*>(a.blob + a.lay.off_len)[pi] = (uint16_t)e.nw;
+  if (B.tc > B.ng) rc_finish(e, out);  // a stream without symbols stays empty
+  if (nonfinite) atomicOr(&B.status[2], 1u);
+  B.lens[pi] = e.nw;
+  reinterpret_cast<uint16_t*>(B.blob + B.lay.off_len)[pi] = (uint16_t)e.nw;
 }
 
-// words of every (kv, layer) row
-__global__ __launch_bounds__(256) void k_row_totals(const uint32_t* lens, int C, uint32_t* row_words) {
+// words of every (kv, layer) row of every blob
+__global__ __launch_bounds__(256) void k_row_totals(EncodeArgs a) {
   __shared__ uint32_t part[4];
-  const uint32_t* r = lens + (size_t)blockIdx.x * C;
+  const EncBlob& B = a.b[blockIdx.y];
+  const uint32_t* r = B.lens + (size_t)blockIdx.x * a.C;
   uint32_t s = 0;
-  for (int j = threadIdx.x; j < C; j += 256) s += r[j];
+  for (int j = threadIdx.x; j < a.C; j += 256) s += r[j];
   for (int o = 32; o; o >>= 1) s += __shfl_xor(s, o);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
   __syncthreads();
-  if (threadIdx.x == 0) row_words[blockIdx.x] = part[0] + part[1] + part[2] + part[3];
+  if (threadIdx.x == 0) B.row_words[blockIdx.x] = part[0] + part[1] + part[2] + part[3];
 }
 
-// row offsets, payload size, header, zero padding; flags a blob larger than cap
+// per blob: row offsets, payload size, header; flags a blob larger than cap
 __global__ void k_row_scan(EncodeArgs a) {
   if (threadIdx.x != 0) return;
+  const EncBlob& B = a.b[blockIdx.x];
   const int rows = 2 * a.L;
-  uint32_t* row_off = reinterpret_cast<uint32_t*>(a.blob + a.lay.off_rows);
+  uint32_t* row_off = reinterpret_cast<uint32_t*>(B.blob + B.lay.off_rows);
   uint64_t w = 0;
   for (int r = 0; r < rows; r++) {
     row_off[r] = (uint32_t)w;
-    w += a.row_words[r];
+    w += B.row_words[r];
   }
-  const size_t total = blob_bytes(a.lay, w);
-  a.status[0] = (uint32_t)w;
-  a.status[1] = (total > a.cap || w > 0x3FFFFFFFull) ? 1u : 0u;
-  uint32_t* h = reinterpret_cast<uint32_t*>(a.blob);
+  const size_t total = blob_bytes(B.lay, w);
+  B.status[0] = (uint32_t)w;
+  B.status[1] = (total > B.cap || w > 0x3FFFFFFFull) ? 1u : 0u;
+  uint32_t* h = reinterpret_cast<uint32_t*>(B.blob);
   h[0] = kBlobMagic;
   h[1] = 1;
   h[2] = (uint32_t)a.L;
   h[3] = (uint32_t)a.C;
   h[4] = (uint32_t)a.T;
-  h[5] = (uint32_t)a.t0;
-  h[6] = (uint32_t)a.tc;
+  h[5] = (uint32_t)B.t0;
+  h[6] = (uint32_t)B.tc;
   h[7] = (uint32_t)a.G;
-  h[8] = (uint32_t)a.ng;
-  h[9] = (uint32_t)a.q;
+  h[8] = (uint32_t)B.ng;
+  h[9] = (uint32_t)B.q;
   h[10] = (uint32_t)w;
   h[11] = kProbBits;
   h[12] = (uint32_t)a.tables_id;
@@ -171,62 +178,68 @@ __global__ void k_row_scan(EncodeArgs a) {
 
 // zero the gap before the payload and the tail after it
 __global__ __launch_bounds__(256) void k_pad(EncodeArgs a) {
-  if (a.status[1]) return;
-  const size_t W = a.status[0];
-  const size_t gap0 = a.lay.off_len + 4 * (size_t)a.L * a.C, gap1 = a.lay.off_pay;
-  const size_t tail0 = a.lay.off_pay + 4 * W, tail1 = blob_bytes(a.lay, W);
-  for (size_t j = gap0 + threadIdx.x; j < gap1; j += 256) a.blob[j] = 0;
-  for (size_t j = tail0 + threadIdx.x; j < tail1; j += 256) a.blob[j] = 0;
+  const EncBlob& B = a.b[blockIdx.x];
+  if (B.status[1]) return;
+  const size_t W = B.status[0];
+  const size_t gap0 = B.lay.off_len + 4 * (size_t)a.L * a.C, gap1 = B.lay.off_pay;
+  const size_t tail0 = B.lay.off_pay + 4 * W, tail1 = blob_bytes(B.lay, W);
+  for (size_t j = gap0 + threadIdx.x; j < gap1; j += 256) B.blob[j] = 0;
+  for (size_t j = tail0 + threadIdx.x; j < tail1; j += 256) B.blob[j] = 0;
 }
 
-// Pack one row: block-wide exclusive prefix sum of the stream lengths (wave
-// scans plus the wave totals), then each wave copies whole streams with
-// coalesced 64-word moves.
+// Pack 256 streams of one row: the row offset plus the lengths of the row's
+// earlier streams, then a block-wide exclusive prefix sum (wave scans plus the
+// wave totals); each wave copies whole streams with coalesced 64-word moves.
 __global__ __launch_bounds__(256) void k_pack(EncodeArgs a) {
-  if (a.status[1]) return;
+  const EncBlob& B = a.b[blockIdx.y];
+  if (B.status[1]) return;
   __shared__ uint32_t wsum[4];
   __shared__ uint32_t soff[256];
   __shared__ uint32_t slen[256];
-  const int row = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const uint32_t* lens = a.lens + (size_t)row * a.C;
-  uint32_t* pay = reinterpret_cast<uint32_t*>(a.blob + a.lay.off_pay);
-  uint32_t base = reinterpret_cast<const uint32_t*>(a.blob + a.lay.off_rows)[row];
-  for (int c0 = 0; c0 < a.C; c0 += 256) {
-    const int c = c0 + tid;
-    const uint32_t len = c < a.C ? lens[c] : 0u;
-    uint32_t incl = len;
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    uint32_t before = base;
-    for (int w = 0; w < wave; w++) before += wsum[w];
-    soff[tid] = before + incl - len;
-    slen[tid] = len;
-    const uint32_t chunk_total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    __syncthreads();
-    const int n = min(256, a.C - c0);
-    for (int j = wave; j < n; j += 4) {
-      const uint32_t* src = a.scratch + ((size_t)row * a.C + c0 + j) * a.swb;
-      uint32_t* dst = pay + soff[j];
-      for (uint32_t k = lane; k < slen[j]; k += 64) dst[k] = src[k];
-    }
-    base += chunk_total;
-    __syncthreads();
+  const int nseg = (a.C + 255) / 256;
+  const int row = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const uint32_t* lens = B.lens + (size_t)row * a.C;
+  uint32_t before = 0;
+  for (int j = tid; j < seg * 256; j += 256) before += lens[j];
+  for (int o = 32; o; o >>= 1) before += __shfl_xor(before, o);
+  if (lane == 0) wsum[wave] = before;
+  __syncthreads();
+  const uint32_t base = reinterpret_cast<const uint32_t*>(B.blob + B.lay.off_rows)[row] +
+                        wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  __syncthreads();
+  const int c = seg * 256 + tid;
+  const uint32_t len = c < a.C ? lens[c] : 0u;
+  uint32_t incl = len;
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t off = base;
+  for (int w = 0; w < wave; w++) off += wsum[w];
+  soff[tid] = off + incl - len;
+  slen[tid] = len;
+  __syncthreads();
+  uint32_t* pay = reinterpret_cast<uint32_t*>(B.blob + B.lay.off_pay);
+  const int n = min(256, a.C - seg * 256);
+  for (int j = wave; j < n; j += 4) {
+    const uint32_t* src = B.scratch + ((size_t)row * a.C + seg * 256 + j) * a.swb;
+    uint32_t* dst = pay + soff[j];
+    for (uint32_t k = lane; k < slen[j]; k += 64) dst[k] = src[k];
   }
 }
 
 }  // namespace
 
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t st) {
-  const int units = 2 * a.L * a.nblk;
-  k_encode<<<(units + kEncWaves - 1) / kEncWaves, kLanes * kEncWaves, 0, st>>>(a);
-  k_row_totals<<<2 * a.L, 256, 0, st>>>(a.lens, a.C, a.row_words);
-  k_row_scan<<<1, 64, 0, st>>>(a);
-  k_pad<<<1, 256, 0, st>>>(a);
-  k_pack<<<2 * a.L, 256, 0, st>>>(a);
+  const unsigned nb = (unsigned)a.nblobs;
+  k_encode<<<nb * a.unit_blocks, kLanes * kEncWaves, 0, st>>>(a);
+  k_row_totals<<<dim3(2 * a.L, nb), 256, 0, st>>>(a);
+  k_row_scan<<<nb, 64, 0, st>>>(a);
+  k_pad<<<nb, 256, 0, st>>>(a);
+  k_pack<<<dim3(2 * a.L * ((a.C + 255) / 256), nb), 256, 0, st>>>(a);
   return hipGetLastError();
 }
 

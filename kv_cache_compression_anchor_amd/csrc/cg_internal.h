@@ -162,24 +162,30 @@ hipError_t launch_images(DevTables& t, hipStream_t st);
 hipError_t launch_tables_id(const DevTables& t, uint64_t* scratch_digests, uint64_t* id_out,
                             hipStream_t st);
 
+constexpr int kEncMaxBlobs = 16;  // blobs per encode launch (kernel-argument descriptors)
+struct EncBlob {
+  uint8_t* blob;      // output
+  size_t cap;
+  int32_t t0, tc, ng, q;
+  uint32_t unit_block0;  // first workgroup of this blob in the encode grid
+  BlobLayout lay;
+  const uint16_t* img;       // cum images of quality q
+  const float* inv_step;     // of quality q
+  uint32_t* scratch;         // per stream: swb words
+  uint32_t* lens;            // [2][L][C] words
+  uint32_t* row_words;       // [2L]
+  uint32_t* status;          // [0] payload words, [1] too large for cap, [2] non-finite input
+};
 struct EncodeArgs {
   const uint16_t* k;
   const uint16_t* v;
-  int L, T, C, G, nblk;
-  int t0, tc, ng, q;
+  int L, T, C, G, nblk, nblobs;
+  uint32_t unit_blocks;  // workgroups per blob
+  size_t swb;
   const float* scale_a;
   const float* inv_a;
-  const float* inv_step;
-  const uint16_t* img;      // cum images of quality q
-  uint32_t* scratch;        // per stream: swb words
-  size_t swb;
-  uint32_t* lens;           // [2][L][C] words
-  uint8_t* blob;            // output
-  BlobLayout lay;
-  uint32_t* row_words;      // [2L]
-  uint32_t* status;         // [0] payload words, [1] too large for cap, [2] non-finite input
-  size_t cap;
   uint64_t tables_id;
+  EncBlob b[kEncMaxBlobs];
 };
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t st);
 
