@@ -239,27 +239,36 @@ static int64_t f16_scaled_int(uint16_t h) {
  * This is the "channel std" unit of the delta step. */
 void cgo_channel_stats(const uint16_t* x, int L, int T, int C, double* sigma,
                        float* absmax, int* nonfinite) {
-  *nonfinite = 0;
+  int nf = 0;
+  /* integer sums do not depend on the order of the terms: layers run in
+   * parallel, tokens in order with one accumulator per channel */
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : nf)
   for (int l = 0; l < L; l++) {
-    for (int c = 0; c < C; c++) {
-      int64_t S1 = 0;
-      unsigned __int128 S2 = 0;
-      uint16_t amax = 0;
-      for (int t = 0; t < T; t++) {
-        uint16_t h = x[((size_t)l * T + t) * C + c];
-        if (((h >> 10) & 31) == 31) { *nonfinite = 1; continue; }
+    int64_t* S1 = (int64_t*)calloc(C, sizeof(int64_t));
+    unsigned __int128* S2 = (unsigned __int128*)calloc(C, sizeof(unsigned __int128));
+    uint16_t* amax = (uint16_t*)calloc(C, sizeof(uint16_t));
+    for (int t = 0; t < T; t++) {
+      const uint16_t* row = x + ((size_t)l * T + t) * C;
+      for (int c = 0; c < C; c++) {
+        uint16_t h = row[c];
+        if (((h >> 10) & 31) == 31) { nf = 1; continue; }
         int64_t X = f16_scaled_int(h);
-        S1 += X;
-        S2 += (unsigned __int128)((__int128)X * X);
-        if ((h & 0x7FFF) > amax) amax = h & 0x7FFF;
+        S1[c] += X;
+        S2[c] += (unsigned __int128)((__int128)X * X);
+        if ((h & 0x7FFF) > amax[c]) amax[c] = h & 0x7FFF;
       }
-      unsigned __int128 num = (unsigned __int128)T * S2 -
-                              (unsigned __int128)((__int128)S1 * S1);
-      double sd = num ? sqrt((double)num) / ((double)T * 16777216.0) : 1.0;
-      sigma[(size_t)l * C + c] = sd;
-      absmax[(size_t)l * C + c] = cgo_f16_to_f32(amax);
     }
+    for (int c = 0; c < C; c++) {
+      unsigned __int128 num = (unsigned __int128)T * S2[c] -
+                              (unsigned __int128)((__int128)S1[c] * S1[c]);
+      sigma[(size_t)l * C + c] = num ? sqrt((double)num) / ((double)T * 16777216.0) : 1.0;
+      absmax[(size_t)l * C + c] = cgo_f16_to_f32(amax[c]);
+    }
+    free(S1);
+    free(S2);
+    free(amax);
   }
+  *nonfinite = nf;
 }
 
 /* ------------------------------------------------------------------------- */
