@@ -1,10 +1,10 @@
 // Chunk decoder (gptget 方法详解: the receiver decodes the bitstream on the GPU;
 // CacheGen blog, section 2.1: anchor plus delta reconstruction).
 //
-// One lane per stream (kv, layer, channel), one wave per chunk, one workgroup
-// per (group of chunks with the same quality, kv, layer, 64-channel block): the
-// workgroup stages the block's 64 cumulative tables in LDS once and every wave
-// decodes its chunk against them.  All lanes of a wave sit on the same token,
+// One lane per stream (kv, layer, channel), one wave per (chunk, kv), one
+// workgroup per (group of chunks with the same quality, layer, 64-channel
+// block): the workgroup stages the block's 2 x 64 cumulative tables (K and V)
+// in LDS once and every wave decodes its chunk's K or V streams against them.  All lanes of a wave sit on the same token,
 // so each reconstructed token row is one coalesced 128-byte store.  Blob bytes
 // are read through a buffer resource bounded by the blob size: a corrupt blob
 // reads zeros past its end instead of faulting.
@@ -29,30 +29,57 @@ __device__ __forceinline__ uint32_t lds16(const uint8_t* base, uint32_t byte_off
   return *reinterpret_cast<const uint16_t*>(base + byte_off);
 }
 
-// Row stride of an LDS table image: entry k of every lane lives in row k.
-constexpr uint32_t kRow = 2 * kLanes;
+// (float)((x >> 8) & 0xFF) in one instruction
+__device__ __forceinline__ float byte1_to_float(uint32_t x) {
+  float f;
+  asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(x));
+  return f;
+}
 
-__global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
-  __shared__ uint16_t tab[kImgRows * kLanes];
+// The workgroup's LDS holds the K and V tables of one (layer, 64-channel block)
+// side by side: row k = [cum[k] of the 64 K streams | cum[k] of the 64 V
+// streams], 256 bytes, so the byte address of entry k of a lane is
+// k * 256 + (kv * 128 + 2 * slot) and bits 8..15 of it are k itself.
+constexpr uint32_t kRow = 4 * kLanes;
+
+// All ones when r * key <= code, else zero.  ncode is ~code, so the 64-bit sum
+// r * key + (2^64 - code - 1) stays within [2^64 - 2^32, 2^64) when
+// r * key <= code and otherwise wraps to r * key - code - 1 < 2^32: its high
+// word is the mask (one v_mad_u64_u32; r * key < 2^32).
+__device__ __forceinline__ uint32_t le_mask(uint32_t r, uint32_t key, uint32_t ncode) {
+  const uint64_t c = 0xFFFFFFFF00000000ull | ncode;
+  return (uint32_t)(((uint64_t)r * key + c) >> 32);
+}
+
+// GS: group size fixed at compile time (0 = the runtime a.G only)
+template <int GS>
+__global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
+  __shared__ uint32_t tab[kImgRows * kLanes];  // [65 rows][K: 64 u16 | V: 64 u16]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int per_grp = 2 * a.L * a.nblk;
+  const int per_grp = a.L * a.nblk;
   const int grp = blockIdx.x / per_grp, rem = blockIdx.x % per_grp;
-  const int kv = rem / (a.L * a.nblk), l = (rem / a.nblk) % a.L, cb = rem % a.nblk;
-  const int row = kv * a.L + l;
+  const int l = rem / a.nblk, cb = rem % a.nblk;
   const int q = a.chunks[a.groups[grp].chunk[0]].q;
   {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(
-        a.img[q] + ((size_t)row * a.nblk + cb) * (kImgRows * kLanes));
-    uint32_t* dst = reinterpret_cast<uint32_t*>(tab);
-    for (int j = tid; j < kImgRows * kLanes / 2; j += blockDim.x) dst[j] = src[j];
+    constexpr size_t img_u32 = kImgRows * kLanes / 2;
+    const uint32_t* src_k = reinterpret_cast<const uint32_t*>(a.img[q]) +
+                            ((size_t)l * a.nblk + cb) * img_u32;
+    const uint32_t* src_v = reinterpret_cast<const uint32_t*>(a.img[q]) +
+                            ((size_t)(a.L + l) * a.nblk + cb) * img_u32;
+    for (int j = tid; j < kImgRows * kLanes; j += blockDim.x) {
+      const int row = j >> 6, half = (j >> 5) & 1, w = j & 31;
+      tab[j] = (half ? src_v : src_k)[row * 32 + w];
+    }
   }
   __syncthreads();
-  const int ci = a.groups[grp].chunk[wave];
+  const int kv = wave & 1;
+  const int ci = a.groups[grp].chunk[wave >> 1];
   if (ci < 0) return;
   const DecChunk ch = a.chunks[ci];
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc((void*)ch.blob, 0, (int)ch.blob_bytes, kBufRsrcWord3);
+  const int row = kv * a.L + l;
 
   const int c = cb * kLanes + lane;
   const bool active = c < a.C;
@@ -76,21 +103,20 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
   const size_t pi = (size_t)row * a.C + c;
   const float scale_a = a.scale_a[pi];
   const float step = a.step[q][pi];
-  const float step_row = step * (1.0f / kRow);  // exact: a power-of-two scaling
 
   const uint8_t* tb = reinterpret_cast<const uint8_t*>(tab);
-  const uint32_t lane_addr = 2u * lane_slot(lane);      // LDS byte address of cum[0]
-  const uint32_t key32 = lds16(tb, lane_addr + 32u * kRow);  // root of the search, kept in a register
+  const uint32_t lane_addr = (uint32_t)kv * (2u * kLanes) + 2u * lane_slot(lane);
+  const uint32_t key32 = lds16(tb, lane_addr + 32u * kRow);  // root of the search
 
-  // bit reader: `code` is the 32-bit window, b1:b0 the next nb bits (most
-  // significant first; 32..64 before every pair of symbols), `nxt` the word
-  // after them, already in flight
+  // decoder state: ncode = ~code; range; bb = the next bits of the stream,
+  // complemented, in its low `left` bits (most significant first, 32..64 of
+  // them before every pair of symbols); nxt = the following word, in flight
   uint32_t wof = ch.off_pay + 4u * start;
-  uint32_t code = ld32(rs, wof);
-  uint32_t b1 = ld32(rs, wof + 4u), b0 = ld32(rs, wof + 8u);
-  uint32_t nxt = ld32(rs, wof + 12u);
-  wof += 16u;
-  int nb = 64;
+  uint32_t ncode = ~ld32(rs, wof);
+  uint64_t bb = ((uint64_t)~ld32(rs, wof + 4u) << 32) | ~ld32(rs, wof + 8u);
+  wof += 12u;  // the word after the buffered ones
+  uint32_t nxt = ld32(rs, wof);
+  uint32_t left = 64;
   uint32_t range = 0xFFFFFFFFu;
 
   // output rows of this (kv, layer, chunk) through a buffer resource: the lane's
@@ -106,62 +132,92 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
   // one symbol: search, interval update, renormalisation, reconstruction
   auto symbol = [&](uint32_t soff, float base) {
     const uint32_t r = range >> kProbBits;
-    // largest s with r * cum[s] <= code; `ad` is the LDS address of cum[s]
-    uint32_t ad = (mul24(r, key32) <= code) ? lane_addr + 32u * kRow : lane_addr;
+    // largest s with r * cum[s] <= code, as the LDS address of cum[s]
+    uint32_t ad = lane_addr | (le_mask(r, key32, ncode) & (32u * kRow));
 #pragma unroll
-    for (uint32_t stp = 16; stp; stp >>= 1) {
-      if (mul24(r, lds16(tb, ad + stp * kRow)) <= code) ad += stp * kRow;
-    }
-    const uint32_t lo = mul24(r, lds16(tb, ad));
-    const uint32_t hi = mul24(r, lds16(tb, ad + kRow));
-    code -= lo;
-    range = hi - lo;
-    // shift in whole bytes until range >= 2^24 (0, 1 or 2 bytes; range > 0)
-    const uint32_t sh = (uint32_t)__builtin_clz(range) & 24u;
-    const uint64_t w_hi = ((uint64_t)code << 32) | b1;
-    const uint64_t w_lo = (((uint64_t)b1 << 32) | b0) << sh;
-    code = (uint32_t)((w_hi << sh) >> 32);
-    b1 = (uint32_t)(w_lo >> 32);
-    b0 = (uint32_t)w_lo;
-    nb -= (int)sh;
-    range <<= sh;
-    // (ad - lane_addr) = s * kRow, so this is fma(s, step, base) exactly
-    const float y = __builtin_fmaf((float)(ad - lane_addr), step_row, base);
+    for (uint32_t stp = 16; stp; stp >>= 1) ad |= le_mask(r, lds16(tb, ad + stp * kRow), ncode) & (stp * kRow);
+    const uint32_t c0 = lds16(tb, ad), c1 = lds16(tb, ad + kRow);
+    ncode += mul24(r, c0);  // code -= r * cum[s]
+    const uint32_t rn = mul24(r, c1 - c0);
+    // shift in whole bytes until range >= 2^24 (0, 1 or 2 bytes; rn >= 2^9)
+    const uint32_t sh = (uint32_t)__builtin_clz(rn) & 24u;
+    range = rn << sh;
+    const uint32_t t = left - sh;
+    ncode = (ncode << sh) | __builtin_amdgcn_ubfe((uint32_t)(bb >> (t & 63u)), 0u, sh);
+    left = t;
+    const float y = __builtin_fmaf(byte1_to_float(ad), step, base);
     __builtin_amdgcn_raw_buffer_store_b16(float_to_half_bits(y), ro, lane_off, soff, 0);
   };
 
-  for (int g = 0; g < ch.ng; g++) {
-    const int ta = g * a.G, te = min(ta + a.G, ch.tc);
+  // Every pair of symbols issues exactly one load and two stores, so the wait
+  // for a word loaded at the previous pair never includes this pair's stores.
+  // A lane takes its buffered word `nxt` when fewer than 32 bits remain (two
+  // symbols need at most 32) and loads the following word into `ld`; a lane
+  // that takes nothing points its load past the blob end (no memory access).
+  // `nxt` is updated from `ld` one pair later, when that load has landed.
+  uint32_t ld = 0, took = 0;
+  auto refill = [&]() {
+    if (took) nxt = ld;
+    took = left < 32;
+    if (took) {
+      bb = (bb << 32) | ~nxt;
+      left += 32;
+      wof += 4u;
+    }
+    ld = ld32(rs, took ? wof : 0xFFFFFFF0u);
+  };
+
+  // one group: the anchor row, then its deltas in pairs (a lone last one when
+  // the group has an even number of tokens)
+  auto group = [&](int g, int ta, int te) {
     const int anc = anc_next;
-    if (g + 1 < ch.ng) anc_next = ld8s(rs, anc_base + (uint32_t)(g + 1) * a.C);
+    anc_next = ld8s(rs, anc_base + (uint32_t)(g + 1) * a.C);  // past the last group: unused
     const float ahat = anchor_value(anc, scale_a);
     __builtin_amdgcn_raw_buffer_store_b16(float_to_half_bits(ahat), ro, lane_off,
                                           (uint32_t)ta * row_bytes, 0);
     const float base = __builtin_fmaf(-32.0f, step, ahat);
-    for (int t = ta + 1; t < te; t += 2) {
-      // at least 32 buffered bits cover the next two symbols (16 bits each at most)
-      if (nb < 32) {
-        const uint64_t add = (uint64_t)nxt << (32 - nb);
-        b1 |= (uint32_t)(add >> 32);
-        b0 |= (uint32_t)add;
-        nb += 32;
-        nxt = ld32(rs, wof);
-        wof += 4u;
-      }
+    int t = ta + 1;
+#pragma unroll
+    for (; t + 1 < te; t += 2) {
+      // keep the refill after the previous pair's stores: its wait then
+      // leaves those two stores in flight
+      __builtin_amdgcn_sched_barrier(0);
+      refill();
       symbol((uint32_t)t * row_bytes, base);
-      if (t + 1 < te) symbol((uint32_t)(t + 1) * row_bytes, base);
+      symbol((uint32_t)(t + 1) * row_bytes, base);
     }
+    if (t < te) {
+      __builtin_amdgcn_sched_barrier(0);
+      refill();
+      symbol((uint32_t)t * row_bytes, base);
+    }
+  };
+
+  // everything loaded so far (scale, step, first words, first anchor) is in
+  // registers before the loop, so no wait inside it is for those loads
+  __builtin_amdgcn_s_waitcnt(0);
+  int g = 0;
+  if constexpr (GS > 0) {
+    // full groups of the compile-time size: the same loads and stores every
+    // iteration, so the anchor loaded one group ahead is waited for without
+    // waiting for the stores issued since
+    const int nfull = ch.tc / GS;
+    for (; g < nfull; g++) group(g, g * GS, g * GS + GS);
   }
+  for (; g < ch.ng; g++) group(g, g * a.G, min(g * a.G + a.G, ch.tc));
   // a valid stream keeps code < range throughout; a corrupt one breaks it for good
-  bad |= (code >= range) ? 1u : 0u;
+  bad |= (~ncode >= range) ? 1u : 0u;
   if (bad) atomicOr(a.status, 1u);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
-  const unsigned blocks = (unsigned)(a.n_groups * 2 * a.L * a.nblk);
-  k_decode<<<blocks, kLanes * a.waves, 0, st>>>(a);
+  const unsigned blocks = (unsigned)(a.n_groups * a.L * a.nblk);
+  if (a.G == 10)
+    k_decode<10><<<blocks, 2 * kLanes * a.waves, 0, st>>>(a);
+  else
+    k_decode<0><<<blocks, 2 * kLanes * a.waves, 0, st>>>(a);
   return hipGetLastError();
 }
 
