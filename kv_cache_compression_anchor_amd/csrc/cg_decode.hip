@@ -25,8 +25,30 @@ __device__ __forceinline__ int ld8s(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return (int)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t lds16(const uint8_t* base, uint32_t byte_off) {
-  return *reinterpret_cast<const uint16_t*>(base + byte_off);
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// The kernel's LDS is all dynamic, so it starts at LDS address 0: pointers are
+// formed from byte addresses directly (constant parts of an address then fold
+// into the instructions' offset fields).
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(3))) T* lds_at(uint32_t byte_addr) {
+  return reinterpret_cast<__attribute__((address_space(3))) T*>(static_cast<uintptr_t>(byte_addr));
+}
+
+__device__ __forceinline__ uint32_t lds32(uint32_t addr) { return *lds_at<uint32_t>(addr); }
+__device__ __forceinline__ uint32_t lds16(uint32_t addr) { return *lds_at<uint16_t>(addr); }
+
+// four words into consecutive ring slots (slots are 256 bytes apart)
+__device__ __forceinline__ void lds_put4(uint32_t lane_addr, uint32_t slot_off, u32x4 v) {
+  auto p = lds_at<uint32_t>(lane_addr + slot_off);
+  p[0] = v.x;
+  p[64] = v.y;
+  p[128] = v.z;
+  p[192] = v.w;
 }
 
 // (float)((x >> 8) & 0xFF) in one instruction
@@ -41,6 +63,11 @@ __device__ __forceinline__ float byte1_to_float(uint32_t x) {
 // streams], 256 bytes, so the byte address of entry k of a lane is
 // k * 256 + (kv * 128 + 2 * slot) and bits 8..15 of it are k itself.
 constexpr uint32_t kRow = 4 * kLanes;
+constexpr uint32_t kTabBytes = kImgRows * kRow;        // 16,640
+constexpr uint32_t kRingBytes = 8 * 4 * kLanes;        // 8 slots x 64 lanes x 4 B
+// first wave's word ring, aligned to the ring size so that a slot address is
+// the lane's ring address with the slot number in bits 8..10
+constexpr uint32_t kRingBase = (kTabBytes + kRingBytes - 1) / kRingBytes * kRingBytes;
 
 // All ones when r * key <= code, else zero.  ncode is ~code, so the 64-bit sum
 // r * key + (2^64 - code - 1) stays within [2^64 - 2^32, 2^64) when
@@ -54,7 +81,9 @@ __device__ __forceinline__ uint32_t le_mask(uint32_t r, uint32_t key, uint32_t n
 // GS: group size fixed at compile time (0 = the runtime a.G only)
 template <int GS>
 __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
-  __shared__ uint32_t tab[kImgRows * kLanes];  // [65 rows][K: 64 u16 | V: 64 u16]
+  // LDS: the tables at 0 ([65 rows][K: 64 u16 | V: 64 u16]), then one word
+  // ring per wave ([8 slots][64 lanes] u32)
+  auto tab = lds_at<uint32_t>(0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int per_grp = a.L * a.nblk;
@@ -104,20 +133,31 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
   const float scale_a = a.scale_a[pi];
   const float step = a.step[q][pi];
 
-  const uint8_t* tb = reinterpret_cast<const uint8_t*>(tab);
   const uint32_t lane_addr = (uint32_t)kv * (2u * kLanes) + 2u * lane_slot(lane);
-  const uint32_t key32 = lds16(tb, lane_addr + 32u * kRow);  // root of the search
+  const uint32_t key32 = lds16(lane_addr + 32u * kRow);  // root of the search
 
   // decoder state: ncode = ~code; range; bb = the next bits of the stream,
   // complemented, in its low `left` bits (most significant first, 32..64 of
-  // them before every pair of symbols); nxt = the following word, in flight
-  uint32_t wof = ch.off_pay + 4u * start;
-  uint32_t ncode = ~ld32(rs, wof);
-  uint64_t bb = ((uint64_t)~ld32(rs, wof + 4u) << 32) | ~ld32(rs, wof + 8u);
-  wof += 12u;  // the word after the buffered ones
-  uint32_t nxt = ld32(rs, wof);
+  // them before every pair of symbols).  Words 0..2 start the state; words 3..
+  // reach bb through the wave's LDS ring: word 3 + i sits in slot i mod 8 of
+  // the lane's column, fetched 16 bytes at a time one group ahead of use.
+  const uint32_t sbase = ch.off_pay + 4u * start;  // byte offset of word 0
+  uint32_t ncode = ~ld32(rs, sbase);
+  uint64_t bb = ((uint64_t)~ld32(rs, sbase + 4u) << 32) | ~ld32(rs, sbase + 8u);
   uint32_t left = 64;
   uint32_t range = 0xFFFFFFFFu;
+  const uint32_t ring = kRingBase + (uint32_t)wave * kRingBytes + 4u * (uint32_t)lane;
+  // ring words taken and written, counted in units of 256 (one slot's size)
+  uint32_t taken = 0;
+  uint32_t landed = 8u << 8;  // words 3..10, written below
+  uint32_t fetch_off = sbase + 44u;  // next 16-byte block: word 11
+  {
+    const u32x4 b0 = ld128(rs, sbase + 12u), b1 = ld128(rs, sbase + 28u);
+    lds_put4(ring, 0u, b0);
+    lds_put4(ring, 4u * 256u, b1);
+  }
+  u32x4 pend = {0u, 0u, 0u, 0u};  // block in flight
+  bool inflight = false;
 
   // output rows of this (kv, layer, chunk) through a buffer resource: the lane's
   // channel is the vector offset, the token row a wave-uniform scalar offset
@@ -135,8 +175,8 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
     // largest s with r * cum[s] <= code, as the LDS address of cum[s]
     uint32_t ad = lane_addr | (le_mask(r, key32, ncode) & (32u * kRow));
 #pragma unroll
-    for (uint32_t stp = 16; stp; stp >>= 1) ad |= le_mask(r, lds16(tb, ad + stp * kRow), ncode) & (stp * kRow);
-    const uint32_t c0 = lds16(tb, ad), c1 = lds16(tb, ad + kRow);
+    for (uint32_t stp = 16; stp; stp >>= 1) ad |= le_mask(r, lds16(ad + stp * kRow), ncode) & (stp * kRow);
+    const uint32_t c0 = lds16(ad), c1 = lds16(ad + kRow);
     ncode += mul24(r, c0);  // code -= r * cum[s]
     const uint32_t rn = mul24(r, c1 - c0);
     // shift in whole bytes until range >= 2^24 (0, 1 or 2 bytes; rn >= 2^9)
@@ -149,27 +189,39 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
     __builtin_amdgcn_raw_buffer_store_b16(float_to_half_bits(y), ro, lane_off, soff, 0);
   };
 
-  // Every pair of symbols issues exactly one load and two stores, so the wait
-  // for a word loaded at the previous pair never includes this pair's stores.
-  // A lane takes its buffered word `nxt` when fewer than 32 bits remain (two
-  // symbols need at most 32) and loads the following word into `ld`; a lane
-  // that takes nothing points its load past the blob end (no memory access).
-  // `nxt` is updated from `ld` one pair later, when that load has landed.
-  uint32_t ld = 0, took = 0;
+  // A lane takes a word when fewer than 32 bits remain (two symbols need at
+  // most 32).  Only stores go to memory inside a group, so no wait in it
+  // drains them; a ring that has run dry (more than the buffered words taken
+  // in one group, which typical data never does) falls back to a direct load.
   auto refill = [&]() {
-    if (took) nxt = ld;
-    took = left < 32;
-    if (took) {
-      bb = (bb << 32) | ~nxt;
+    const bool take = left < 32;
+    const uint32_t slot = (taken & 0x700u) | ring;
+    if (take && taken >= landed)
+      *lds_at<uint32_t>(slot) = ld32(rs, sbase + 12u + (taken >> 6));
+    const uint32_t w = lds32(slot);
+    if (take) {
+      bb = (bb << 32) | ~w;
       left += 32;
-      wof += 4u;
+      taken += 256u;
     }
-    ld = ld32(rs, took ? wof : 0xFFFFFFF0u);
+  };
+  // once per group: write the block fetched one group earlier into the ring,
+  // then fetch the next one if the ring has room for it when it lands (lanes
+  // without room point their load past the blob end: no memory access)
+  auto ring_step = [&]() {
+    if (inflight) {
+      lds_put4(ring, landed & 0x400u, pend);
+      landed += 4u * 256u;
+    }
+    inflight = landed + 4u * 256u <= taken + 8u * 256u;
+    pend = ld128(rs, inflight ? fetch_off : 0xFFFFFFF0u);
+    if (inflight) fetch_off += 16u;
   };
 
   // one group: the anchor row, then its deltas in pairs (a lone last one when
   // the group has an even number of tokens)
   auto group = [&](int g, int ta, int te) {
+    ring_step();
     const int anc = anc_next;
     anc_next = ld8s(rs, anc_base + (uint32_t)(g + 1) * a.C);  // past the last group: unused
     const float ahat = anchor_value(anc, scale_a);
@@ -214,10 +266,11 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   const unsigned blocks = (unsigned)(a.n_groups * a.L * a.nblk);
+  const size_t lds_bytes = kRingBase + (size_t)2 * a.waves * kRingBytes;
   if (a.G == 10)
-    k_decode<10><<<blocks, 2 * kLanes * a.waves, 0, st>>>(a);
+    k_decode<10><<<blocks, 2 * kLanes * a.waves, lds_bytes, st>>>(a);
   else
-    k_decode<0><<<blocks, 2 * kLanes * a.waves, 0, st>>>(a);
+    k_decode<0><<<blocks, 2 * kLanes * a.waves, lds_bytes, st>>>(a);
   return hipGetLastError();
 }
 

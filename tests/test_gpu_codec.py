@@ -99,6 +99,42 @@ def test_cross_decoding_both_ways():
         assert not bad and gu.same_bits(ko2, ko) and gu.same_bits(vo2, vo)
 
 
+@pytest.mark.parametrize("group_tokens", [10, 7])
+def test_costly_symbols_drain_the_word_ring(group_tokens):
+    """Tables built from one K/V pair, data from another whose deltas all hit
+    the clipped extremes, each of which the tables give a tiny probability:
+    about 15 bits per symbol, more than the decoder's per-group word fetches
+    supply, so its direct-load refill runs (group size 10 takes the unrolled
+    path, 7 the generic one)."""
+    w = gu.workload(layers=2, tokens=900, channels=70, chunk_tokens=450,
+                    group_tokens=group_tokens, layer_group_end=(1, 2), layer_step=(0.5, 1.0),
+                    qualities=(0, 2))
+    k, v = synth.gen_kv(w)
+    kd, vd = gu.to_dev(k), gu.to_dev(v)
+    tab = gu.gpu_tables(w, kd, vd)
+    ot = oracle.build_tables(oracle.params_for(w), k, v)
+    sign = np.where(np.arange(w.tokens) % 2 == 0, 1.0, -1.0)[None, :, None]
+    k2 = (k.astype(np.float32) + 3000.0 * sign).astype(np.float16)
+    v2 = (v.astype(np.float32) - 3000.0 * sign).astype(np.float16)
+    kd2, vd2 = gu.to_dev(k2), gu.to_dev(v2)
+    import kv_cache_compression_anchor_amd as cg
+    for ch in range(w.n_chunks):
+        for q in w.qualities:
+            out = gu.torch().empty(cg.cg_encode_bound(tab, ch), dtype=gu.torch().uint8,
+                                   device="cuda")
+            n = cg.cg_encode(tab, kd2, vd2, ch, q, out)
+            gb = out[:n].cpu().numpy().tobytes()
+            ob = oracle.encode_chunk(ot, k2, v2, ch, q)
+            assert gb == ob, ("blob differs", ch, q, gu.first_difference(gb, ob))
+            bv = oracle.blob_view(ob)
+            tc = oracle.parse_blob_header(ob)["chunk_tokens"]
+            assert bv.lengths.mean() * 32 > 12 * tc, "streams are not costly enough"
+            kg, vg, st = gu.gpu_decode(tab, [out[:n]], k.shape)
+            ko, vo, bad = gu.oracle_decode(ot, [ob], k.shape)
+            assert st == 0 and not bad
+            assert gu.same_bits(kg, ko) and gu.same_bits(vg, vo), ("decode differs", ch, q)
+
+
 def test_degenerate_channels():
     w = gu.workload(layers=1, tokens=64, channels=6, chunk_tokens=64, layer_group_end=(1,),
                     layer_step=(0.5,), qualities=(0,))
