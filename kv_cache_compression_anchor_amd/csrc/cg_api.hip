@@ -543,6 +543,12 @@ int cg_encode_batch(const cg_tables* ch, const void* k_dev, const void* v_dev, i
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   HIP_TRY(hipMemsetAsync(h->enc_status, 0, 16 * (size_t)n, st), "clear status");
+  // blobs in quality order, so that the blobs of one launch fall into few groups
+  // of one quality (a group's workgroups stage each table once for all of them)
+  std::vector<int> order(n);
+  for (int i = 0; i < n; i++) order[i] = i;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int x, int y) { return qualities[x] < qualities[y]; });
   for (int i0 = 0; i0 < n; i0 += slots) {
     EncodeArgs a;
     memset(&a, 0, sizeof(a));
@@ -554,13 +560,13 @@ int cg_encode_batch(const cg_tables* ch, const void* k_dev, const void* v_dev, i
     a.G = t.G;
     a.nblk = t.nblk;
     a.nblobs = std::min(slots, n - i0);
-    a.unit_blocks = (uint32_t)((2 * t.L * t.nblk + 3) / 4);
     a.swb = swb;
     a.scale_a = reinterpret_cast<const float*>(t.ser + t.lay.off_scale_a);
     a.inv_a = reinterpret_cast<const float*>(t.ser + t.lay.off_inv_a);
     a.tables_id = h->id;
+    a.waves = 1;
     for (int j = 0; j < a.nblobs; j++) {
-      const int i = i0 + j;
+      const int i = order[i0 + j];
       const ChunkGeo g = chunk_geo(t, chunks[i]);
       EncBlob& B = a.b[j];
       B.blob = static_cast<uint8_t*>(outs_dev[i]);
@@ -576,6 +582,16 @@ int cg_encode_batch(const cg_tables* ch, const void* k_dev, const void* v_dev, i
       B.lens = h->lens + (size_t)j * t.lay.n;
       B.row_words = h->row_words + (size_t)j * 2 * t.L;
       B.status = h->enc_status + 4 * (size_t)i;
+      // open a new group at a quality change or when the current one is full
+      if (j == 0 || a.b[j - 1].q != B.q || a.groups[a.n_groups - 1].blob[3] >= 0) {
+        EncGroup& eg = a.groups[a.n_groups++];
+        for (int w = 0; w < 4; w++) eg.blob[w] = -1;
+      }
+      EncGroup& eg = a.groups[a.n_groups - 1];
+      int w = 0;
+      while (eg.blob[w] >= 0) w++;
+      eg.blob[w] = (int8_t)j;
+      a.waves = std::max(a.waves, w + 1);
     }
     HIP_TRY(launch_encode(a, st), "encode launch");
   }

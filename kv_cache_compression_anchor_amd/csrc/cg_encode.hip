@@ -9,8 +9,6 @@
 namespace cg {
 namespace {
 
-constexpr int kEncWaves = 4;
-
 // Range coder state of one lane.  Output bytes are final when emitted: a
 // possible carry is held back in `cache` plus a run of `pending` 0xFF bytes.
 struct RcEnc {
@@ -77,23 +75,38 @@ __device__ __forceinline__ void rc_finish(RcEnc& e, uint32_t* out) {
   if (e.nacc) out[e.nw++] = e.acc << (8 * (4 - e.nacc));
 }
 
-// One wave per (blob, kv, layer, 64-channel block); a launch covers up to
-// kEncMaxBlobs (chunk, quality) blobs of the same tensors so that enough waves are
-// in flight to hide the latency of each lane's serial coder.
-__global__ __launch_bounds__(kLanes * kEncWaves) void k_encode(EncodeArgs a) {
-  __shared__ uint16_t tab[kEncWaves][kImgRows * kLanes];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int bi = blockIdx.x / a.unit_blocks;
-  const EncBlob& B = a.b[bi];
-  const int units = 2 * a.L * a.nblk;
-  const int unit = (blockIdx.x % a.unit_blocks) * kEncWaves + wave;
-  if (unit < units) {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(B.img + (size_t)unit * kImgRows * kLanes);
-    uint32_t* dst = reinterpret_cast<uint32_t*>(tab[wave]);
-    for (int j = lane; j < kImgRows * kLanes / 2; j += kLanes) dst[j] = src[j];
+// A workgroup is (group of up to 4 blobs of one quality, kv, layer, 64-channel
+// block) with one wave per blob: the block's cumulative table is staged in LDS
+// once for all of them.  A launch covers up to kEncMaxBlobs (chunk, quality)
+// blobs of the same tensors so that enough waves are in flight to hide the
+// latency of each lane's serial coder.
+constexpr int kEncMaxWaves = 4;
+
+__device__ __forceinline__ uint32_t ld_half(__amdgpu_buffer_rsrc_t r, uint32_t lane_off,
+                                            uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, lane_off, soff, 0);
+}
+
+// GS: group size fixed at compile time (0 = the runtime a.G only).  With GS,
+// the input of full groups is loaded two groups ahead, so the wait for it
+// never includes the stores issued since (every group issues the same loads).
+template <int GS>
+__global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) {
+  __shared__ uint16_t tab[kImgRows * kLanes];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int per_grp = 2 * a.L * a.nblk;
+  const int grp = blockIdx.x / per_grp, unit = blockIdx.x % per_grp;
+  const EncGroup eg = a.groups[grp];
+  {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.b[eg.blob[0]].img +
+                                                            (size_t)unit * kImgRows * kLanes);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(tab);
+    for (int j = threadIdx.x; j < kImgRows * kLanes / 2; j += blockDim.x) dst[j] = src[j];
   }
   __syncthreads();
-  if (unit >= units) return;
+  const int bi = eg.blob[wave];
+  if (bi < 0) return;
+  const EncBlob& B = a.b[bi];
   const int kv = unit / (a.L * a.nblk);
   const int l = (unit / a.nblk) % a.L;
   const int cb = unit % a.nblk;
@@ -101,28 +114,59 @@ __global__ __launch_bounds__(kLanes * kEncWaves) void k_encode(EncodeArgs a) {
   if (c >= a.C) return;
   const size_t pi = ((size_t)kv * a.L + l) * a.C + c;
   const float scale_a = a.scale_a[pi], inv_a = a.inv_a[pi], inv_step = B.inv_step[pi];
-  const uint16_t* x = (kv ? a.v : a.k) + ((size_t)l * a.T + B.t0) * a.C + c;
-  const uint8_t* tb = reinterpret_cast<const uint8_t*>(tab[wave]) + 2 * lane_slot(lane);
+  // the chunk's rows of this (kv, layer): the lane's channel is the vector
+  // offset, the token row a scalar offset; rows past the chunk read as zero
+  const uint32_t row_bytes = 2u * (uint32_t)a.C;
+  const __amdgpu_buffer_rsrc_t xin = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((kv ? a.v : a.k) + ((size_t)l * a.T + B.t0) * a.C), 0,
+      (int)((uint32_t)B.tc * row_bytes), kBufRsrcWord3);
+  const uint32_t lane_off = 2u * (uint32_t)c;
+  const uint8_t* tb = reinterpret_cast<const uint8_t*>(tab) + 2 * lane_slot(lane);
   uint32_t* out = B.scratch + pi * a.swb;
   int8_t* anchors = reinterpret_cast<int8_t*>(B.blob + B.lay.off_anchor) +
                     ((size_t)kv * a.L + l) * B.ng * a.C + c;
   RcEnc e = {0, 0xFFFFFFFFu, 0, 0, 0, 0, 0, 0};
   uint32_t nonfinite = 0;
-  for (int g = 0; g < B.ng; g++) {
-    const int ta = g * a.G, te = min(ta + a.G, B.tc);
-    const uint16_t ha = x[(size_t)ta * a.C];
+
+  // one group from its tokens' binary16 bits: the anchor, then the deltas
+  auto code_group = [&](int g, int n, auto half_of) {
+    const uint32_t ha = half_of(0);
     nonfinite |= (ha & 0x7C00u) == 0x7C00u;
     const int av = quant_anchor(half_bits_to_float(ha), inv_a);
     anchors[(size_t)g * a.C] = (int8_t)av;
     const float ahat = anchor_value(av, scale_a);
-    for (int t = ta + 1; t < te; t++) {
-      const uint16_t hx = x[(size_t)t * a.C];
+    for (int j = 1; j < n; j++) {
+      const uint32_t hx = half_of(j);
       nonfinite |= (hx & 0x7C00u) == 0x7C00u;
       const uint32_t s = quant_delta(half_bits_to_float(hx), ahat, inv_step);
       const uint32_t c0 = *reinterpret_cast<const uint16_t*>(tb + s * (2 * kLanes));
       const uint32_t c1 = *reinterpret_cast<const uint16_t*>(tb + (s + 1) * (2 * kLanes));
       rc_put(e, c0, c1 - c0, out);
     }
+  };
+
+  int g = 0;
+  if constexpr (GS > 0) {
+    const int nfull = B.tc / GS;
+    uint32_t xa[GS], xb[GS];
+    auto load = [&](uint32_t (&xv)[GS], int gg) {
+#pragma unroll
+      for (int j = 0; j < GS; j++) xv[j] = ld_half(xin, lane_off, (uint32_t)(gg * GS + j) * row_bytes);
+    };
+    load(xa, 0);
+    load(xb, 1);
+    for (; g + 2 <= nfull; g += 2) {
+      code_group(g, GS, [&](int j) { return xa[j]; });
+      load(xa, g + 2);
+      code_group(g + 1, GS, [&](int j) { return xb[j]; });
+      load(xb, g + 3);
+    }
+    if (g < nfull) code_group(g++, GS, [&](int j) { return xa[j]; });
+  }
+  for (; g < B.ng; g++) {
+    const int ta = g * a.G;
+    code_group(g, min(a.G, B.tc - ta),
+               [&](int j) { return ld_half(xin, lane_off, (uint32_t)(ta + j) * row_bytes); });
   }
   if (B.tc > B.ng) rc_finish(e, out);  // a stream without symbols stays empty
   if (nonfinite) atomicOr(&B.status[2], 1u);
@@ -235,7 +279,11 @@ __global__ __launch_bounds__(256) void k_pack(EncodeArgs a) {
 
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t st) {
   const unsigned nb = (unsigned)a.nblobs;
-  k_encode<<<nb * a.unit_blocks, kLanes * kEncWaves, 0, st>>>(a);
+  const unsigned blocks = (unsigned)(a.n_groups * 2 * a.L * a.nblk);
+  if (a.G == 10)
+    k_encode<10><<<blocks, kLanes * a.waves, 0, st>>>(a);
+  else
+    k_encode<0><<<blocks, kLanes * a.waves, 0, st>>>(a);
   k_row_totals<<<dim3(2 * a.L, nb), 256, 0, st>>>(a);
   k_row_scan<<<nb, 64, 0, st>>>(a);
   k_pad<<<nb, 256, 0, st>>>(a);

@@ -167,7 +167,6 @@ struct EncBlob {
   uint8_t* blob;      // output
   size_t cap;
   int32_t t0, tc, ng, q;
-  uint32_t unit_block0;  // first workgroup of this blob in the encode grid
   BlobLayout lay;
   const uint16_t* img;       // cum images of quality q
   const float* inv_step;     // of quality q
@@ -176,15 +175,19 @@ struct EncBlob {
   uint32_t* row_words;       // [2L]
   uint32_t* status;          // [0] payload words, [1] too large for cap, [2] non-finite input
 };
+struct EncGroup {  // blobs of one quality coded by one workgroup (one wave each)
+  int8_t blob[4];
+};
 struct EncodeArgs {
   const uint16_t* k;
   const uint16_t* v;
   int L, T, C, G, nblk, nblobs;
-  uint32_t unit_blocks;  // workgroups per blob
+  int n_groups, waves;  // workgroups per (kv, layer, block) and their widest group
   size_t swb;
   const float* scale_a;
   const float* inv_a;
   uint64_t tables_id;
+  EncGroup groups[kEncMaxBlobs];
   EncBlob b[kEncMaxBlobs];
 };
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t st);
