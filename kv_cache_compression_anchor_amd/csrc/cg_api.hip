@@ -162,11 +162,11 @@ int alloc_tables(cg_tables* h) {
 
 // Tables id of the device copy, computed on the GPU; syncs the stream.
 int compute_id(cg_tables* h, hipStream_t st) {
-  const size_t nblk = (h->t.lay.total + kIdBlock - 1) / kIdBlock;
+  const size_t nd = id_leaves(h->t.lay.total) + id_mids(h->t.lay.total);
   uint64_t* dig = nullptr;
-  HIP_TRY(hipMalloc(&dig, 8 * (nblk + 1)), "hipMalloc(id)");
-  hipError_t e = launch_tables_id(h->t, dig, dig + nblk, st);
-  if (e == hipSuccess) e = hipMemcpyAsync(h->host_status, dig + nblk, 8, hipMemcpyDeviceToHost, st);
+  HIP_TRY(hipMalloc(&dig, 8 * (nd + 1)), "hipMalloc(id)");
+  hipError_t e = launch_tables_id(h->t, dig, dig + nd, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(h->host_status, dig + nd, 8, hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   (void)hipFree(dig);
   if (e != hipSuccess) return hip_fail(e, "tables id");

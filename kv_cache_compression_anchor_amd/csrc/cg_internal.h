@@ -23,7 +23,8 @@ constexpr uint32_t kTabMagic = 0x31544743u;   // "CGT1"
 constexpr uint32_t kBlobMagic = 0x314B4743u;  // "CGK1"
 constexpr int kMaxTokens = 1 << 21;
 constexpr int kMaxChunk = 65536;
-constexpr int kIdBlock = 16384;        // tables id: FNV-1a-64 over 16 KiB blocks
+constexpr int kIdLeaf = 1024;          // tables id: FNV-1a-64 tree over 1 KiB leaves,
+constexpr int kIdFan = 256;            // 256 leaf digests per middle digest
 constexpr int kImgRows = kNSym + 1;    // cumulative table cum[0..64]
 constexpr int kLanes = 64;             // one wave64 = 64 channels
 constexpr uint32_t kBufRsrcWord3 = 0x00020000u;  // raw buffer, gfx9 family
@@ -159,6 +160,9 @@ hipError_t launch_histogram(const uint16_t* x, int kv, const DevTables& t, uint3
                             hipStream_t st);
 hipError_t launch_normalize(const DevTables& t, const uint32_t* counts, hipStream_t st);
 hipError_t launch_images(DevTables& t, hipStream_t st);
+// digests the tables id needs: leaves, then middle digests
+inline size_t id_leaves(size_t bytes) { return (bytes + kIdLeaf - 1) / kIdLeaf; }
+inline size_t id_mids(size_t bytes) { return (id_leaves(bytes) + kIdFan - 1) / kIdFan; }
 hipError_t launch_tables_id(const DevTables& t, uint64_t* scratch_digests, uint64_t* id_out,
                             hipStream_t st);
 

@@ -214,39 +214,40 @@ struct NormArgs {
 
 // counts -> frequencies summing to 2^15: one slot each, the rest in proportion
 // (rounded down), the remainder to the most counted symbol (lowest on ties).
+// One wave per table, one lane per symbol.
 __global__ __launch_bounds__(256) void k_normalize(NormArgs a) {
   const size_t ntab = (size_t)2 * a.nq * a.L * a.C;
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= ntab) return;
+  const size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int k = threadIdx.x & 63;
+  if (i >= ntab) return;  // whole waves leave together
   const size_t lc = (size_t)a.L * a.C;
   const int kv = (int)(i / (a.nq * lc));
   const int s = (int)((i / lc) % a.nq);
   const size_t rest = i % lc;  // l * C + c
-  const uint32_t* cnt = a.counts + i * kNSym;
-  uint64_t N = 0;
-  for (int k = 0; k < kNSym; k++) N += cnt[k];
+  const uint32_t c_k = a.counts[i * kNSym + k];
+  uint64_t N = c_k;
+  for (int o = 32; o; o >>= 1) N += __shfl_xor(N, o);
+  const uint32_t ck = N ? c_k : 1u;
   const double spare = (double)(kProbTotal - kNSym);
   const double den = N ? (double)N : (double)kNSym;
   // floor of an exact quotient of integers below 2^36 and 2^22: the correctly
   // rounded binary64 quotient never crosses an integer
-  uint32_t total = 0, bestc = 0;
-  int best = -1;
-  for (int k = 0; k < kNSym; k++) {
-    const uint32_t ck = N ? cnt[k] : 1u;
-    total += 1u + (uint32_t)floor((double)ck * spare / den);
-    if (best < 0 || ck > bestc) {
-      bestc = ck;
-      best = k;
+  uint32_t f = 1u + (uint32_t)floor((double)ck * spare / den);
+  uint32_t total = f;
+  for (int o = 32; o; o >>= 1) total += __shfl_xor(total, o);
+  // the most counted symbol, lowest index on ties
+  uint32_t bc = ck, bk = (uint32_t)k;
+  for (int o = 32; o; o >>= 1) {
+    const uint32_t oc = __shfl_xor(bc, o), ok = __shfl_xor(bk, o);
+    if (oc > bc || (oc == bc && ok < bk)) {
+      bc = oc;
+      bk = ok;
     }
   }
+  if ((uint32_t)k == bk) f += kProbTotal - total;
   uint16_t* out = reinterpret_cast<uint16_t*>(a.ser + a.off_freq[a.q_of_slot[s]]) +
                   ((size_t)kv * lc + rest) * kNSym;
-  for (int k = 0; k < kNSym; k++) {
-    const uint32_t ck = N ? cnt[k] : 1u;
-    uint32_t f = 1u + (uint32_t)floor((double)ck * spare / den);
-    if (k == best) f += kProbTotal - total;
-    out[k] = (uint16_t)f;
-  }
+  out[k] = (uint16_t)f;
 }
 
 struct ImgArgs {
@@ -297,33 +298,54 @@ __device__ __forceinline__ uint64_t fnv_byte(uint64_t h, uint32_t b) {
   return (h ^ b) * kFnvPrime;
 }
 
-__global__ __launch_bounds__(256) void k_id_blocks(const uint8_t* ser, size_t n,
-                                                   uint64_t* digests) {
-  const size_t nblk = (n + kIdBlock - 1) / kIdBlock;
+// Tables id, a three-level FNV-1a-64 tree: digests of 1 KiB leaves (one thread
+// each, 16-byte loads), digests of the little-endian bytes of 256 leaf digests,
+// then the digest of the middle digests.
+__global__ __launch_bounds__(256) void k_id_leaves(const uint8_t* ser, size_t n, uint64_t* d0) {
+  const size_t n0 = (n + kIdLeaf - 1) / kIdLeaf;
   const size_t b = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= nblk) return;
-  const size_t start = b * kIdBlock;
-  const size_t len = min((size_t)kIdBlock, n - start);
-  const uint32_t* w = reinterpret_cast<const uint32_t*>(ser + start);
+  if (b >= n0) return;
+  const size_t start = b * kIdLeaf;
+  const size_t len = min((size_t)kIdLeaf, n - start);
   uint64_t h = kFnvBasis;
   size_t k = 0;
-  for (; k + 4 <= len; k += 4) {
-    const uint32_t v = w[k / 4];
-    h = fnv_byte(h, v & 0xFF);
-    h = fnv_byte(h, (v >> 8) & 0xFF);
-    h = fnv_byte(h, (v >> 16) & 0xFF);
-    h = fnv_byte(h, v >> 24);
+  if (len == (size_t)kIdLeaf) {  // full leaf: 16 bytes per load (ser is 256-byte aligned)
+    const uint4* w = reinterpret_cast<const uint4*>(ser + start);
+    for (; k < (size_t)kIdLeaf; k += 16) {
+      const uint4 v = w[k / 16];
+      const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        h = fnv_byte(h, q[j] & 0xFF);
+        h = fnv_byte(h, (q[j] >> 8) & 0xFF);
+        h = fnv_byte(h, (q[j] >> 16) & 0xFF);
+        h = fnv_byte(h, q[j] >> 24);
+      }
+    }
   }
   for (; k < len; k++) h = fnv_byte(h, ser[start + k]);
-  digests[b] = h;
+  d0[b] = h;
 }
 
-__global__ void k_id_final(const uint64_t* digests, size_t nblk, uint64_t* out) {
+__device__ __forceinline__ uint64_t fnv_digest(uint64_t h, uint64_t d) {
+#pragma unroll
+  for (int j = 0; j < 8; j++) h = fnv_byte(h, (uint32_t)(d >> (8 * j)) & 0xFF);
+  return h;
+}
+
+__global__ __launch_bounds__(64) void k_id_mid(const uint64_t* d0, size_t n0, uint64_t* d1) {
+  const size_t n1 = (n0 + kIdFan - 1) / kIdFan;
+  const size_t j = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n1) return;
+  const size_t end = min(n0, (j + 1) * (size_t)kIdFan);
   uint64_t h = kFnvBasis;
-  for (size_t b = 0; b < nblk; b++) {
-    const uint64_t d = digests[b];
-    for (int j = 0; j < 8; j++) h = fnv_byte(h, (uint32_t)(d >> (8 * j)) & 0xFF);
-  }
+  for (size_t i = j * kIdFan; i < end; i++) h = fnv_digest(h, d0[i]);
+  d1[j] = h;
+}
+
+__global__ void k_id_final(const uint64_t* d1, size_t n1, uint64_t* out) {
+  uint64_t h = kFnvBasis;
+  for (size_t j = 0; j < n1; j++) h = fnv_digest(h, d1[j]);
   *out = h;
 }
 
@@ -394,7 +416,7 @@ hipError_t launch_normalize(const DevTables& t, const uint32_t* counts, hipStrea
     if ((t.mask >> q) & 1u) a.q_of_slot[s++] = q;
   }
   const size_t ntab = (size_t)2 * a.nq * t.L * t.C;
-  k_normalize<<<blocks_for(ntab, 256), 256, 0, st>>>(a);
+  k_normalize<<<blocks_for(ntab * kLanes, 256), 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -416,9 +438,10 @@ hipError_t launch_images(DevTables& t, hipStream_t st) {
 
 hipError_t launch_tables_id(const DevTables& t, uint64_t* digests, uint64_t* id_out,
                             hipStream_t st) {
-  const size_t nblk = (t.lay.total + kIdBlock - 1) / kIdBlock;
-  k_id_blocks<<<blocks_for(nblk, 64), 64, 0, st>>>(t.ser, t.lay.total, digests);
-  k_id_final<<<1, 1, 0, st>>>(digests, nblk, id_out);
+  const size_t n0 = id_leaves(t.lay.total), n1 = id_mids(t.lay.total);
+  k_id_leaves<<<blocks_for(n0, 256), 256, 0, st>>>(t.ser, t.lay.total, digests);
+  k_id_mid<<<blocks_for(n1, 64), 64, 0, st>>>(digests, n0, digests + n0);
+  k_id_final<<<1, 1, 0, st>>>(digests + n0, n1, id_out);
   return hipGetLastError();
 }
 

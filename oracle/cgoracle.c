@@ -325,20 +325,38 @@ uint64_t cgo_fnv1a64(const uint8_t* data, size_t n) {
   return h;
 }
 
-/* Identity of a serialized table set, stamped into every blob: FNV-1a-64 of
- * the little-endian FNV-1a-64 digests of its consecutive 16 KiB blocks (the
- * last block may be shorter). */
-#define ID_BLOCK 16384
+/* Identity of a serialized table set, stamped into every blob (a digest of
+ * the codebook, which the pages leave to the implementation): a three-level
+ * FNV-1a-64 tree.  Leaves are the digests of consecutive 1 KiB blocks (the last
+ * may be shorter); each middle digest covers the little-endian bytes of up to
+ * 256 consecutive leaf digests; the id is the digest of the little-endian
+ * middle digests. */
+#define ID_LEAF 1024
+#define ID_FAN 256
+static uint64_t fnv1a64_of_digests(const uint64_t* d, size_t n) {
+  uint8_t* b = (uint8_t*)malloc(8 * (n ? n : 1));
+  for (size_t i = 0; i < n; i++)
+    for (int j = 0; j < 8; j++) b[8 * i + j] = (uint8_t)(d[i] >> (8 * j));
+  uint64_t h = cgo_fnv1a64(b, 8 * n);
+  free(b);
+  return h;
+}
 uint64_t cgo_tables_id(const uint8_t* data, size_t n) {
-  size_t nblk = (n + ID_BLOCK - 1) / ID_BLOCK;
-  uint8_t* d = (uint8_t*)malloc(8 * (nblk ? nblk : 1));
-  for (size_t b = 0; b < nblk; b++) {
-    size_t len = (n - ID_BLOCK * b < ID_BLOCK) ? n - ID_BLOCK * b : ID_BLOCK;
-    uint64_t h = cgo_fnv1a64(data + ID_BLOCK * b, len);
-    for (int j = 0; j < 8; j++) d[8 * b + j] = (uint8_t)(h >> (8 * j));
+  size_t n0 = (n + ID_LEAF - 1) / ID_LEAF;
+  size_t n1 = (n0 + ID_FAN - 1) / ID_FAN;
+  uint64_t* d0 = (uint64_t*)malloc(8 * (n0 ? n0 : 1));
+  uint64_t* d1 = (uint64_t*)malloc(8 * (n1 ? n1 : 1));
+  for (size_t i = 0; i < n0; i++) {
+    size_t len = (n - ID_LEAF * i < ID_LEAF) ? n - ID_LEAF * i : ID_LEAF;
+    d0[i] = cgo_fnv1a64(data + ID_LEAF * i, len);
   }
-  uint64_t id = cgo_fnv1a64(d, 8 * nblk);
-  free(d);
+  for (size_t j = 0; j < n1; j++) {
+    size_t cnt = (n0 - ID_FAN * j < ID_FAN) ? n0 - ID_FAN * j : ID_FAN;
+    d1[j] = fnv1a64_of_digests(d0 + ID_FAN * j, cnt);
+  }
+  uint64_t id = fnv1a64_of_digests(d1, n1);
+  free(d0);
+  free(d1);
   return id;
 }
 

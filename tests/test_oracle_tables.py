@@ -168,8 +168,21 @@ def test_fnv_and_tables_id(oracle_lib):
     assert oracle_lib.fnv1a64(b"a") == 0xaf63dc4c8601ec8c
     assert oracle_lib.fnv1a64(b"foobar") == 0x85944171f73967e8
     rng = np.random.default_rng(2)
-    for n in (1, 16383, 16384, 16385, 300000):
+
+    def fnv_of_digests(ds):
+        return oracle_lib.fnv1a64(b"".join(x.to_bytes(8, "little") for x in ds))
+
+    # the id is a three-level tree: 1 KiB leaves, middle digests over 256 leaves,
+    # the id over the middle digests (sizes straddle every boundary)
+    for n in (1, 1023, 1024, 1025, 262143, 262144, 262145, 600000):
         d = rng.integers(0, 256, n, dtype=np.uint8).tobytes()
-        blocks = [d[i:i + 16384] for i in range(0, n, 16384)]
-        digest = b"".join(oracle_lib.fnv1a64(b).to_bytes(8, "little") for b in blocks)
-        assert oracle_lib.tables_id(d) == oracle_lib.fnv1a64(digest)
+        leaves = [oracle_lib.fnv1a64(d[i:i + 1024]) for i in range(0, n, 1024)]
+        mids = [fnv_of_digests(leaves[j:j + 256]) for j in range(0, len(leaves), 256)]
+        assert oracle_lib.tables_id(d) == fnv_of_digests(mids)
+    # one changed byte anywhere changes the id
+    d = bytearray(rng.integers(0, 256, 300000, dtype=np.uint8).tobytes())
+    base = oracle_lib.tables_id(bytes(d))
+    for pos in (0, 1023, 1024, 262143, 262144, 299999):
+        e = bytearray(d)
+        e[pos] ^= 1
+        assert oracle_lib.tables_id(bytes(e)) != base
