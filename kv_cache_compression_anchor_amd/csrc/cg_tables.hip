@@ -162,12 +162,17 @@ struct HistArgs {
 
 // Delta-symbol histogram of one (kv, layer, 64-channel block, chunk): each lane
 // owns a channel, the four waves take interleaved groups; counts go to LDS with
-// atomics ([slot][symbol][lane] keeps the 64 lanes in distinct banks), then to
-// global memory with one atomic per non-zero bin.
+// atomics, two 16-bit counters per word (symbols s and s + 32; a chunk has at
+// most 65,535 deltas per channel), laid out [slot][s mod 32][lane] so that the
+// 64 lanes hit distinct banks; then to global memory with one atomic per
+// non-zero bin.
+constexpr int kHistWords = 3 * (kNSym / 2) * kLanes;
+
+template <int GS>
 __global__ __launch_bounds__(256) void k_histogram(HistArgs a) {
-  __shared__ uint32_t hist[3 * kNSym * kLanes];
+  __shared__ uint32_t hist[kHistWords];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  for (int j = tid; j < a.nq * kNSym * kLanes; j += 256) hist[j] = 0;
+  for (int j = tid; j < a.nq * (kNSym / 2) * kLanes; j += 256) hist[j] = 0;
   __syncthreads();
   const int c = blockIdx.x * kLanes + lane;
   const int chunk = blockIdx.y, l = blockIdx.z;
@@ -180,27 +185,65 @@ __global__ __launch_bounds__(256) void k_histogram(HistArgs a) {
     const float is0 = a.inv_step[0][pi];
     const float is1 = a.nq > 1 ? a.inv_step[1][pi] : 1.0f;
     const float is2 = a.nq > 2 ? a.inv_step[2][pi] : 1.0f;
-    const uint16_t* xc = a.x + ((size_t)l * a.T + t0) * a.C + c;
-    for (int g = wave; g < ng; g += 4) {
-      const int ta = g * a.G, te = min(ta + a.G, tc);
-      const float ahat = anchor_value(quant_anchor(half_bits_to_float(xc[(size_t)ta * a.C]), inv_a),
-                                      scale_a);
-      for (int t = ta + 1; t < te; t++) {
-        const float xv = half_bits_to_float(xc[(size_t)t * a.C]);
-        atomicAdd(&hist[(0 * kNSym + quant_delta(xv, ahat, is0)) * kLanes + lane], 1u);
-        if (a.nq > 1) atomicAdd(&hist[(1 * kNSym + quant_delta(xv, ahat, is1)) * kLanes + lane], 1u);
-        if (a.nq > 2) atomicAdd(&hist[(2 * kNSym + quant_delta(xv, ahat, is2)) * kLanes + lane], 1u);
+    // the chunk's rows of this layer: channel as the vector offset, token row as
+    // a scalar offset; rows past the chunk read as zero
+    const uint32_t row_bytes = 2u * (uint32_t)a.C;
+    const __amdgpu_buffer_rsrc_t xin = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.x + ((size_t)l * a.T + t0) * a.C), 0, (int)((uint32_t)tc * row_bytes),
+        kBufRsrcWord3);
+    const uint32_t lane_off = 2u * (uint32_t)c;
+    auto ld = [&](int t) -> uint32_t {
+      return __builtin_amdgcn_raw_buffer_load_b16(xin, lane_off, (uint32_t)t * row_bytes, 0);
+    };
+    auto count = [&](int slot, uint32_t sym) {
+      atomicAdd(&hist[(slot * (kNSym / 2) + (sym & 31u)) * kLanes + lane], 1u << ((sym >> 5) << 4));
+    };
+    auto group = [&](int n, auto half_of) {
+      const float ahat = anchor_value(quant_anchor(half_bits_to_float(half_of(0)), inv_a), scale_a);
+      for (int j = 1; j < n; j++) {
+        const float xv = half_bits_to_float(half_of(j));
+        count(0, quant_delta(xv, ahat, is0));
+        if (a.nq > 1) count(1, quant_delta(xv, ahat, is1));
+        if (a.nq > 2) count(2, quant_delta(xv, ahat, is2));
       }
+    };
+    int g = wave;
+    if constexpr (GS > 0) {
+      // full groups of the compile-time size, loaded one of this wave's groups
+      // ahead (the loop issues only loads to memory, so the waits are exact)
+      const int nfull = tc / GS;
+      uint32_t xa[GS], xb[GS];
+      auto load = [&](uint32_t (&xv)[GS], int gg) {
+#pragma unroll
+        for (int j = 0; j < GS; j++) xv[j] = ld(gg * GS + j);
+      };
+      load(xa, g);
+      load(xb, g + 4);
+      for (; g + 4 < nfull; g += 8) {
+        group(GS, [&](int j) { return xa[j]; });
+        load(xa, g + 8);
+        group(GS, [&](int j) { return xb[j]; });
+        load(xb, g + 12);
+      }
+      if (g < nfull) {
+        group(GS, [&](int j) { return xa[j]; });
+        g += 4;
+      }
+    }
+    for (; g < ng; g += 4) {
+      const int ta = g * a.G;
+      group(min(a.G, tc - ta), [&](int j) { return ld(ta + j); });
     }
   }
   __syncthreads();
-  for (int j = tid; j < a.nq * kNSym * kLanes; j += 256) {
+  for (int j = tid; j < a.nq * (kNSym / 2) * kLanes; j += 256) {
     const uint32_t v = hist[j];
     if (!v) continue;
-    const int s = j / (kNSym * kLanes), sym = (j / kLanes) % kNSym, ln = j % kLanes;
+    const int s = j / ((kNSym / 2) * kLanes), sym = (j / kLanes) % (kNSym / 2), ln = j % kLanes;
     const int cc = blockIdx.x * kLanes + ln;
     const size_t ti = (((size_t)a.kv * a.nq + s) * a.L + l) * a.C + cc;
-    atomicAdd(&a.counts[ti * kNSym + sym], v);
+    if (v & 0xFFFFu) atomicAdd(&a.counts[ti * kNSym + sym], v & 0xFFFFu);
+    if (v >> 16) atomicAdd(&a.counts[ti * kNSym + sym + kNSym / 2], v >> 16);
   }
 }
 
@@ -400,7 +443,10 @@ hipError_t launch_histogram(const uint16_t* x, int kv, const DevTables& t, uint3
   a.counts = counts;
   const int nchunks = (t.T + t.CH - 1) / t.CH;
   dim3 grid((unsigned)t.nblk, (unsigned)nchunks, (unsigned)t.L);
-  k_histogram<<<grid, 256, 0, st>>>(a);
+  if (t.G == 10)
+    k_histogram<10><<<grid, 256, 0, st>>>(a);
+  else
+    k_histogram<0><<<grid, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
