@@ -56,7 +56,22 @@ __global__ __launch_bounds__(256) void k_stats(const uint16_t* __restrict__ x, i
   const bool paired = has1 && ((C & 1) == 0);
   Acc a0 = {0, 0, 0, 0, 0, 0}, a1 = {0, 0, 0, 0, 0, 0};
   const uint16_t* base = x + (size_t)l * T * C + c0;
-  for (int t = tbeg + ph; t < tend; t += 2) {
+  int t = tbeg + ph;
+  if (paired) {
+    // eight rows' loads in flight before they are accumulated
+    constexpr int kU = 8;
+    for (; t + 2 * (kU - 1) < tend; t += 2 * kU) {
+      uint32_t w[kU];
+#pragma unroll
+      for (int j = 0; j < kU; j++) w[j] = *reinterpret_cast<const uint32_t*>(base + (size_t)(t + 2 * j) * C);
+#pragma unroll
+      for (int j = 0; j < kU; j++) {
+        accumulate(a0, w[j] & 0xFFFFu);
+        accumulate(a1, w[j] >> 16);
+      }
+    }
+  }
+  for (; t < tend; t += 2) {
     const uint16_t* p = base + (size_t)t * C;
     if (paired) {
       const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
