@@ -9,70 +9,103 @@
 namespace cg {
 namespace {
 
-// Range coder state of one lane.  Output bytes are final when emitted: a
-// possible carry is held back in `cache` plus a run of `pending` 0xFF bytes.
+// Range coder of one lane, producing the same bytes as a byte-at-a-time coder
+// with carry propagation, a whole 32-bit word at a time: `L` holds the coder's
+// 32-bit low window plus up to three output bytes not yet taken above it, so a
+// carry out of the window simply runs into those bytes.  A word leaves `L` once
+// four bytes sit above the window; the last one taken (`W`) and a run of
+// 0xFFFFFFFF words after it (`P`) stay open until no carry can reach them.
 struct RcEnc {
-  uint64_t low;     // < 2^33; bit 32 is a carry into the bytes held back
+  uint64_t L;       // window (bits 0..31) and the bytes above it (bits 32..kb-1)
+  uint32_t kb;      // 32 + 8 * bytes above the window: 32..56
   uint32_t range;
-  uint32_t cache;   // last byte not yet emitted
-  uint32_t pending; // 0xFF bytes after the cache
-  uint32_t have;    // cache holds a byte
-  uint32_t acc;     // bytes of the current output word, first byte highest
-  uint32_t nacc;
+  uint32_t W;       // last word taken out of L, not final yet
+  uint32_t P;       // 0xFFFFFFFF words after W, not final yet
+  uint32_t have;    // W holds a word
   uint32_t nw;      // words written
 };
 
-__device__ __forceinline__ void put_byte(RcEnc& e, uint32_t b, uint32_t* out) {
-  e.acc = (e.acc << 8) | (b & 0xFFu);
-  if (++e.nacc == 4) {
-    out[e.nw++] = e.acc;
-    e.acc = 0;
-    e.nacc = 0;
+__device__ __forceinline__ void emit_word(RcEnc& e, uint32_t w, uint32_t* out) { out[e.nw++] = w; }
+
+// a carry out of L reaches the open words: the 0xFFFFFFFF run wraps to zeros
+// (W + 1 and all of them but the last are then final), or W takes it
+__device__ __forceinline__ void carry_open(RcEnc& e, uint32_t* out) {
+  if (e.P) {
+    emit_word(e, e.W + 1u, out);
+    for (uint32_t j = 1; j < e.P; j++) emit_word(e, 0u, out);
+    e.W = 0;
+    e.P = 0;
+  } else {
+    e.W += 1u;
   }
 }
 
-__device__ __forceinline__ void shift_low(RcEnc& e, uint32_t* out) {
-  const uint32_t carry = (uint32_t)(e.low >> 32);
-  const uint32_t byte = (uint32_t)(e.low >> 24) & 0xFFu;
+// a word taken out of L: an all-ones word may still wrap, any other closes the
+// open words before it
+__device__ __forceinline__ void take_word(RcEnc& e, uint32_t wn, uint32_t* out) {
   if (!e.have) {
-    e.cache = byte;  // the first byte can still take a carry, never overflow
+    e.W = wn;
     e.have = 1;
-  } else if (byte != 0xFFu || carry) {
-    put_byte(e, e.cache + carry, out);
-    for (; e.pending; e.pending--) put_byte(e, 0xFFu + carry, out);
-    e.cache = byte;
+  } else if (wn == 0xFFFFFFFFu) {
+    e.P++;
   } else {
-    e.pending++;
+    emit_word(e, e.W, out);
+    for (; e.P; e.P--) emit_word(e, 0xFFFFFFFFu, out);
+    e.W = wn;
   }
-  e.low = (e.low & 0x00FFFFFFull) << 8;
+}
+
+__device__ __forceinline__ void add_low(RcEnc& e, uint64_t x, uint32_t* out) {
+  e.L += x;
+  if (e.L >> e.kb) {  // at most one carry out of the held bytes
+    e.L &= (1ull << e.kb) - 1ull;
+    carry_open(e, out);
+  }
+}
+
+// shift nb (0..2) bytes out of the window; a word leaves when four are held
+__device__ __forceinline__ void shift_bytes(RcEnc& e, uint32_t nb, uint32_t* out) {
+  const uint32_t kb = e.kb + 8u * nb;
+  if (kb >= 64u) {
+    const uint64_t L1 = e.L << (64u - e.kb);
+    take_word(e, (uint32_t)(L1 >> 32), out);
+    e.L = (L1 & 0xFFFFFFFFull) << (kb - 64u);
+    e.kb = kb - 32u;
+  } else {
+    e.L <<= 8u * nb;
+    e.kb = kb;
+  }
 }
 
 __device__ __forceinline__ void rc_put(RcEnc& e, uint32_t c0, uint32_t freq, uint32_t* out) {
   const uint32_t r = e.range >> kProbBits;
-  e.low += (uint64_t)mul24(r, c0);
-  e.range = mul24(r, freq);
-  while (e.range < kTop) {
-    shift_low(e, out);
-    e.range <<= 8;
-  }
+  add_low(e, (uint64_t)mul24(r, c0), out);
+  const uint32_t rn = mul24(r, freq);
+  const uint32_t nb = (uint32_t)__builtin_clz(rn) >> 3;  // renormalise while range < 2^24
+  e.range = rn << (8u * nb);
+  shift_bytes(e, nb, out);
 }
 
 // Flush: the fewest bytes (one or two) that name an aligned block inside
-// [low, low + range), so the stream decodes whatever bytes follow it.
+// [low, low + range), so the stream decodes whatever bytes follow it; then the
+// open words and the bytes still held, the last word padded with zero bytes.
 __device__ __forceinline__ void rc_finish(RcEnc& e, uint32_t* out) {
-  int k = 1;
-  uint64_t V = (e.low + 0xFFFFFFull) & ~0xFFFFFFull;
-  if (V + 0x1000000ull > e.low + e.range) {
-    k = 2;
-    V = (e.low + 0xFFFFull) & ~0xFFFFull;
+  const uint64_t win = e.L & 0xFFFFFFFFull;
+  uint32_t nb = 1;
+  uint64_t V = (win + 0xFFFFFFull) & ~0xFFFFFFull;
+  if (V + 0x1000000ull > win + e.range) {
+    nb = 2;
+    V = (win + 0xFFFFull) & ~0xFFFFull;
   }
-  e.low = V;
-  for (int j = 0; j < k; j++) shift_low(e, out);
+  e.L -= win;
+  add_low(e, V, out);
+  shift_bytes(e, nb, out);
   if (e.have) {
-    put_byte(e, e.cache, out);
-    for (; e.pending; e.pending--) put_byte(e, 0xFFu, out);
+    emit_word(e, e.W, out);
+    for (; e.P; e.P--) emit_word(e, 0xFFFFFFFFu, out);
   }
-  if (e.nacc) out[e.nw++] = e.acc << (8 * (4 - e.nacc));
+  const uint32_t k = (e.kb - 32u) >> 3;
+  if (k) emit_word(e, (uint32_t)(e.L >> 32) << (8u * (4u - k)), out);
 }
 
 // A workgroup is (group of up to 4 blobs of one quality, kv, layer, 64-channel
@@ -125,7 +158,7 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
   uint32_t* out = B.scratch + pi * a.swb;
   int8_t* anchors = reinterpret_cast<int8_t*>(B.blob + B.lay.off_anchor) +
                     ((size_t)kv * a.L + l) * B.ng * a.C + c;
-  RcEnc e = {0, 0xFFFFFFFFu, 0, 0, 0, 0, 0, 0};
+  RcEnc e = {0, 32u, 0xFFFFFFFFu, 0, 0, 0, 0};
   uint32_t nonfinite = 0;
 
   // one group from its tokens' binary16 bits: the anchor, then the deltas
