@@ -15,9 +15,11 @@ namespace {
 // carry out of the window simply runs into those bytes.  A word leaves `L` once
 // four bytes sit above the window; the last one taken (`W`) and a run of
 // 0xFFFFFFFF words after it (`P`) stay open until no carry can reach them.
+// The common steps are branch-free; the rare ones (the first word, an
+// all-ones word, a carry into an all-ones run) take branches of their own.
 struct RcEnc {
-  uint64_t L;       // window (bits 0..31) and the bytes above it (bits 32..kb-1)
-  uint32_t kb;      // 32 + 8 * bytes above the window: 32..56
+  uint64_t L;       // window (bits 0..31) and the bytes above it (bits 32..32+kh-1)
+  uint32_t kh;      // 8 * bytes above the window: 0..24
   uint32_t range;
   uint32_t W;       // last word taken out of L, not final yet
   uint32_t P;       // 0xFFFFFFFF words after W, not final yet
@@ -27,22 +29,18 @@ struct RcEnc {
 
 __device__ __forceinline__ void emit_word(RcEnc& e, uint32_t w, uint32_t* out) { out[e.nw++] = w; }
 
-// a carry out of L reaches the open words: the 0xFFFFFFFF run wraps to zeros
-// (W + 1 and all of them but the last are then final), or W takes it
-__device__ __forceinline__ void carry_open(RcEnc& e, uint32_t* out) {
-  if (e.P) {
-    emit_word(e, e.W + 1u, out);
-    for (uint32_t j = 1; j < e.P; j++) emit_word(e, 0u, out);
-    e.W = 0;
-    e.P = 0;
-  } else {
-    e.W += 1u;
-  }
+// a carry reached an all-ones run: it wraps to zeros, W + 1 and all but the
+// last zero word are final, the last zero word stays open
+__device__ __forceinline__ void carry_into_run(RcEnc& e, uint32_t* out) {
+  emit_word(e, e.W + 1u, out);
+  for (uint32_t j = 1; j < e.P; j++) emit_word(e, 0u, out);
+  e.W = 0;
+  e.P = 0;
 }
 
-// a word taken out of L: an all-ones word may still wrap, any other closes the
-// open words before it
-__device__ __forceinline__ void take_word(RcEnc& e, uint32_t wn, uint32_t* out) {
+// a word taken out of L in the rare cases: the first word, an all-ones word
+// (it may still wrap), or a word closing an all-ones run
+__device__ __forceinline__ void take_word_rare(RcEnc& e, uint32_t wn, uint32_t* out) {
   if (!e.have) {
     e.W = wn;
     e.have = 1;
@@ -57,23 +55,33 @@ __device__ __forceinline__ void take_word(RcEnc& e, uint32_t wn, uint32_t* out) 
 
 __device__ __forceinline__ void add_low(RcEnc& e, uint64_t x, uint32_t* out) {
   e.L += x;
-  if (e.L >> e.kb) {  // at most one carry out of the held bytes
-    e.L &= (1ull << e.kb) - 1ull;
-    carry_open(e, out);
+  // at most one carry out of the held bytes: it is bit 32 + kh
+  uint32_t hi = (uint32_t)(e.L >> 32);
+  const uint32_t c = hi >> e.kh;
+  hi = __builtin_amdgcn_ubfe(hi, 0, e.kh);
+  e.L = ((uint64_t)hi << 32) | (uint32_t)e.L;
+  if (c && e.P) {
+    carry_into_run(e, out);
+  } else {
+    e.W += c;
   }
 }
 
-// shift nb (0..2) bytes out of the window; a word leaves when four are held
-__device__ __forceinline__ void shift_bytes(RcEnc& e, uint32_t nb, uint32_t* out) {
-  const uint32_t kb = e.kb + 8u * nb;
-  if (kb >= 64u) {
-    const uint64_t L1 = e.L << (64u - e.kb);
-    take_word(e, (uint32_t)(L1 >> 32), out);
-    e.L = (L1 & 0xFFFFFFFFull) << (kb - 64u);
-    e.kb = kb - 32u;
-  } else {
-    e.L <<= 8u * nb;
-    e.kb = kb;
+// shift nb8 / 8 (0..2) bytes out of the window; a word leaves when four are held
+__device__ __forceinline__ void shift_bytes(RcEnc& e, uint32_t nb8, uint32_t* out) {
+  const uint32_t kh2 = e.kh + nb8;
+  const bool ext = kh2 >= 32u;
+  const uint64_t L1 = e.L << (ext ? 32u - e.kh : nb8);
+  const uint32_t wn = (uint32_t)(L1 >> 32);
+  e.L = ext ? (uint64_t)(uint32_t)L1 << (kh2 - 32u) : L1;
+  e.kh = ext ? kh2 - 32u : kh2;
+  if (ext) {
+    if (e.have && e.P == 0 && wn != 0xFFFFFFFFu) {
+      emit_word(e, e.W, out);
+      e.W = wn;
+    } else {
+      take_word_rare(e, wn, out);
+    }
   }
 }
 
@@ -81,9 +89,9 @@ __device__ __forceinline__ void rc_put(RcEnc& e, uint32_t c0, uint32_t freq, uin
   const uint32_t r = e.range >> kProbBits;
   add_low(e, (uint64_t)mul24(r, c0), out);
   const uint32_t rn = mul24(r, freq);
-  const uint32_t nb = (uint32_t)__builtin_clz(rn) >> 3;  // renormalise while range < 2^24
-  e.range = rn << (8u * nb);
-  shift_bytes(e, nb, out);
+  const uint32_t nb8 = (uint32_t)__builtin_clz(rn) & 24u;  // renormalise while range < 2^24
+  e.range = rn << nb8;
+  shift_bytes(e, nb8, out);
 }
 
 // Flush: the fewest bytes (one or two) that name an aligned block inside
@@ -91,20 +99,20 @@ __device__ __forceinline__ void rc_put(RcEnc& e, uint32_t c0, uint32_t freq, uin
 // open words and the bytes still held, the last word padded with zero bytes.
 __device__ __forceinline__ void rc_finish(RcEnc& e, uint32_t* out) {
   const uint64_t win = e.L & 0xFFFFFFFFull;
-  uint32_t nb = 1;
+  uint32_t nb8 = 8;
   uint64_t V = (win + 0xFFFFFFull) & ~0xFFFFFFull;
   if (V + 0x1000000ull > win + e.range) {
-    nb = 2;
+    nb8 = 16;
     V = (win + 0xFFFFull) & ~0xFFFFull;
   }
   e.L -= win;
   add_low(e, V, out);
-  shift_bytes(e, nb, out);
+  shift_bytes(e, nb8, out);
   if (e.have) {
     emit_word(e, e.W, out);
     for (; e.P; e.P--) emit_word(e, 0xFFFFFFFFu, out);
   }
-  const uint32_t k = (e.kb - 32u) >> 3;
+  const uint32_t k = e.kh >> 3;
   if (k) emit_word(e, (uint32_t)(e.L >> 32) << (8u * (4u - k)), out);
 }
 
@@ -137,7 +145,8 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
     for (int j = threadIdx.x; j < kImgRows * kLanes / 2; j += blockDim.x) dst[j] = src[j];
   }
   __syncthreads();
-  const int bi = eg.blob[wave];
+  // wave-uniform, so that the blob's fields and buffer resources live in SGPRs
+  const int bi = __builtin_amdgcn_readfirstlane(eg.blob[wave]);
   if (bi < 0) return;
   const EncBlob& B = a.b[bi];
   const int kv = unit / (a.L * a.nblk);
@@ -158,7 +167,7 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
   uint32_t* out = B.scratch + pi * a.swb;
   int8_t* anchors = reinterpret_cast<int8_t*>(B.blob + B.lay.off_anchor) +
                     ((size_t)kv * a.L + l) * B.ng * a.C + c;
-  RcEnc e = {0, 32u, 0xFFFFFFFFu, 0, 0, 0, 0};
+  RcEnc e = {0, 0u, 0xFFFFFFFFu, 0, 0, 0, 0};
   uint32_t nonfinite = 0;
 
   // one group from its tokens' binary16 bits: the anchor, then the deltas

@@ -186,7 +186,8 @@ constexpr int kHistWords = 3 * (kNSym / 2) * kLanes;
 template <int GS>
 __global__ __launch_bounds__(256) void k_histogram(HistArgs a) {
   __shared__ uint32_t hist[kHistWords];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // token rows are scalar offsets
   for (int j = tid; j < a.nq * (kNSym / 2) * kLanes; j += 256) hist[j] = 0;
   __syncthreads();
   const int c = blockIdx.x * kLanes + lane;
