@@ -150,10 +150,19 @@ def main():
     ratio_q = {("HML"[q]): eight_bit / sum(sizes[(c, q)] for c in range(nch)) for q in w.qualities}
 
     traffic = decode_traffic(args.traffic_json, w.name)
+    # algorithmic bytes of the other two steps: every encoded blob reads its
+    # chunk's fp16 K/V once and writes the blob; building reads K/V twice
+    # (statistics, then the histogram)
+    chunk_elems = {c: 2 * w.layers * min(w.chunk_tokens, w.tokens - c * w.chunk_tokens) * w.channels
+                   for c in range(nch)}
+    enc_bytes = sum(2 * chunk_elems[c] + n for (c, q), n in sizes.items())
+    enc_achieved = enc_bytes / (enc_ms * 1e-3) / 1e9
+    build_achieved = 2 * fp16_bytes / (build_ms * 1e-3) / 1e9
 
-    cpu = None
+    cpu = cpu_enc = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, k, v, results[-1]["tab"], bufs, sizes, sel, args.cpu_sample_seconds)
+        cpu_enc = cpu_baseline_encode(w, k, v, results[-1]["tab"], args.cpu_sample_seconds / 2)
 
     line = {
         "metric": "decode GB/s (fp16 KV out) + compress ratio vs 8-bit, Mistral-7B-shape 9K tok",
@@ -186,6 +195,13 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
         "cpu_baseline": cpu,
+        "encode_roofline": {"bound": "hbm", "kernel": "k_encode + k_pack (all 18 blobs)",
+                            "achieved": round(enc_achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                            "frac": round(enc_achieved / HBM_PEAK_GBPS, 4)},
+        "build_roofline": {"bound": "hbm", "kernel": "cg_build_tables (all kernels)",
+                           "achieved": round(build_achieved, 2), "peak": HBM_PEAK_GBPS,
+                           "unit": "GB/s", "frac": round(build_achieved / HBM_PEAK_GBPS, 4)},
+        "cpu_baseline_encode": cpu_enc,
         "input_generation_s": round(t_gen, 2),
     }
     print(json.dumps(line), flush=True)
@@ -328,6 +344,31 @@ def cpu_baseline(w, k, v, tab, bufs, sizes, sel, seconds):
             "sample": f"oracle decode of {n} chunk blobs of the selection "
                       f"({n // len(blobs)}+ passes, {2 * w.layers * tok * w.channels} elements, "
                       f"{dt:.1f} s)"}
+
+
+def cpu_baseline_encode(w, k, v, tab, seconds):
+    """The oracle encoding chunks of the workload (H, M, L in turn) on this host's
+    cores until about `seconds` have passed; GB/s of fp16 read (one chunk's K/V
+    per blob)."""
+    import kv_cache_compression_anchor_amd as cg
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    t = cg.cg_tables_serialize(tab)
+    n = 0
+    elems = 0
+    t0 = time.perf_counter()
+    while True:
+        c = n % w.n_chunks
+        q = w.qualities[n % len(w.qualities)]
+        oracle.encode_chunk(t, k, v, c, q, threads=threads)
+        elems += 2 * w.layers * min(w.chunk_tokens, w.tokens - c * w.chunk_tokens) * w.channels
+        n += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
+    return {"value": round(2 * elems / dt / 1e9, 4), "unit": "GB/s of fp16 in", "cores": threads,
+            "kind": "oracle",
+            "sample": f"oracle encode of {n} chunk blobs ({elems} elements, {dt:.1f} s)"}
 
 
 if __name__ == "__main__":

@@ -549,7 +549,10 @@ int cg_encode_batch(const cg_tables* ch, const void* k_dev, const void* v_dev, i
   for (int i = 0; i < n; i++) order[i] = i;
   std::stable_sort(order.begin(), order.end(),
                    [&](int x, int y) { return qualities[x] < qualities[y]; });
-  for (int i0 = 0; i0 < n; i0 += slots) {
+  // launches of equal size (a small last launch would leave most of the GPU idle)
+  const int launches = (n + slots - 1) / slots;
+  const int per_launch = (n + launches - 1) / launches;
+  for (int i0 = 0; i0 < n; i0 += per_launch) {
     EncodeArgs a;
     memset(&a, 0, sizeof(a));
     a.k = static_cast<const uint16_t*>(k_dev);
@@ -559,7 +562,7 @@ int cg_encode_batch(const cg_tables* ch, const void* k_dev, const void* v_dev, i
     a.C = t.C;
     a.G = t.G;
     a.nblk = t.nblk;
-    a.nblobs = std::min(slots, n - i0);
+    a.nblobs = std::min(per_launch, n - i0);
     a.swb = swb;
     a.scale_a = reinterpret_cast<const float*>(t.ser + t.lay.off_scale_a);
     a.inv_a = reinterpret_cast<const float*>(t.ser + t.lay.off_inv_a);
