@@ -27,9 +27,25 @@ __device__ __forceinline__ int ld8s(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ u32x4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// a ring block of RB (2 or 4) words
+template <int RB>
+struct Block;
+template <>
+struct Block<2> {
+  u32x2 v;
+  __device__ static Block load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return {__builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0)};
+  }
+};
+template <>
+struct Block<4> {
+  u32x4 v;
+  __device__ static Block load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return {__builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0)};
+  }
+};
 
 // The kernel's LDS is all dynamic, so it starts at LDS address 0: pointers are
 // formed from byte addresses directly (constant parts of an address then fold
@@ -42,13 +58,18 @@ __device__ __forceinline__ __attribute__((address_space(3))) T* lds_at(uint32_t 
 __device__ __forceinline__ uint32_t lds32(uint32_t addr) { return *lds_at<uint32_t>(addr); }
 __device__ __forceinline__ uint32_t lds16(uint32_t addr) { return *lds_at<uint16_t>(addr); }
 
-// four words into consecutive ring slots (slots are 256 bytes apart)
-__device__ __forceinline__ void lds_put4(uint32_t lane_addr, uint32_t slot_off, u32x4 v) {
+// a block's words into consecutive ring slots (slots are 256 bytes apart)
+__device__ __forceinline__ void lds_put(uint32_t lane_addr, uint32_t slot_off, const Block<2>& b) {
   auto p = lds_at<uint32_t>(lane_addr + slot_off);
-  p[0] = v.x;
-  p[64] = v.y;
-  p[128] = v.z;
-  p[192] = v.w;
+  p[0] = b.v.x;
+  p[64] = b.v.y;
+}
+__device__ __forceinline__ void lds_put(uint32_t lane_addr, uint32_t slot_off, const Block<4>& b) {
+  auto p = lds_at<uint32_t>(lane_addr + slot_off);
+  p[0] = b.v.x;
+  p[64] = b.v.y;
+  p[128] = b.v.z;
+  p[192] = b.v.w;
 }
 
 // (float)((x >> 8) & 0xFF) in one instruction
@@ -64,10 +85,13 @@ __device__ __forceinline__ float byte1_to_float(uint32_t x) {
 // k * 256 + (kv * 128 + 2 * slot) and bits 8..15 of it are k itself.
 constexpr uint32_t kRow = 4 * kLanes;
 constexpr uint32_t kTabBytes = kImgRows * kRow;        // 16,640
-constexpr uint32_t kRingBytes = 8 * 4 * kLanes;        // 8 slots x 64 lanes x 4 B
-// first wave's word ring, aligned to the ring size so that a slot address is
-// the lane's ring address with the slot number in bits 8..10
-constexpr uint32_t kRingBase = (kTabBytes + kRingBytes - 1) / kRingBytes * kRingBytes;
+// A wave's word ring: 2 * RB slots (two blocks of RB words) x 64 lanes x 4 B.
+// The first wave's ring is aligned to the ring size, so a slot address is the
+// lane's ring address with the slot number in the bits above 7.
+__host__ __device__ constexpr uint32_t ring_bytes(int rb) { return 2u * rb * 4u * kLanes; }
+__host__ __device__ constexpr uint32_t ring_base(int rb) {
+  return (kTabBytes + ring_bytes(rb) - 1) / ring_bytes(rb) * ring_bytes(rb);
+}
 
 // All ones when r * key <= code, else zero.  ncode is ~code, so the 64-bit sum
 // r * key + (2^64 - code - 1) stays within [2^64 - 2^32, 2^64) when
@@ -78,11 +102,13 @@ __device__ __forceinline__ uint32_t le_mask(uint32_t r, uint32_t key, uint32_t n
   return (uint32_t)(((uint64_t)r * key + c) >> 32);
 }
 
-// GS: group size fixed at compile time (0 = the runtime a.G only)
-template <int GS>
+// GS: group size fixed at compile time (0 = the runtime a.G only).
+// RB: words per fetched block (4 in workgroups of several chunks; 2 when a
+// workgroup holds one chunk, so that eight of them fit a CU's LDS).
+template <int GS, int RB>
 __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
   // LDS: the tables at 0 ([65 rows][K: 64 u16 | V: 64 u16]), then one word
-  // ring per wave ([8 slots][64 lanes] u32)
+  // ring per wave ([2 RB slots][64 lanes] u32)
   auto tab = lds_at<uint32_t>(0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -146,17 +172,19 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
   uint64_t bb = ((uint64_t)~ld32(rs, sbase + 4u) << 32) | ~ld32(rs, sbase + 8u);
   uint32_t left = 64;
   uint32_t range = 0xFFFFFFFFu;
-  const uint32_t ring = kRingBase + (uint32_t)wave * kRingBytes + 4u * (uint32_t)lane;
+  constexpr uint32_t kSlotMask = (2u * RB - 1u) << 8;
+  const uint32_t ring = ring_base(RB) + (uint32_t)wave * ring_bytes(RB) + 4u * (uint32_t)lane;
   // ring words taken and written, counted in units of 256 (one slot's size)
   uint32_t taken = 0;
-  uint32_t landed = 8u << 8;  // words 3..10, written below
-  uint32_t fetch_off = sbase + 44u;  // next 16-byte block: word 11
+  uint32_t landed = (2u * RB) << 8;                  // words 3 .. 2 RB + 2, written below
+  uint32_t fetch_off = sbase + 12u + 8u * RB;        // the next block
   {
-    const u32x4 b0 = ld128(rs, sbase + 12u), b1 = ld128(rs, sbase + 28u);
-    lds_put4(ring, 0u, b0);
-    lds_put4(ring, 4u * 256u, b1);
+    const Block<RB> b0 = Block<RB>::load(rs, sbase + 12u);
+    const Block<RB> b1 = Block<RB>::load(rs, sbase + 12u + 4u * RB);
+    lds_put(ring, 0u, b0);
+    lds_put(ring, (uint32_t)RB << 8, b1);
   }
-  u32x4 pend = {0u, 0u, 0u, 0u};  // block in flight
+  Block<RB> pend = {};  // block in flight
   bool inflight = false;
 
   // output rows of this (kv, layer, chunk) through a buffer resource: the lane's
@@ -195,7 +223,7 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
   // in one group, which typical data never does) falls back to a direct load.
   auto refill = [&]() {
     const bool take = left < 32;
-    const uint32_t slot = (taken & 0x700u) | ring;
+    const uint32_t slot = (taken & kSlotMask) | ring;
     if (take && taken >= landed)
       *lds_at<uint32_t>(slot) = ld32(rs, sbase + 12u + (taken >> 6));
     const uint32_t w = lds32(slot);
@@ -210,12 +238,12 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
   // without room point their load past the blob end: no memory access)
   auto ring_step = [&]() {
     if (inflight) {
-      lds_put4(ring, landed & 0x400u, pend);
-      landed += 4u * 256u;
+      lds_put(ring, landed & ((uint32_t)RB << 8), pend);
+      landed += (uint32_t)RB << 8;
     }
-    inflight = landed + 4u * 256u <= taken + 8u * 256u;
-    pend = ld128(rs, inflight ? fetch_off : 0xFFFFFFF0u);
-    if (inflight) fetch_off += 16u;
+    inflight = landed + ((uint32_t)RB << 8) <= taken + ((2u * RB) << 8);
+    pend = Block<RB>::load(rs, inflight ? fetch_off : 0xFFFFFFF0u);
+    if (inflight) fetch_off += 4u * RB;
   };
 
   // one group: the anchor row, then its deltas in pairs (a lone last one when
@@ -266,11 +294,20 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   const unsigned blocks = (unsigned)(a.n_groups * a.L * a.nblk);
-  const size_t lds_bytes = kRingBase + (size_t)2 * a.waves * kRingBytes;
-  if (a.G == 10)
-    k_decode<10><<<blocks, 2 * kLanes * a.waves, lds_bytes, st>>>(a);
-  else
-    k_decode<0><<<blocks, 2 * kLanes * a.waves, lds_bytes, st>>>(a);
+  const dim3 grid(blocks), block(2 * kLanes * a.waves);
+  if (a.waves == 1) {  // one chunk per workgroup: small rings
+    const size_t lds = ring_base(2) + (size_t)2 * a.waves * ring_bytes(2);
+    if (a.G == 10)
+      k_decode<10, 2><<<grid, block, lds, st>>>(a);
+    else
+      k_decode<0, 2><<<grid, block, lds, st>>>(a);
+  } else {
+    const size_t lds = ring_base(4) + (size_t)2 * a.waves * ring_bytes(4);
+    if (a.G == 10)
+      k_decode<10, 4><<<grid, block, lds, st>>>(a);
+    else
+      k_decode<0, 4><<<grid, block, lds, st>>>(a);
+  }
   return hipGetLastError();
 }
 
