@@ -40,6 +40,11 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (for HBM counter scaling)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "decode_traffic.json"))
+    ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                          "COPY_WRITE_CSV"),
+                    help="write the --workload's record of --traffic-json from rocprofv3 --pmc "
+                         "counter_collection.csv files (FETCH_SIZE and WRITE_SIZE of the decoder, "
+                         "then of a --copy-calibration run); no GPU work")
     ap.add_argument("--streamed", action="store_true",
                     help="measure the chunk pipeline instead: the Llama-70B-shape 16K schedule "
                          "decoded from pinned host memory (H2D on one stream, decode on another)")
@@ -48,6 +53,9 @@ def parse():
 
 def main():
     args = parse()
+    if args.record_traffic:
+        record_traffic(args.traffic_json, args.workload, *args.record_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the codec's streams are independent, sharding is described in DESIGN.md)",
@@ -165,7 +173,9 @@ def main():
         cpu_enc = cpu_baseline_encode(w, k, v, results[-1]["tab"], args.cpu_sample_seconds / 2)
 
     line = {
-        "metric": "decode GB/s (fp16 KV out) + compress ratio vs 8-bit, Mistral-7B-shape 9K tok",
+        "metric": ("decode GB/s (fp16 KV out) + compress ratio vs 8-bit, Mistral-7B-shape 9K tok"
+                   if w.name == "mistral7b_9k" else
+                   f"decode GB/s (fp16 KV out) + compress ratio vs 8-bit, {w.name}"),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -300,18 +310,71 @@ DECODE_SOURCES = ["kv_cache_compression_anchor_amd/csrc/cg_decode.hip",
 def decode_traffic(path, workload):
     """HBM bytes per decode launch from the committed FETCH_SIZE / WRITE_SIZE
     counter runs (scaled by the same counters on a plain copy of known size);
-    None when the record is for another workload or the decoder changed since."""
-    import hashlib
+    None when there is no record for the workload or the decoder changed since."""
     try:
         rec = json.load(open(path))
-        src = b"".join(open(os.path.join(ROOT, p), "rb").read() for p in DECODE_SOURCES)
-        if rec.get("workload") != workload:
+        if rec.get("kernel_source_sha256") != decoder_source_sha256():
             return None
-        if rec.get("kernel_source_sha256") != hashlib.sha256(src).hexdigest():
-            return None
-        return int(rec["bytes_per_launch"])
+        return int(rec["workloads"][workload]["bytes_per_launch"])
     except (OSError, ValueError, KeyError):
         return None
+
+
+def decoder_source_sha256():
+    import hashlib
+    src = b"".join(open(os.path.join(ROOT, p), "rb").read() for p in DECODE_SOURCES)
+    return hashlib.sha256(src).hexdigest()
+
+
+def _counter_per_dispatch(csv_path, kernel_prefix):
+    """{dispatch id: counter value summed over the rows of that dispatch} for
+    the dispatches whose kernel name starts with kernel_prefix."""
+    import csv
+    out = {}
+    with open(csv_path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r["Kernel_Name"].startswith(kernel_prefix):
+                d = int(r["Dispatch_Id"])
+                out[d] = out.get(d, 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def record_traffic(path, workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """Store the decoder's HBM bytes per launch for `workload`: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch, averaged over the decoder's dispatches), each
+    scaled so that the same counter reads the true byte count of a plain copy
+    (the largest copy dispatches of a --copy-calibration run)."""
+    dec = "void cg::(anonymous namespace)::k_decode<"
+    fk = list(_counter_per_dispatch(fetch_csv, dec).values())
+    wk = list(_counter_per_dispatch(write_csv, dec).values())
+    cf = list(_counter_per_dispatch(copy_fetch_csv, "__amd_rocclr_copyBuffer").values())
+    cw = list(_counter_per_dispatch(copy_write_csv, "__amd_rocclr_copyBuffer").values())
+    if not (fk and wk and cf and cw):
+        raise SystemExit("record-traffic: a counter file holds no decoder or copy dispatch")
+    copy_bytes = 1 << 30
+    cf_kib, cw_kib = max(cf), max(cw)
+    fetch_scale = copy_bytes / 1024 / cf_kib
+    write_scale = copy_bytes / 1024 / cw_kib
+    f_kib, w_kib = sum(fk) / len(fk), sum(wk) / len(wk)
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        rec = {}
+    sha = decoder_source_sha256()
+    if rec.get("kernel_source_sha256") != sha:
+        rec = {"kernel": "k_decode", "kernel_source_sha256": sha, "workloads": {}}
+    rec["copy_calibration"] = {"bytes": copy_bytes, "fetch_kib": cf_kib, "write_kib": cw_kib,
+                               "fetch_scale": fetch_scale, "write_scale": write_scale}
+    rec.setdefault("workloads", {})[workload] = {
+        "dispatches": len(fk),
+        "fetch_kib_per_dispatch": f_kib,
+        "write_kib_per_dispatch": w_kib,
+        "bytes_per_launch": int(round(1024 * (f_kib * fetch_scale + w_kib * write_scale))),
+    }
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec["workloads"][workload]))
 
 
 def cpu_baseline(w, k, v, tab, bufs, sizes, sel, seconds):

@@ -29,6 +29,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Cache policy of the fp16 output stores: non-temporal.  The decoded rows are
+// written once and not read back here; streaming them past the L2 leaves it to
+// the lanes' stream bytes, which are re-read 8 or 16 bytes at a time.
+constexpr int kStoreNT = 2;
+
 // a ring block of RB (2 or 4) words
 template <int RB>
 struct Block;
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
     ncode = (ncode << sh) | __builtin_amdgcn_ubfe((uint32_t)(bb >> (t & 63u)), 0u, sh);
     left = t;
     const float y = __builtin_fmaf(byte1_to_float(ad), step, base);
-    __builtin_amdgcn_raw_buffer_store_b16(float_to_half_bits(y), ro, lane_off, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b16(float_to_half_bits(y), ro, lane_off, soff, kStoreNT);
   };
 
   // A lane takes a word when fewer than 32 bits remain (two symbols need at
@@ -254,7 +259,7 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
     anc_next = ld8s(rs, anc_base + (uint32_t)(g + 1) * a.C);  // past the last group: unused
     const float ahat = anchor_value(anc, scale_a);
     __builtin_amdgcn_raw_buffer_store_b16(float_to_half_bits(ahat), ro, lane_off,
-                                          (uint32_t)ta * row_bytes, 0);
+                                          (uint32_t)ta * row_bytes, kStoreNT);
     const float base = __builtin_fmaf(-32.0f, step, ahat);
     int t = ta + 1;
 #pragma unroll

@@ -1,0 +1,62 @@
+"""Host-side logic of bench.py: the HBM-traffic record written from rocprofv3
+counter files, and the one-GPU guard.  No GPU work."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+DEC = "void cg::(anonymous namespace)::k_decode<10, 4>(cg::DecodeArgs)"
+ENC = "void cg::(anonymous namespace)::k_encode<10>(cg::EncodeArgs)"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+def _counters(path, rows):
+    """A counter_collection.csv with the columns bench.py reads; rows are
+    (dispatch id, kernel name, value), several rows per dispatch allowed."""
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for d, k, v in rows:
+            w.writerow([d, k, "X", v])
+    return str(path)
+
+
+def test_record_then_read_traffic(tmp_path):
+    # a decoder dispatch split over two rows (summed), an encoder dispatch that
+    # must be ignored, a copy that reads half its bytes on FETCH_SIZE
+    fetch = _counters(tmp_path / "f.csv", [(5, ENC, 999.0), (7, DEC, 300.0), (7, DEC, 200.0)])
+    write = _counters(tmp_path / "w.csv", [(5, ENC, 1.0), (7, DEC, 1500.0)])
+    cf = _counters(tmp_path / "cf.csv", [(1, "fill", 3.0), (2, COPY, 524288.0), (3, COPY, 10.0)])
+    cw = _counters(tmp_path / "cw.csv", [(2, COPY, 1048576.0)])
+    out = tmp_path / "traffic.json"
+    bench.record_traffic(str(out), "wl", fetch, write, cf, cw)
+    rec = json.load(open(out))
+    assert rec["copy_calibration"]["fetch_scale"] == pytest.approx(2.0)
+    assert rec["copy_calibration"]["write_scale"] == pytest.approx(1.0)
+    assert rec["workloads"]["wl"]["bytes_per_launch"] == 1024 * (500 * 2 + 1500)
+    assert bench.decode_traffic(str(out), "wl") == 1024 * 2500
+    assert bench.decode_traffic(str(out), "other") is None
+    # a second workload joins the same record
+    bench.record_traffic(str(out), "wl2", fetch, write, cf, cw)
+    assert set(json.load(open(out))["workloads"]) == {"wl", "wl2"}
+
+
+def test_traffic_is_dropped_when_the_decoder_changes(tmp_path):
+    out = tmp_path / "traffic.json"
+    json.dump({"kernel": "k_decode", "kernel_source_sha256": "0" * 64,
+               "workloads": {"wl": {"bytes_per_launch": 1}}}, open(out, "w"))
+    assert bench.decode_traffic(str(out), "wl") is None
+    assert bench.decode_traffic(str(tmp_path / "missing.json"), "wl") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
