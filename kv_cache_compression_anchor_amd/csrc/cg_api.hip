@@ -324,7 +324,7 @@ int cg_build_tables(const cg_params* params, const void* k_dev, const void* v_de
   }
   const size_t n = t.lay.n;
   const size_t counts_words = (size_t)n * t.lay.nq * kNSym;
-  const size_t tmp_bytes = 4 * 8 * n + 4 * n + 16 + 4 * counts_words;
+  const size_t tmp_bytes = 3 * 8 * n + 4 * n + 16 + 4 * counts_words;
   uint8_t* tmp = nullptr;
   hipError_t e = hipMalloc(&tmp, tmp_bytes);
   if (e != hipSuccess) {
@@ -334,8 +334,7 @@ int cg_build_tables(const cg_params* params, const void* k_dev, const void* v_de
   StatsBuf sb;
   sb.s1 = reinterpret_cast<uint64_t*>(tmp);
   sb.sa = sb.s1 + n;
-  sb.sb = sb.sa + n;
-  sb.sc = sb.sb + n;
+  sb.sc = sb.sa + n;
   sb.amax = reinterpret_cast<uint32_t*>(sb.sc + n);
   sb.flags = sb.amax + n;
   uint32_t* counts = sb.flags + 4;

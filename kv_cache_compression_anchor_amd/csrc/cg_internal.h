@@ -92,21 +92,29 @@ inline size_t stream_words_bound(int64_t n) { return (stream_bytes_bound(n) + 3)
 // ----------------------------------------------------------------------------
 // Per-lane quantiser (binary32, no contraction; identical in every kernel)
 // ----------------------------------------------------------------------------
+// The clamps are one v_med3_f32 each: for every value but NaN it equals
+// min(max(r, lo), hi).  NaN arises only from non-finite input, which every
+// caller flags and rejects; its code stays in range either way.
 __device__ __forceinline__ int quant_anchor(float x, float inv_a) {
   float p = x * inv_a;
   float r = __builtin_rintf(p);
-  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  r = __builtin_amdgcn_fmed3f(r, -127.0f, 127.0f);
   return (int)r;
 }
 
 __device__ __forceinline__ float anchor_value(int a, float scale_a) { return (float)a * scale_a; }
 
-__device__ __forceinline__ uint32_t quant_delta(float x, float ahat, float inv_step) {
+// the delta's level in -32 .. 31 (the symbol minus 32)
+__device__ __forceinline__ int quant_delta_level(float x, float ahat, float inv_step) {
   float d = x - ahat;
   float u = d * inv_step;
   float r = __builtin_rintf(u);
-  r = fminf(fmaxf(r, -32.0f), 31.0f);
-  return (uint32_t)((int)r + 32);
+  r = __builtin_amdgcn_fmed3f(r, -32.0f, 31.0f);
+  return (int)r;
+}
+
+__device__ __forceinline__ uint32_t quant_delta(float x, float ahat, float inv_step) {
+  return (uint32_t)(quant_delta_level(x, ahat, inv_step) + 32);
 }
 
 // binary16 <-> binary32 with the hardware conversions (round to nearest even,
@@ -145,10 +153,9 @@ struct DevTables {
 };
 
 struct StatsBuf {
-  uint64_t* s1;    // sum of x*2^24 (two's complement)
-  uint64_t* sa;    // sum of (|X|>>20)^2
-  uint64_t* sb;    // sum of (|X|>>20)*(|X|&0xFFFFF)
-  uint64_t* sc;    // sum of (|X|&0xFFFFF)^2
+  uint64_t* s1;    // sum of X = x*2^24 (two's complement)
+  uint64_t* sa;    // sum over workgroups of (their sum of X^2) >> 40
+  uint64_t* sc;    // sum over workgroups of (their sum of X^2) mod 2^40
   uint32_t* amax;  // max |x| as binary16 magnitude bits
   uint32_t* flags; // [0]: non-finite input, [1]: degenerate step
 };

@@ -11,104 +11,101 @@ namespace {
 
 constexpr int kStatsRows = 1024;  // tokens per stats workgroup
 
-struct Acc {
-  uint64_t s1, sa, sb, sc;
-  uint32_t amax, nf;
-};
+// Exact moments of X = |x| * 2^24 for binary16 x.  A finite x is M * 2^(E-24)
+// with M = m (+ 1024 when the exponent field e is not 0) and E = max(e - 1, 0),
+// so X = M << E.  Each element adds only to its bucket, the binary16 bits
+// 10..15 (sign and e): the packed word m + 2^20 (sum of m below bit 20, count
+// above; a bucket sees at most 1024 elements) and m^2.  The buckets are folded
+// into S1 = sum of signed X and S2 = sum of X^2 once per workgroup:
+//   sum M = sum m + 1024 n,   sum M^2 = sum m^2 + 2048 sum m + 2^20 n   (e > 0).
+// LDS: [64 buckets][packed | squares][64 lanes] u32.
+constexpr int kStatsWords = 64 * 2 * kLanes;
 
-// |X| = |x| * 2^24 = M << E for a finite binary16 x; split as A*2^20 + B so that
-// the squares fit 64-bit partial sums: X^2 = A^2 2^40 + 2AB 2^20 + B^2.
-__device__ __forceinline__ void accumulate(Acc& a, uint32_t h) {
-  const uint32_t e = (h >> 10) & 31u, m = h & 1023u;
-  if (e == 31u) {
-    a.nf = 1;
-    return;
-  }
-  const uint32_t M = e ? (m | 1024u) : m;
-  const uint32_t E = e ? e - 1u : 0u;
-  uint32_t A, B;
-  if (E < 20u) {
-    const uint32_t v = M << E;
-    A = v >> 20;
-    B = v & 0xFFFFFu;
-  } else {
-    A = M << (E - 20u);
-    B = 0;
-  }
-  a.sa += (uint64_t)A * A;
-  a.sb += (uint64_t)A * B;
-  a.sc += (uint64_t)B * B;
-  const uint64_t mag = ((uint64_t)A << 20) | B;
-  a.s1 += (h & 0x8000u) ? (0ull - mag) : mag;
-  a.amax = max(a.amax, h & 0x7FFFu);
+__device__ __forceinline__ void stats_add(uint32_t* bk, uint32_t h, uint32_t lane4,
+                                          uint32_t& amax) {
+  const uint32_t ad = ((h >> 1) & 0x7E00u) | lane4;  // bucket * 512 + lane * 4
+  uint32_t* p = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(bk) + ad);
+  const uint32_t m = h & 0x3FFu;
+  atomicAdd(p, m | 0x100000u);
+  atomicAdd(p + kLanes, m * m);
+  amax = max(amax, h & 0x7FFFu);
 }
 
+// One workgroup: 64 channels (a lane each) x kStatsRows tokens of one layer; the
+// four waves take every fourth row, sixteen loads in flight per wave.
 __global__ __launch_bounds__(256) void k_stats(const uint16_t* __restrict__ x, int kv, int L,
                                                int T, int C, StatsBuf sb) {
-  __shared__ Acc part[128][2];
-  const int tid = threadIdx.x;
-  const int cp = tid & 127, ph = tid >> 7;
-  const int c0 = blockIdx.x * 256 + 2 * cp;
+  __shared__ uint32_t bk[kStatsWords];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  for (int j = tid; j < kStatsWords; j += 256) bk[j] = 0;
+  __syncthreads();
+  const int c = blockIdx.x * kLanes + lane;
   const int l = blockIdx.z;
   const int tbeg = blockIdx.y * kStatsRows;
-  const int tend = min(tbeg + kStatsRows, T);
-  const bool has0 = c0 < C, has1 = c0 + 1 < C;
-  const bool paired = has1 && ((C & 1) == 0);
-  Acc a0 = {0, 0, 0, 0, 0, 0}, a1 = {0, 0, 0, 0, 0, 0};
-  const uint16_t* base = x + (size_t)l * T * C + c0;
-  int t = tbeg + ph;
-  if (paired) {
-    // eight rows' loads in flight before they are accumulated
-    constexpr int kU = 8;
-    for (; t + 2 * (kU - 1) < tend; t += 2 * kU) {
-      uint32_t w[kU];
+  const int n = min(kStatsRows, T - tbeg);
+  const uint32_t lane4 = 4u * (uint32_t)lane;
+  uint32_t amax = 0;
+  if (c < C) {
+    const uint32_t row_bytes = 2u * (uint32_t)C;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(x + ((size_t)l * T + tbeg) * C + (size_t)blockIdx.x * kLanes), 0,
+        (int)((uint32_t)n * row_bytes), kBufRsrcWord3);
+    const uint32_t lane_off = 2u * (uint32_t)lane;
+    int t = wave;
+    constexpr int kU = 16;
+    for (; t + 4 * (kU - 1) < n; t += 4 * kU) {
+      uint32_t h[kU];
 #pragma unroll
-      for (int j = 0; j < kU; j++) w[j] = *reinterpret_cast<const uint32_t*>(base + (size_t)(t + 2 * j) * C);
+      for (int j = 0; j < kU; j++)
+        h[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, lane_off, (uint32_t)(t + 4 * j) * row_bytes, 0);
 #pragma unroll
-      for (int j = 0; j < kU; j++) {
-        accumulate(a0, w[j] & 0xFFFFu);
-        accumulate(a1, w[j] >> 16);
-      }
+      for (int j = 0; j < kU; j++) stats_add(bk, h[j], lane4, amax);
     }
-  }
-  for (; t < tend; t += 2) {
-    const uint16_t* p = base + (size_t)t * C;
-    if (paired) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
-      accumulate(a0, w & 0xFFFFu);
-      accumulate(a1, w >> 16);
-    } else {
-      if (has0) accumulate(a0, p[0]);
-      if (has1) accumulate(a1, p[1]);
-    }
-  }
-  if (ph) {
-    part[cp][0] = a0;
-    part[cp][1] = a1;
+    for (; t < n; t += 4)
+      stats_add(bk, __builtin_amdgcn_raw_buffer_load_b16(rs, lane_off, (uint32_t)t * row_bytes, 0),
+                lane4, amax);
   }
   __syncthreads();
-  if (ph) return;
-  const Acc o0 = part[cp][0], o1 = part[cp][1];
-  a0.s1 += o0.s1; a0.sa += o0.sa; a0.sb += o0.sb; a0.sc += o0.sc;
-  a0.amax = max(a0.amax, o0.amax); a0.nf |= o0.nf;
-  a1.s1 += o1.s1; a1.sa += o1.sa; a1.sb += o1.sb; a1.sc += o1.sc;
-  a1.amax = max(a1.amax, o1.amax); a1.nf |= o1.nf;
-  const size_t i0 = ((size_t)kv * L + l) * C + c0;
-  if (has0) {
-    atomicAdd((unsigned long long*)&sb.s1[i0], (unsigned long long)a0.s1);
-    atomicAdd((unsigned long long*)&sb.sa[i0], (unsigned long long)a0.sa);
-    atomicAdd((unsigned long long*)&sb.sb[i0], (unsigned long long)a0.sb);
-    atomicAdd((unsigned long long*)&sb.sc[i0], (unsigned long long)a0.sc);
-    atomicMax(&sb.amax[i0], a0.amax);
+  // fold: wave w takes buckets 16w .. 16w + 15 of its lane's channel
+  int64_t s1 = 0;
+  unsigned __int128 s2 = 0;
+  for (int b = 16 * wave; b < 16 * wave + 16; b++) {
+    const uint32_t e = (uint32_t)b & 31u;
+    if (e == 31u) continue;  // infinities and NaNs: flagged through amax
+    const uint32_t pk = bk[(b * 2) * kLanes + lane], sq = bk[(b * 2 + 1) * kLanes + lane];
+    const uint64_t cnt = pk >> 20, sm = pk & 0xFFFFFu;
+    const uint64_t SM = e ? sm + (cnt << 10) : sm;
+    const uint64_t SQ = e ? (uint64_t)sq + (sm << 11) + (cnt << 20) : (uint64_t)sq;
+    const uint32_t E = e ? e - 1u : 0u;
+    const int64_t v = (int64_t)(SM << E);
+    s1 += (b & 32) ? -v : v;
+    s2 += (unsigned __int128)SQ << (2u * E);
   }
-  if (has1) {
-    atomicAdd((unsigned long long*)&sb.s1[i0 + 1], (unsigned long long)a1.s1);
-    atomicAdd((unsigned long long*)&sb.sa[i0 + 1], (unsigned long long)a1.sa);
-    atomicAdd((unsigned long long*)&sb.sb[i0 + 1], (unsigned long long)a1.sb);
-    atomicAdd((unsigned long long*)&sb.sc[i0 + 1], (unsigned long long)a1.sc);
-    atomicMax(&sb.amax[i0 + 1], a1.amax);
+  __syncthreads();
+  // the four waves' partials of each channel, summed by wave 0
+  uint64_t* part = reinterpret_cast<uint64_t*>(bk);  // [wave][s1, sa, sc][lane]
+  uint32_t* pmax = bk + 4 * 3 * kLanes * 2;          // [wave][lane]
+  part[(wave * 3 + 0) * kLanes + lane] = (uint64_t)s1;
+  part[(wave * 3 + 1) * kLanes + lane] = (uint64_t)(s2 >> 40);
+  part[(wave * 3 + 2) * kLanes + lane] = (uint64_t)s2 & ((1ull << 40) - 1);
+  pmax[wave * kLanes + lane] = amax;
+  __syncthreads();
+  if (wave != 0 || c >= C) return;
+  uint64_t t1 = 0, ta = 0, tc = 0;
+  uint32_t mx = 0;
+  for (int w = 0; w < 4; w++) {
+    t1 += part[(w * 3 + 0) * kLanes + lane];
+    ta += part[(w * 3 + 1) * kLanes + lane];
+    tc += part[(w * 3 + 2) * kLanes + lane];
+    mx = max(mx, pmax[w * kLanes + lane]);
   }
-  if (a0.nf | a1.nf) atomicOr(&sb.flags[0], 1u);
+  const size_t i0 = ((size_t)kv * L + l) * C + c;
+  atomicAdd((unsigned long long*)&sb.s1[i0], (unsigned long long)t1);
+  atomicAdd((unsigned long long*)&sb.sa[i0], (unsigned long long)ta);
+  atomicAdd((unsigned long long*)&sb.sc[i0], (unsigned long long)tc);
+  atomicMax(&sb.amax[i0], mx);
+  if (mx >= 0x7C00u) atomicOr(&sb.flags[0], 1u);
 }
 
 // Correctly rounded (to nearest, ties to even) conversion of a 128-bit integer:
@@ -142,9 +139,7 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs a) {
   if (i >= n) return;
   const int l = (int)((i / a.C) % a.L);
   const int64_t S1 = (int64_t)a.sb.s1[i];
-  const unsigned __int128 S2 = ((unsigned __int128)a.sb.sa[i] << 40) +
-                               ((unsigned __int128)a.sb.sb[i] << 21) +
-                               (unsigned __int128)a.sb.sc[i];
+  const unsigned __int128 S2 = ((unsigned __int128)a.sb.sa[i] << 40) + (unsigned __int128)a.sb.sc[i];
   const unsigned __int128 num =
       (unsigned __int128)a.T * S2 - (unsigned __int128)((__int128)S1 * S1);
   const double sigma = num ? sqrt(u128_to_f64(num)) / ((double)a.T * 16777216.0) : 1.0;
@@ -177,18 +172,16 @@ struct HistArgs {
 
 // Delta-symbol histogram of one (kv, layer, 64-channel block, chunk): each lane
 // owns a channel, the four waves take interleaved groups; counts go to LDS with
-// atomics, two 16-bit counters per word (symbols s and s + 32; a chunk has at
-// most 65,535 deltas per channel), laid out [slot][s mod 32][lane] so that the
-// 64 lanes hit distinct banks; then to global memory with one atomic per
-// non-zero bin.
-constexpr int kHistWords = 3 * (kNSym / 2) * kLanes;
-
-template <int GS>
+// atomics, laid out [slot][symbol][lane] so that the 64 lanes hit distinct
+// banks and a count's address is one shift-add of the delta level; then to
+// global memory with one atomic per non-zero bin.  LDS: nq * 16 KB, dynamic.
+template <int GS, int NQ>
 __global__ __launch_bounds__(256) void k_histogram(HistArgs a) {
-  __shared__ uint32_t hist[kHistWords];
+  extern __shared__ uint32_t hist[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // token rows are scalar offsets
-  for (int j = tid; j < a.nq * (kNSym / 2) * kLanes; j += 256) hist[j] = 0;
+  const int words = NQ * kNSym * kLanes;
+  for (int j = tid; j < words; j += 256) hist[j] = 0;
   __syncthreads();
   const int c = blockIdx.x * kLanes + lane;
   const int chunk = blockIdx.y, l = blockIdx.z;
@@ -199,8 +192,8 @@ __global__ __launch_bounds__(256) void k_histogram(HistArgs a) {
     const size_t pi = ((size_t)a.kv * a.L + l) * a.C + c;
     const float scale_a = a.scale_a[pi], inv_a = a.inv_a[pi];
     const float is0 = a.inv_step[0][pi];
-    const float is1 = a.nq > 1 ? a.inv_step[1][pi] : 1.0f;
-    const float is2 = a.nq > 2 ? a.inv_step[2][pi] : 1.0f;
+    const float is1 = NQ > 1 ? a.inv_step[1][pi] : 1.0f;
+    const float is2 = NQ > 2 ? a.inv_step[2][pi] : 1.0f;
     // the chunk's rows of this layer: channel as the vector offset, token row as
     // a scalar offset; rows past the chunk read as zero
     const uint32_t row_bytes = 2u * (uint32_t)a.C;
@@ -211,16 +204,20 @@ __global__ __launch_bounds__(256) void k_histogram(HistArgs a) {
     auto ld = [&](int t) -> uint32_t {
       return __builtin_amdgcn_raw_buffer_load_b16(xin, lane_off, (uint32_t)t * row_bytes, 0);
     };
-    auto count = [&](int slot, uint32_t sym) {
-      atomicAdd(&hist[(slot * (kNSym / 2) + (sym & 31u)) * kLanes + lane], 1u << ((sym >> 5) << 4));
+    // byte address of level 0 of each slot's column for this lane
+    const uint32_t at0 = (uint32_t)(32 * kLanes + lane) * 4u;
+    const uint32_t at1 = at0 + kNSym * kLanes * 4u, at2 = at1 + kNSym * kLanes * 4u;
+    auto count = [&](uint32_t at, int level) {
+      atomicAdd(reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(hist) + at +
+                                            ((uint32_t)level << 8)), 1u);
     };
     auto group = [&](int n, auto half_of) {
       const float ahat = anchor_value(quant_anchor(half_bits_to_float(half_of(0)), inv_a), scale_a);
       for (int j = 1; j < n; j++) {
         const float xv = half_bits_to_float(half_of(j));
-        count(0, quant_delta(xv, ahat, is0));
-        if (a.nq > 1) count(1, quant_delta(xv, ahat, is1));
-        if (a.nq > 2) count(2, quant_delta(xv, ahat, is2));
+        count(at0, quant_delta_level(xv, ahat, is0));
+        if constexpr (NQ > 1) count(at1, quant_delta_level(xv, ahat, is1));
+        if constexpr (NQ > 2) count(at2, quant_delta_level(xv, ahat, is2));
       }
     };
     int g = wave;
@@ -252,14 +249,13 @@ __global__ __launch_bounds__(256) void k_histogram(HistArgs a) {
     }
   }
   __syncthreads();
-  for (int j = tid; j < a.nq * (kNSym / 2) * kLanes; j += 256) {
+  for (int j = tid; j < words; j += 256) {
     const uint32_t v = hist[j];
     if (!v) continue;
-    const int s = j / ((kNSym / 2) * kLanes), sym = (j / kLanes) % (kNSym / 2), ln = j % kLanes;
+    const int s = j / (kNSym * kLanes), sym = (j / kLanes) % kNSym, ln = j % kLanes;
     const int cc = blockIdx.x * kLanes + ln;
-    const size_t ti = (((size_t)a.kv * a.nq + s) * a.L + l) * a.C + cc;
-    if (v & 0xFFFFu) atomicAdd(&a.counts[ti * kNSym + sym], v & 0xFFFFu);
-    if (v >> 16) atomicAdd(&a.counts[ti * kNSym + sym + kNSym / 2], v >> 16);
+    const size_t ti = (((size_t)a.kv * NQ + s) * a.L + l) * a.C + cc;
+    atomicAdd(&a.counts[ti * kNSym + sym], v);
   }
 }
 
@@ -414,7 +410,7 @@ inline unsigned blocks_for(size_t n, unsigned per) { return (unsigned)((n + per 
 
 hipError_t launch_stats(const uint16_t* x, int kv, int L, int T, int C, const StatsBuf& sb,
                         hipStream_t st) {
-  dim3 grid((unsigned)((C + 255) / 256), (unsigned)((T + kStatsRows - 1) / kStatsRows),
+  dim3 grid((unsigned)((C + kLanes - 1) / kLanes), (unsigned)((T + kStatsRows - 1) / kStatsRows),
             (unsigned)L);
   k_stats<<<grid, 256, 0, st>>>(x, kv, L, T, C, sb);
   return hipGetLastError();
@@ -459,10 +455,18 @@ hipError_t launch_histogram(const uint16_t* x, int kv, const DevTables& t, uint3
   a.counts = counts;
   const int nchunks = (t.T + t.CH - 1) / t.CH;
   dim3 grid((unsigned)t.nblk, (unsigned)nchunks, (unsigned)t.L);
-  if (t.G == 10)
-    k_histogram<10><<<grid, 256, 0, st>>>(a);
-  else
-    k_histogram<0><<<grid, 256, 0, st>>>(a);
+  const size_t lds = (size_t)a.nq * kNSym * kLanes * 4;
+  const bool g10 = t.G == 10;
+  if (a.nq == 1) {
+    if (g10) k_histogram<10, 1><<<grid, 256, lds, st>>>(a);
+    else k_histogram<0, 1><<<grid, 256, lds, st>>>(a);
+  } else if (a.nq == 2) {
+    if (g10) k_histogram<10, 2><<<grid, 256, lds, st>>>(a);
+    else k_histogram<0, 2><<<grid, 256, lds, st>>>(a);
+  } else {
+    if (g10) k_histogram<10, 3><<<grid, 256, lds, st>>>(a);
+    else k_histogram<0, 3><<<grid, 256, lds, st>>>(a);
+  }
   return hipGetLastError();
 }
 
