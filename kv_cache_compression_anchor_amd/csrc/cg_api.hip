@@ -27,8 +27,9 @@ struct cg_tables {
   uint32_t* enc_status = nullptr;   // per blob of a batch: W, too large, non-finite, pad
   uint32_t* enc_host = nullptr;     // pinned mirror
   int enc_status_cap = 0;
-  uint32_t* status = nullptr;    // device words: id scratch, decode status
-  uint32_t* host_status = nullptr;  // pinned mirror
+  uint8_t* dev_block = nullptr;  // one allocation: serialized tables, images, status words
+  uint32_t* status = nullptr;    // device words: decode status
+  uint32_t* host_status = nullptr;  // pinned mirror, allocated on first use
 };
 
 namespace {
@@ -136,41 +137,95 @@ void write_header(uint8_t* h, const cg_params& p) {
 void free_tables(cg_tables* t) {
   if (!t) return;
   DeviceGuard g(t->dev);
-  if (t->t.ser) (void)hipFree(t->t.ser);
-  for (int q = 0; q < 3; q++)
-    if (t->t.img[q]) (void)hipFree(t->t.img[q]);
+  if (t->dev_block) (void)hipFree(t->dev_block);
   if (t->scratch) (void)hipFree(t->scratch);
   if (t->lens) (void)hipFree(t->lens);
   if (t->row_words) (void)hipFree(t->row_words);
   if (t->enc_status) (void)hipFree(t->enc_status);
   if (t->enc_host) (void)hipHostFree(t->enc_host);
-  if (t->status) (void)hipFree(t->status);
   if (t->host_status) (void)hipHostFree(t->host_status);
   delete t;
 }
 
 // Allocates the device copies of a table set whose params are already checked.
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// The tables' device memory in one allocation: serialized tables, the LDS
+// images of each built quality, 64 status words.
 int alloc_tables(cg_tables* h) {
   DevTables& t = h->t;
-  HIP_TRY(hipMalloc(&t.ser, t.lay.total), "hipMalloc(tables)");
+  size_t off = align256(t.lay.total);
+  size_t img_off[3] = {0, 0, 0};
   for (int q = 0; q < 3; q++)
-    if ((t.mask >> q) & 1u) HIP_TRY(hipMalloc(&t.img[q], img_bytes(t)), "hipMalloc(images)");
-  HIP_TRY(hipMalloc(&h->status, 64), "hipMalloc(status)");
-  HIP_TRY(hipHostMalloc(&h->host_status, 64, hipHostMallocDefault), "hipHostMalloc(status)");
+    if ((t.mask >> q) & 1u) {
+      img_off[q] = off;
+      off += align256(img_bytes(t));
+    }
+  const size_t status_off = off;
+  off += 256;
+  HIP_TRY(hipMalloc(&h->dev_block, off), "hipMalloc(tables)");
+  t.ser = h->dev_block;
+  for (int q = 0; q < 3; q++)
+    if ((t.mask >> q) & 1u) t.img[q] = reinterpret_cast<uint16_t*>(h->dev_block + img_off[q]);
+  h->status = reinterpret_cast<uint32_t*>(h->dev_block + status_off);
   return CG_OK;
+}
+
+int ensure_host_status(cg_tables* h) {
+  if (!h->host_status)
+    HIP_TRY(hipHostMalloc(&h->host_status, 64, hipHostMallocDefault), "hipHostMalloc(status)");
+  return CG_OK;
+}
+
+// Device workspace of cg_build_tables and of the tables id (statistics, symbol
+// counts, digests) and a pinned word block for reading back status and id:
+// one per device, grown when a build needs more and kept until the process
+// ends.  A build holds the mutex until it has synchronised its stream, so
+// builds on one device take turns.
+struct BuildWs {
+  std::mutex mu;
+  uint8_t* dev = nullptr;
+  size_t bytes = 0;
+  uint32_t* host = nullptr;
+};
+constexpr int kMaxDevices = 64;
+
+BuildWs* build_ws(int dev) {
+  static BuildWs ws[kMaxDevices];
+  return dev >= 0 && dev < kMaxDevices ? &ws[dev] : nullptr;
+}
+
+// with ws->mu held
+int reserve_ws(BuildWs* ws, size_t bytes) {
+  if (!ws->host) HIP_TRY(hipHostMalloc(&ws->host, 64, hipHostMallocDefault), "hipHostMalloc(build)");
+  if (ws->bytes >= bytes) return CG_OK;
+  if (ws->dev) (void)hipFree(ws->dev);
+  ws->dev = nullptr;
+  ws->bytes = 0;
+  if (hipMalloc(&ws->dev, bytes) != hipSuccess)
+    return fail(CG_E_NOMEM, "device allocation for the table build workspace");
+  ws->bytes = bytes;
+  return CG_OK;
+}
+
+size_t id_digest_bytes(const DevTables& t) {
+  return 8 * (id_leaves(t.lay.total) + id_mids(t.lay.total));
 }
 
 // Tables id of the device copy, computed on the GPU; syncs the stream.
 int compute_id(cg_tables* h, hipStream_t st) {
-  const size_t nd = id_leaves(h->t.lay.total) + id_mids(h->t.lay.total);
-  uint64_t* dig = nullptr;
-  HIP_TRY(hipMalloc(&dig, 8 * (nd + 1)), "hipMalloc(id)");
+  BuildWs* ws = build_ws(h->dev);
+  if (!ws) return fail(CG_E_INVAL, "device index beyond the supported range");
+  std::lock_guard<std::mutex> lock(ws->mu);
+  int rc = reserve_ws(ws, id_digest_bytes(h->t) + 8);
+  if (rc) return rc;
+  uint64_t* dig = reinterpret_cast<uint64_t*>(ws->dev);
+  const size_t nd = id_digest_bytes(h->t) / 8;
   hipError_t e = launch_tables_id(h->t, dig, dig + nd, st);
-  if (e == hipSuccess) e = hipMemcpyAsync(h->host_status, dig + nd, 8, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(ws->host, dig + nd, 8, hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
-  (void)hipFree(dig);
   if (e != hipSuccess) return hip_fail(e, "tables id");
-  memcpy(&h->id, h->host_status, 8);
+  memcpy(&h->id, ws->host, 8);
   return CG_OK;
 }
 
@@ -324,25 +379,35 @@ int cg_build_tables(const cg_params* params, const void* k_dev, const void* v_de
   }
   const size_t n = t.lay.n;
   const size_t counts_words = (size_t)n * t.lay.nq * kNSym;
+  // workspace: [s1 | sa | sc] u64, amax u32, 4 flag words (the last two hold
+  // the tables id), counts; then the id digests
   const size_t tmp_bytes = 3 * 8 * n + 4 * n + 16 + 4 * counts_words;
-  uint8_t* tmp = nullptr;
-  hipError_t e = hipMalloc(&tmp, tmp_bytes);
-  if (e != hipSuccess) {
+  const size_t dig_off = align256(tmp_bytes);
+  BuildWs* ws = build_ws(h->dev);
+  if (!ws) {
     free_tables(h);
-    return fail(CG_E_NOMEM, "device allocation for table statistics");
+    return fail(CG_E_INVAL, "device index beyond the supported range");
   }
+  std::lock_guard<std::mutex> lock(ws->mu);
+  if ((rc = reserve_ws(ws, dig_off + id_digest_bytes(t)))) {
+    free_tables(h);
+    return rc;
+  }
+  uint8_t* tmp = ws->dev;
   StatsBuf sb;
   sb.s1 = reinterpret_cast<uint64_t*>(tmp);
   sb.sa = sb.s1 + n;
   sb.sc = sb.sa + n;
   sb.amax = reinterpret_cast<uint32_t*>(sb.sc + n);
   sb.flags = sb.amax + n;
+  uint64_t* id_dev = reinterpret_cast<uint64_t*>(sb.flags + 2);
   uint32_t* counts = sb.flags + 4;
+  uint64_t* dig = reinterpret_cast<uint64_t*>(tmp + dig_off);
   uint8_t hdr[kTabHdr];
   write_header(hdr, *params);
   const uint16_t* k = static_cast<const uint16_t*>(k_dev);
   const uint16_t* v = static_cast<const uint16_t*>(v_dev);
-  e = hipMemsetAsync(tmp, 0, tmp_bytes, st);
+  hipError_t e = hipMemsetAsync(tmp, 0, tmp_bytes, st);
   if (e == hipSuccess) e = hipMemcpyAsync(t.ser, hdr, kTabHdr, hipMemcpyHostToDevice, st);
   if (e == hipSuccess) e = launch_stats(k, 0, t.L, t.T, t.C, sb, st);
   if (e == hipSuccess) e = launch_stats(v, 1, t.L, t.T, t.C, sb, st);
@@ -351,25 +416,23 @@ int cg_build_tables(const cg_params* params, const void* k_dev, const void* v_de
   if (e == hipSuccess) e = launch_histogram(v, 1, t, counts, st);
   if (e == hipSuccess) e = launch_normalize(t, counts, st);
   if (e == hipSuccess) e = launch_images(t, st);
-  if (e == hipSuccess) e = hipMemcpyAsync(h->host_status, sb.flags, 8, hipMemcpyDeviceToHost, st);
+  // the id of whatever was built; discarded below when the build failed
+  if (e == hipSuccess) e = launch_tables_id(t, dig, id_dev, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(ws->host, sb.flags, 16, hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
-  (void)hipFree(tmp);
   if (e != hipSuccess) {
     free_tables(h);
     return hip_fail(e, "build tables");
   }
-  if (h->host_status[0]) {
+  if (ws->host[0]) {
     free_tables(h);
     return fail(CG_E_INVAL, "K/V hold a non-finite value");
   }
-  if (h->host_status[1]) {
+  if (ws->host[1]) {
     free_tables(h);
     return fail(CG_E_INVAL, "a delta step is not a normal binary32 value");
   }
-  if ((rc = compute_id(h, st))) {
-    free_tables(h);
-    return rc;
-  }
+  memcpy(&h->id, ws->host + 2, 8);
   *out = h;
   return CG_OK;
 }
@@ -664,6 +727,8 @@ int cg_decode(const cg_tables* ch, int32_t n, const void* const* blobs_dev, cons
   }
   if (n == 0) return CG_OK;
   std::lock_guard<std::mutex> lk(h->mu);
+  int rs = ensure_host_status(const_cast<cg_tables*>(h));  // a cache the lock guards
+  if (rs) return rs;
   uint32_t* status = h->status + 8;
   HIP_TRY(hipMemsetAsync(status, 0, 4, st), "clear status");
   int rc = enqueue_decode(h, n, blobs_dev, infos.data(), k_out_dev, v_out_dev, status, st);
