@@ -576,7 +576,8 @@ int cg_encode_batch(const cg_tables* ch, const void* k_dev, const void* v_dev, i
   DeviceGuard dg(h->dev);
   if (!dg.ok) return fail(CG_E_HIP, "cannot select the tables' device");
   std::lock_guard<std::mutex> lk(h->mu);
-  const size_t swb = std::max<size_t>(stream_words_bound(t.CH - (t.CH + t.G - 1) / t.G), 1);
+  // a stream's words plus the placeholder word in front of them
+  const size_t swb = std::max<size_t>(stream_words_bound(t.CH - (t.CH + t.G - 1) / t.G), 1) + 1;
   const size_t slot_words = t.lay.n * swb;
   const int slots = (int)std::max<size_t>(
       1, std::min<size_t>({(size_t)kEncMaxBlobs, (size_t)n, kEncScratchBudget / (4 * slot_words)}));

@@ -15,89 +15,123 @@ namespace {
 // carry out of the window simply runs into those bytes.  A word leaves `L` once
 // four bytes sit above the window; the last one taken (`W`) and a run of
 // 0xFFFFFFFF words after it (`P`) stay open until no carry can reach them.
-// The common steps are branch-free; the rare ones (the first word, an
-// all-ones word, a carry into an all-ones run) take branches of their own.
+// `W` always has a slot: before the first word is taken it is a placeholder
+// word in front of the stream, which the first emission fills and nothing reads
+// (no carry can reach past the first word).
 struct RcEnc {
-  uint64_t L;       // window (bits 0..31) and the bytes above it (bits 32..32+kh-1)
-  uint32_t kh;      // 8 * bytes above the window: 0..24
+  uint64_t L;      // window (bits 0..31) and the bytes above it (bits 32..32+kh-1)
+  uint32_t kh;     // 8 * bytes above the window: 0..24
+  uint32_t hmask;  // (1 << kh) - 1, the held bytes' bits in the high word of L
   uint32_t range;
-  uint32_t W;       // last word taken out of L, not final yet
-  uint32_t P;       // 0xFFFFFFFF words after W, not final yet
-  uint32_t have;    // W holds a word
-  uint32_t nw;      // words written
+  uint32_t W;      // last word taken out of L, not final yet
+  uint32_t P;      // 0xFFFFFFFF words after W, not final yet
 };
 
-__device__ __forceinline__ void emit_word(RcEnc& e, uint32_t w, uint32_t* out) { out[e.nw++] = w; }
+// A lane's output words, through a buffer resource over the wave's 64 streams:
+// `woff` is the byte offset of W's slot.
+struct Sink {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t woff;
+};
+
+__device__ __forceinline__ void emit_word(Sink& o, uint32_t w) {
+  __builtin_amdgcn_raw_buffer_store_b32(w, o.rs, o.woff, 0, 0);
+  o.woff += 4u;
+}
+
+// --- general steps: every case, used for the rare symbols and the flush ----
 
 // a carry reached an all-ones run: it wraps to zeros, W + 1 and all but the
 // last zero word are final, the last zero word stays open
-__device__ __forceinline__ void carry_into_run(RcEnc& e, uint32_t* out) {
-  emit_word(e, e.W + 1u, out);
-  for (uint32_t j = 1; j < e.P; j++) emit_word(e, 0u, out);
+__device__ __forceinline__ void carry_into_run(RcEnc& e, Sink& o) {
+  emit_word(o, e.W + 1u);
+  for (uint32_t j = 1; j < e.P; j++) emit_word(o, 0u);
   e.W = 0;
   e.P = 0;
 }
 
-// a word taken out of L in the rare cases: the first word, an all-ones word
-// (it may still wrap), or a word closing an all-ones run
-__device__ __forceinline__ void take_word_rare(RcEnc& e, uint32_t wn, uint32_t* out) {
-  if (!e.have) {
-    e.W = wn;
-    e.have = 1;
-  } else if (wn == 0xFFFFFFFFu) {
-    e.P++;
-  } else {
-    emit_word(e, e.W, out);
-    for (; e.P; e.P--) emit_word(e, 0xFFFFFFFFu, out);
-    e.W = wn;
-  }
-}
-
-__device__ __forceinline__ void add_low(RcEnc& e, uint64_t x, uint32_t* out) {
-  e.L += x;
-  // at most one carry out of the held bytes: it is bit 32 + kh
+// the carry out of the held bytes after an addition to L: into W, or through
+// an all-ones run
+__device__ __forceinline__ void settle_carry(RcEnc& e, Sink& o) {
   uint32_t hi = (uint32_t)(e.L >> 32);
-  const uint32_t c = hi >> e.kh;
-  hi = __builtin_amdgcn_ubfe(hi, 0, e.kh);
+  const bool c = hi > e.hmask;
+  hi &= e.hmask;
   e.L = ((uint64_t)hi << 32) | (uint32_t)e.L;
   if (c && e.P) {
-    carry_into_run(e, out);
+    carry_into_run(e, o);
   } else {
-    e.W += c;
+    e.W += c ? 1u : 0u;
   }
 }
 
-// shift nb8 / 8 (0..2) bytes out of the window; a word leaves when four are held
-__device__ __forceinline__ void shift_bytes(RcEnc& e, uint32_t nb8, uint32_t* out) {
+// shift nb8 / 8 (0..2) bytes out of the window; a word leaves when four are
+// held after the shift: it is the four top bytes of L before it
+__device__ __forceinline__ void shift_bytes(RcEnc& e, uint32_t nb8, Sink& o) {
+  const uint32_t lo = (uint32_t)e.L, hi = (uint32_t)(e.L >> 32);
   const uint32_t kh2 = e.kh + nb8;
   const bool ext = kh2 >= 32u;
-  const uint64_t L1 = e.L << (ext ? 32u - e.kh : nb8);
-  const uint32_t wn = (uint32_t)(L1 >> 32);
-  e.L = ext ? (uint64_t)(uint32_t)L1 << (kh2 - 32u) : L1;
-  e.kh = ext ? kh2 - 32u : kh2;
+  const uint32_t wn = __builtin_amdgcn_alignbit(hi, lo, e.kh);
+  const uint32_t lo_k = ext ? __builtin_amdgcn_ubfe(lo, 0u, e.kh) : lo;
+  const uint32_t hi_k = ext ? 0u : hi;
+  e.L = (((uint64_t)hi_k << 32) | lo_k) << nb8;
+  e.kh = kh2 & 31u;
+  e.hmask = (1u << e.kh) - 1u;
   if (ext) {
-    if (e.have && e.P == 0 && wn != 0xFFFFFFFFu) {
-      emit_word(e, e.W, out);
-      e.W = wn;
+    if (wn == 0xFFFFFFFFu) {
+      e.P++;  // may still wrap
     } else {
-      take_word_rare(e, wn, out);
+      emit_word(o, e.W);
+      for (; e.P; e.P--) emit_word(o, 0xFFFFFFFFu);
+      e.W = wn;
     }
   }
 }
 
-__device__ __forceinline__ void rc_put(RcEnc& e, uint32_t c0, uint32_t freq, uint32_t* out) {
+// --- one symbol -----------------------------------------------------------
+// The common case (no all-ones run open, and no all-ones word taken) runs
+// branch-free for the whole wave; a lane in a rare case redoes the symbol from
+// its previous state with the general steps, in a branch the wave takes only
+// when some lane needs it.
+__device__ __forceinline__ void rc_put(RcEnc& e, uint32_t c0, uint32_t freq, Sink& o) {
+  const RcEnc e0 = e;
   const uint32_t r = e.range >> kProbBits;
-  add_low(e, (uint64_t)mul24(r, c0), out);
+  const uint64_t L1 = e.L + (uint64_t)r * c0;  // one 32 x 32 -> 64 multiply-add
+  const uint32_t lo = (uint32_t)L1, hx = (uint32_t)(L1 >> 32);
+  const bool c = hx > e.hmask;
+  const uint32_t hi = hx & e.hmask;
   const uint32_t rn = mul24(r, freq);
   const uint32_t nb8 = (uint32_t)__builtin_clz(rn) & 24u;  // renormalise while range < 2^24
+  const uint32_t kh2 = e.kh + nb8;
+  const bool ext = kh2 >= 32u;
+  const uint32_t wn = __builtin_amdgcn_alignbit(hi, lo, e.kh);
+  const bool rare = e.P != 0u ? (c || ext) : (ext && wn == 0xFFFFFFFFu);
+  const uint32_t W1 = e.W + (c ? 1u : 0u);
+  const bool emit = ext && !rare;
+  if (emit) __builtin_amdgcn_raw_buffer_store_b32(W1, o.rs, o.woff, 0, 0);
+  o.woff += emit ? 4u : 0u;
+  e.W = emit ? wn : W1;
+  const uint32_t lo_k = ext ? __builtin_amdgcn_ubfe(lo, 0u, e.kh) : lo;
+  const uint32_t hi_k = ext ? 0u : hi;
+  e.L = (((uint64_t)hi_k << 32) | lo_k) << nb8;
+  e.kh = kh2 & 31u;
+  e.hmask = (1u << e.kh) - 1u;
   e.range = rn << nb8;
-  shift_bytes(e, nb8, out);
+  if (__builtin_amdgcn_ballot_w64(rare)) {
+    if (rare) {
+      RcEnc s = e0;
+      s.L = L1;
+      settle_carry(s, o);
+      s.range = rn << nb8;
+      shift_bytes(s, nb8, o);
+      e = s;
+    }
+  }
 }
 
 // Flush: the fewest bytes (one or two) that name an aligned block inside
 // [low, low + range), so the stream decodes whatever bytes follow it; then the
 // open words and the bytes still held, the last word padded with zero bytes.
-__device__ __forceinline__ void rc_finish(RcEnc& e, uint32_t* out) {
+__device__ __forceinline__ void rc_finish(RcEnc& e, Sink& o) {
   const uint64_t win = e.L & 0xFFFFFFFFull;
   uint32_t nb8 = 8;
   uint64_t V = (win + 0xFFFFFFull) & ~0xFFFFFFull;
@@ -105,15 +139,13 @@ __device__ __forceinline__ void rc_finish(RcEnc& e, uint32_t* out) {
     nb8 = 16;
     V = (win + 0xFFFFull) & ~0xFFFFull;
   }
-  e.L -= win;
-  add_low(e, V, out);
-  shift_bytes(e, nb8, out);
-  if (e.have) {
-    emit_word(e, e.W, out);
-    for (; e.P; e.P--) emit_word(e, 0xFFFFFFFFu, out);
-  }
+  e.L = e.L - win + V;
+  settle_carry(e, o);
+  shift_bytes(e, nb8, o);
+  emit_word(o, e.W);  // the placeholder when no word was taken
+  for (; e.P; e.P--) emit_word(o, 0xFFFFFFFFu);
   const uint32_t k = e.kh >> 3;
-  if (k) emit_word(e, (uint32_t)(e.L >> 32) << (8u * (4u - k)), out);
+  if (k) emit_word(o, (uint32_t)(e.L >> 32) << (8u * (4u - k)));
 }
 
 // A workgroup is (group of up to 4 blobs of one quality, kv, layer, 64-channel
@@ -164,10 +196,17 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
       (int)((uint32_t)B.tc * row_bytes), kBufRsrcWord3);
   const uint32_t lane_off = 2u * (uint32_t)c;
   const uint8_t* tb = reinterpret_cast<const uint8_t*>(tab) + 2 * lane_slot(lane);
-  uint32_t* out = B.scratch + pi * a.swb;
+  // the wave's 64 streams of swb words in scratch, each led by its placeholder
+  const uint32_t swb4 = 4u * (uint32_t)a.swb;
+  Sink o;
+  const size_t wave_pi = ((size_t)kv * a.L + l) * a.C + (size_t)cb * kLanes;  // lane 0's stream
+  o.rs = __builtin_amdgcn_make_buffer_rsrc(B.scratch + wave_pi * a.swb, 0, (int)(kLanes * swb4),
+                                           kBufRsrcWord3);
+  o.woff = (uint32_t)lane * swb4;
+  const uint32_t woff0 = o.woff + 4u;  // the stream's first word
   int8_t* anchors = reinterpret_cast<int8_t*>(B.blob + B.lay.off_anchor) +
                     ((size_t)kv * a.L + l) * B.ng * a.C + c;
-  RcEnc e = {0, 0u, 0xFFFFFFFFu, 0, 0, 0, 0};
+  RcEnc e = {0, 0u, 0u, 0xFFFFFFFFu, 0u, 0u};
   uint32_t nonfinite = 0;
 
   // one group from its tokens' binary16 bits: the anchor, then the deltas
@@ -183,7 +222,7 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
       const uint32_t s = quant_delta(half_bits_to_float(hx), ahat, inv_step);
       const uint32_t c0 = *reinterpret_cast<const uint16_t*>(tb + s * (2 * kLanes));
       const uint32_t c1 = *reinterpret_cast<const uint16_t*>(tb + (s + 1) * (2 * kLanes));
-      rc_put(e, c0, c1 - c0, out);
+      rc_put(e, c0, c1 - c0, o);
     }
   };
 
@@ -210,10 +249,11 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
     code_group(g, min(a.G, B.tc - ta),
                [&](int j) { return ld_half(xin, lane_off, (uint32_t)(ta + j) * row_bytes); });
   }
-  if (B.tc > B.ng) rc_finish(e, out);  // a stream without symbols stays empty
+  if (B.tc > B.ng) rc_finish(e, o);  // a stream without symbols stays empty
   if (nonfinite) atomicOr(&B.status[2], 1u);
-  B.lens[pi] = e.nw;
-  reinterpret_cast<uint16_t*>(B.blob + B.lay.off_len)[pi] = (uint16_t)e.nw;
+  const uint32_t nwords = o.woff > woff0 ? (o.woff - woff0) >> 2 : 0u;
+  B.lens[pi] = nwords;
+  reinterpret_cast<uint16_t*>(B.blob + B.lay.off_len)[pi] = (uint16_t)nwords;
 }
 
 // words of every (kv, layer) row of every blob
@@ -311,7 +351,7 @@ __global__ __launch_bounds__(256) void k_pack(EncodeArgs a) {
   uint32_t* pay = reinterpret_cast<uint32_t*>(B.blob + B.lay.off_pay);
   const int n = min(256, a.C - seg * 256);
   for (int j = wave; j < n; j += 4) {
-    const uint32_t* src = B.scratch + ((size_t)row * a.C + seg * 256 + j) * a.swb;
+    const uint32_t* src = B.scratch + ((size_t)row * a.C + seg * 256 + j) * a.swb + 1;
     uint32_t* dst = pay + soff[j];
     for (uint32_t k = lane; k < slen[j]; k += 64) dst[k] = src[k];
   }

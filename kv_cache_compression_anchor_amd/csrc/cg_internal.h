@@ -181,7 +181,7 @@ struct EncBlob {
   BlobLayout lay;
   const uint16_t* img;       // cum images of quality q
   const float* inv_step;     // of quality q
-  uint32_t* scratch;         // per stream: swb words
+  uint32_t* scratch;         // per stream: swb words, the first a placeholder
   uint32_t* lens;            // [2][L][C] words
   uint32_t* row_words;       // [2L]
   uint32_t* status;          // [0] payload words, [1] too large for cap, [2] non-finite input
