@@ -9,7 +9,7 @@
 #include <string>
 #include <vector>
 
-#include "cg_internal.h"
+#include "cg_build.h"
 
 using namespace cg;
 

@@ -1,0 +1,86 @@
+// Definitions of the table builder and the encoder (libcachegen): the per-lane
+// quantiser, the statistics buffer, and their kernel launchers.
+#pragma once
+
+#include "cg_internal.h"
+
+namespace cg {
+
+// ----------------------------------------------------------------------------
+// Per-lane quantiser (binary32, no contraction; identical in every kernel)
+// ----------------------------------------------------------------------------
+// The clamps are one v_med3_f32 each: for every value but NaN it equals
+// min(max(r, lo), hi).  NaN arises only from non-finite input, which every
+// caller flags and rejects; its code stays in range either way.
+__device__ __forceinline__ int quant_anchor(float x, float inv_a) {
+  float p = x * inv_a;
+  float r = __builtin_rintf(p);
+  r = __builtin_amdgcn_fmed3f(r, -127.0f, 127.0f);
+  return (int)r;
+}
+
+// the delta's level in -32 .. 31 (the symbol minus 32)
+__device__ __forceinline__ int quant_delta_level(float x, float ahat, float inv_step) {
+  float d = x - ahat;
+  float u = d * inv_step;
+  float r = __builtin_rintf(u);
+  r = __builtin_amdgcn_fmed3f(r, -32.0f, 31.0f);
+  return (int)r;
+}
+
+__device__ __forceinline__ uint32_t quant_delta(float x, float ahat, float inv_step) {
+  return (uint32_t)(quant_delta_level(x, ahat, inv_step) + 32);
+}
+
+struct StatsBuf {
+  uint64_t* s1;    // sum of X = x*2^24 (two's complement)
+  uint64_t* sa;    // sum over workgroups of (their sum of X^2) >> 40
+  uint64_t* sc;    // sum over workgroups of (their sum of X^2) mod 2^40
+  uint32_t* amax;  // max |x| as binary16 magnitude bits
+  uint32_t* flags; // [0]: non-finite input, [1]: degenerate step
+};
+
+hipError_t launch_stats(const uint16_t* x, int kv, int L, int T, int C, const StatsBuf& sb,
+                        hipStream_t st);
+hipError_t launch_finalize(const cg_params& p, const StatsBuf& sb, DevTables& t, hipStream_t st);
+hipError_t launch_histogram(const uint16_t* x, int kv, const DevTables& t, uint32_t* counts,
+                            hipStream_t st);
+hipError_t launch_normalize(const DevTables& t, const uint32_t* counts, hipStream_t st);
+hipError_t launch_images(DevTables& t, hipStream_t st);
+// digests the tables id needs: leaves, then middle digests
+inline size_t id_leaves(size_t bytes) { return (bytes + kIdLeaf - 1) / kIdLeaf; }
+inline size_t id_mids(size_t bytes) { return (id_leaves(bytes) + kIdFan - 1) / kIdFan; }
+hipError_t launch_tables_id(const DevTables& t, uint64_t* scratch_digests, uint64_t* id_out,
+                            hipStream_t st);
+
+constexpr int kEncMaxBlobs = 16;  // blobs per encode launch (kernel-argument descriptors)
+struct EncBlob {
+  uint8_t* blob;      // output
+  size_t cap;
+  int32_t t0, tc, ng, q;
+  BlobLayout lay;
+  const uint16_t* img;       // cum images of quality q
+  const float* inv_step;     // of quality q
+  uint32_t* scratch;         // per stream: swb words, the first a placeholder
+  uint32_t* lens;            // [2][L][C] words
+  uint32_t* row_words;       // [2L]
+  uint32_t* status;          // [0] payload words, [1] too large for cap, [2] non-finite input
+};
+struct EncGroup {  // blobs of one quality coded by one workgroup (one wave each)
+  int8_t blob[4];
+};
+struct EncodeArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  int L, T, C, G, nblk, nblobs;
+  int n_groups, waves;  // workgroups per (kv, layer, block) and their widest group
+  size_t swb;
+  const float* scale_a;
+  const float* inv_a;
+  uint64_t tables_id;
+  EncGroup groups[kEncMaxBlobs];
+  EncBlob b[kEncMaxBlobs];
+};
+hipError_t launch_encode(const EncodeArgs& a, hipStream_t st);
+
+}  // namespace cg

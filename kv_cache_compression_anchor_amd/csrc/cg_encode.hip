@@ -4,7 +4,7 @@
 // of one (kv, layer) row in lockstep, so every input row it reads is one
 // coalesced 128-byte segment.  Streams land in per-stream scratch, then a
 // wavefront prefix sum over the stream lengths packs them into the blob.
-#include "cg_internal.h"
+#include "cg_build.h"
 
 namespace cg {
 namespace {

@@ -4,7 +4,7 @@
 // depend on the order in which workgroups run.
 #include <float.h>
 
-#include "cg_internal.h"
+#include "cg_build.h"
 
 namespace cg {
 namespace {
