@@ -19,10 +19,10 @@ struct cg_tables {
   DevTables t;
   uint64_t id = 0;
   std::mutex mu;  // guards the encode buffers and the status words
-  uint32_t* scratch = nullptr;   // per launch slot: [2][L][C] streams of swb words
+  uint32_t* scratch = nullptr;   // per launch slot: [2][L][nblk] blocks of [swb][64] words
   size_t scratch_words = 0;
   uint32_t* lens = nullptr;      // per launch slot: [2][L][C]
-  uint32_t* row_words = nullptr; // per launch slot: [2L]
+  uint32_t* row_words = nullptr; // per launch slot: [2L] rows, then [2L][nblk] blocks
   int enc_slots = 0;             // blobs one encode launch can hold
   uint32_t* enc_status = nullptr;   // per blob of a batch: W, too large, non-finite, pad
   uint32_t* enc_host = nullptr;     // pinned mirror
@@ -578,7 +578,7 @@ int cg_encode_batch(const cg_tables* ch, const void* k_dev, const void* v_dev, i
   std::lock_guard<std::mutex> lk(h->mu);
   // a stream's words plus the placeholder word in front of them
   const size_t swb = std::max<size_t>(stream_words_bound(t.CH - (t.CH + t.G - 1) / t.G), 1) + 1;
-  const size_t slot_words = t.lay.n * swb;
+  const size_t slot_words = (size_t)2 * t.L * t.nblk * kLanes * swb;  // whole 64-stream blocks
   const int slots = (int)std::max<size_t>(
       1, std::min<size_t>({(size_t)kEncMaxBlobs, (size_t)n, kEncScratchBudget / (4 * slot_words)}));
   if (h->enc_slots < slots) {
@@ -590,7 +590,7 @@ int cg_encode_batch(const cg_tables* ch, const void* k_dev, const void* v_dev, i
     h->enc_slots = 0;
     if (hipMalloc(&h->scratch, 4 * slot_words * slots) != hipSuccess ||
         hipMalloc(&h->lens, 4 * t.lay.n * slots) != hipSuccess ||
-        hipMalloc(&h->row_words, 8 * (size_t)t.L * slots) != hipSuccess)
+        hipMalloc(&h->row_words, 4 * (size_t)2 * t.L * (1 + t.nblk) * slots) != hipSuccess)
       return fail(CG_E_NOMEM, "encode scratch");
     h->enc_slots = slots;
   }
@@ -646,7 +646,8 @@ int cg_encode_batch(const cg_tables* ch, const void* k_dev, const void* v_dev, i
       B.inv_step = reinterpret_cast<const float*>(t.ser + t.lay.off_inv_step[qualities[i]]);
       B.scratch = h->scratch + (size_t)j * slot_words;
       B.lens = h->lens + (size_t)j * t.lay.n;
-      B.row_words = h->row_words + (size_t)j * 2 * t.L;
+      B.row_words = h->row_words + (size_t)j * 2 * t.L * (1 + t.nblk);
+      B.block_words = B.row_words + 2 * t.L;
       B.status = h->enc_status + 4 * (size_t)i;
       // open a new group at a quality change or when the current one is full
       if (j == 0 || a.b[j - 1].q != B.q || a.groups[a.n_groups - 1].blob[3] >= 0) {

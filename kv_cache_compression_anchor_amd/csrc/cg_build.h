@@ -61,9 +61,10 @@ struct EncBlob {
   BlobLayout lay;
   const uint16_t* img;       // cum images of quality q
   const float* inv_step;     // of quality q
-  uint32_t* scratch;         // per stream: swb words, the first a placeholder
+  uint32_t* scratch;         // per 64-stream block: [swb rows][64 lanes] words, row 0 placeholders
   uint32_t* lens;            // [2][L][C] words
   uint32_t* row_words;       // [2L]
+  uint32_t* block_words;     // [2L][nblk] words of each 64-stream block
   uint32_t* status;          // [0] payload words, [1] too large for cap, [2] non-finite input
 };
 struct EncGroup {  // blobs of one quality coded by one workgroup (one wave each)

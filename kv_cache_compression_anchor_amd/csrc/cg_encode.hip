@@ -27,8 +27,12 @@ struct RcEnc {
   uint32_t P;      // 0xFFFFFFFF words after W, not final yet
 };
 
-// A lane's output words, through a buffer resource over the wave's 64 streams:
-// `woff` is the byte offset of W's slot.
+// A lane's output words, through a buffer resource over the wave's 64 streams,
+// which lie interleaved word by word ([row][lane]): the lanes of a wave emit at
+// similar rates, so the 64 streams' current words share a few cache lines
+// instead of holding 64 lines partly written.  `woff` is the byte offset of
+// W's slot; a word's successor is one row (256 bytes) further.
+constexpr uint32_t kRowBytes = 4u * kLanes;
 struct Sink {
   __amdgpu_buffer_rsrc_t rs;
   uint32_t woff;
@@ -36,7 +40,7 @@ struct Sink {
 
 __device__ __forceinline__ void emit_word(Sink& o, uint32_t w) {
   __builtin_amdgcn_raw_buffer_store_b32(w, o.rs, o.woff, 0, 0);
-  o.woff += 4u;
+  o.woff += kRowBytes;
 }
 
 // --- general steps: every case, used for the rare symbols and the flush ----
@@ -108,7 +112,7 @@ __device__ __forceinline__ void rc_put(RcEnc& e, uint32_t c0, uint32_t freq, Sin
   const uint32_t W1 = e.W + (c ? 1u : 0u);
   const bool emit = ext && !rare;
   if (emit) __builtin_amdgcn_raw_buffer_store_b32(W1, o.rs, o.woff, 0, 0);
-  o.woff += emit ? 4u : 0u;
+  o.woff += emit ? kRowBytes : 0u;
   e.W = emit ? wn : W1;
   const uint32_t lo_k = ext ? __builtin_amdgcn_ubfe(lo, 0u, e.kh) : lo;
   const uint32_t hi_k = ext ? 0u : hi;
@@ -196,14 +200,14 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
       (int)((uint32_t)B.tc * row_bytes), kBufRsrcWord3);
   const uint32_t lane_off = 2u * (uint32_t)c;
   const uint8_t* tb = reinterpret_cast<const uint8_t*>(tab) + 2 * lane_slot(lane);
-  // the wave's 64 streams of swb words in scratch, each led by its placeholder
-  const uint32_t swb4 = 4u * (uint32_t)a.swb;
+  // the wave's block of 64 streams in scratch, [swb rows][64 lanes], row 0
+  // holding the placeholders
   Sink o;
-  const size_t wave_pi = ((size_t)kv * a.L + l) * a.C + (size_t)cb * kLanes;  // lane 0's stream
-  o.rs = __builtin_amdgcn_make_buffer_rsrc(B.scratch + wave_pi * a.swb, 0, (int)(kLanes * swb4),
-                                           kBufRsrcWord3);
-  o.woff = (uint32_t)lane * swb4;
-  const uint32_t woff0 = o.woff + 4u;  // the stream's first word
+  const size_t block = ((size_t)kv * a.L + l) * a.nblk + cb;
+  o.rs = __builtin_amdgcn_make_buffer_rsrc(B.scratch + block * kLanes * a.swb, 0,
+                                           (int)(kRowBytes * (uint32_t)a.swb), kBufRsrcWord3);
+  o.woff = 4u * (uint32_t)lane;
+  const uint32_t woff0 = o.woff + kRowBytes;  // the stream's first word
   int8_t* anchors = reinterpret_cast<int8_t*>(B.blob + B.lay.off_anchor) +
                     ((size_t)kv * a.L + l) * B.ng * a.C + c;
   RcEnc e = {0, 0u, 0u, 0xFFFFFFFFu, 0u, 0u};
@@ -251,22 +255,29 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
   }
   if (B.tc > B.ng) rc_finish(e, o);  // a stream without symbols stays empty
   if (nonfinite) atomicOr(&B.status[2], 1u);
-  const uint32_t nwords = o.woff > woff0 ? (o.woff - woff0) >> 2 : 0u;
+  const uint32_t nwords = o.woff > woff0 ? (o.woff - woff0) / kRowBytes : 0u;
   B.lens[pi] = nwords;
   reinterpret_cast<uint16_t*>(B.blob + B.lay.off_len)[pi] = (uint16_t)nwords;
 }
 
-// words of every (kv, layer) row of every blob
+// words of every 64-stream block and of every (kv, layer) row of every blob
 __global__ __launch_bounds__(256) void k_row_totals(EncodeArgs a) {
   __shared__ uint32_t part[4];
   const EncBlob& B = a.b[blockIdx.y];
-  const uint32_t* r = B.lens + (size_t)blockIdx.x * a.C;
-  uint32_t s = 0;
-  for (int j = threadIdx.x; j < a.C; j += 256) s += r[j];
-  for (int o = 32; o; o >>= 1) s += __shfl_xor(s, o);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+  const int row = blockIdx.x, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t* r = B.lens + (size_t)row * a.C;
+  uint32_t total = 0;
+  for (int cb = wave; cb < a.nblk; cb += 4) {
+    const int c = cb * kLanes + lane;
+    uint32_t s = c < a.C ? r[c] : 0u;
+    for (int o = 32; o; o >>= 1) s += __shfl_xor(s, o);
+    if (lane == 0) B.block_words[(size_t)row * a.nblk + cb] = s;
+    total += s;
+  }
+  if (lane == 0) part[wave] = total;
   __syncthreads();
-  if (threadIdx.x == 0) B.row_words[blockIdx.x] = part[0] + part[1] + part[2] + part[3];
+  if (threadIdx.x == 0) B.row_words[row] = part[0] + part[1] + part[2] + part[3];
 }
 
 // per blob: row offsets, payload size, header; flags a blob larger than cap
@@ -313,47 +324,57 @@ __global__ __launch_bounds__(256) void k_pad(EncodeArgs a) {
   for (size_t j = tail0 + threadIdx.x; j < tail1; j += 256) B.blob[j] = 0;
 }
 
-// Pack 256 streams of one row: the row offset plus the lengths of the row's
-// earlier streams, then a block-wide exclusive prefix sum (wave scans plus the
-// wave totals); each wave copies whole streams with coalesced 64-word moves.
+// Pack one 64-stream block: its payload offset is the row's offset plus the
+// words of the row's earlier blocks, each stream's the block's offset plus the
+// lengths of the streams before it (a wave scan).  The block's words are
+// [row][lane] in scratch; 64-row tiles go through LDS (rows padded to 65 words,
+// so reading a column hits 64 distinct banks) and leave as each stream's
+// consecutive words, 64 at a time.
+constexpr int kPackPitch = kLanes + 1;
 __global__ __launch_bounds__(256) void k_pack(EncodeArgs a) {
   const EncBlob& B = a.b[blockIdx.y];
   if (B.status[1]) return;
-  __shared__ uint32_t wsum[4];
-  __shared__ uint32_t soff[256];
-  __shared__ uint32_t slen[256];
-  const int nseg = (a.C + 255) / 256;
-  const int row = blockIdx.x / nseg, seg = blockIdx.x % nseg;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const uint32_t* lens = B.lens + (size_t)row * a.C;
-  uint32_t before = 0;
-  for (int j = tid; j < seg * 256; j += 256) before += lens[j];
-  for (int o = 32; o; o >>= 1) before += __shfl_xor(before, o);
-  if (lane == 0) wsum[wave] = before;
-  __syncthreads();
-  const uint32_t base = reinterpret_cast<const uint32_t*>(B.blob + B.lay.off_rows)[row] +
-                        wsum[0] + wsum[1] + wsum[2] + wsum[3];
-  __syncthreads();
-  const int c = seg * 256 + tid;
-  const uint32_t len = c < a.C ? lens[c] : 0u;
-  uint32_t incl = len;
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
+  __shared__ uint32_t tile[kLanes * kPackPitch];
+  __shared__ uint32_t soff[kLanes], slen[kLanes];
+  __shared__ uint32_t maxlen;
+  const int row = blockIdx.x / a.nblk, cb = blockIdx.x % a.nblk;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (wave == 0) {
+    const uint32_t* bw = B.block_words + (size_t)row * a.nblk;
+    uint32_t before = 0;
+    for (int j = lane; j < cb; j += kLanes) before += bw[j];
+    for (int o = 32; o; o >>= 1) before += __shfl_xor(before, o);
+    const int c = cb * kLanes + lane;
+    const uint32_t len = c < a.C ? B.lens[(size_t)row * a.C + c] : 0u;
+    uint32_t incl = len, mx = len;
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    for (int o = 32; o; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
+    const uint32_t base = reinterpret_cast<const uint32_t*>(B.blob + B.lay.off_rows)[row] + before;
+    soff[lane] = base + incl - len;
+    slen[lane] = len;
+    if (lane == 0) maxlen = mx;
   }
-  if (lane == 63) wsum[wave] = incl;
   __syncthreads();
-  uint32_t off = base;
-  for (int w = 0; w < wave; w++) off += wsum[w];
-  soff[tid] = off + incl - len;
-  slen[tid] = len;
-  __syncthreads();
+  const uint32_t* src = B.scratch + ((size_t)row * a.nblk + cb) * kLanes * a.swb + kLanes;  // row 1
   uint32_t* pay = reinterpret_cast<uint32_t*>(B.blob + B.lay.off_pay);
-  const int n = min(256, a.C - seg * 256);
-  for (int j = wave; j < n; j += 4) {
-    const uint32_t* src = B.scratch + ((size_t)row * a.C + seg * 256 + j) * a.swb + 1;
-    uint32_t* dst = pay + soff[j];
-    for (uint32_t k = lane; k < slen[j]; k += 64) dst[k] = src[k];
+  const uint32_t mx = maxlen;
+  const int nt = (int)((mx + kLanes - 1) / kLanes), ns = min(kLanes, a.C - cb * kLanes);
+  for (int kt = 0; kt < nt; kt++) {
+    // rows kt*64 .. kt*64 + 63 of the block that hold words (the longest
+    // stream's; rows past it lie outside the block): wave w loads every fourth
+    for (int k = wave; k < kLanes && (uint32_t)(kt * kLanes + k) < mx; k += 4)
+      tile[k * kPackPitch + lane] = src[((size_t)kt * kLanes + k) * kLanes + lane];
+    __syncthreads();
+    // stream j's words kt*64 + lane
+    for (int j = wave; j < ns; j += 4) {
+      const uint32_t kk = (uint32_t)(kt * kLanes + lane);
+      if (kk < slen[j]) pay[soff[j] + kk] = tile[lane * kPackPitch + j];
+    }
+    __syncthreads();
   }
 }
 
@@ -369,7 +390,7 @@ hipError_t launch_encode(const EncodeArgs& a, hipStream_t st) {
   k_row_totals<<<dim3(2 * a.L, nb), 256, 0, st>>>(a);
   k_row_scan<<<nb, 64, 0, st>>>(a);
   k_pad<<<nb, 256, 0, st>>>(a);
-  k_pack<<<dim3(2 * a.L * ((a.C + 255) / 256), nb), 256, 0, st>>>(a);
+  k_pack<<<dim3(2 * a.L * a.nblk, nb), 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
