@@ -9,8 +9,10 @@ H,M,L,H,M,L with one cg_decode_async call.  Inputs are resident in HBM when the 
 `value` is the decode throughput in GB/s of fp16 KV written; the roofline entry
 counts the decode kernel's algorithmic bytes (blob bytes read + fp16 written)
 per launch against MI355X's 8 TB/s HBM peak, with the kernel's duration taken
-from HIP events on the stream it runs on.  The CPU baseline is the oracle's
-decode of a bounded sample of the same selection on this host's cores.
+from HIP events on the stream it runs on, and also against what a plain 1 GiB
+device-to-device copy reaches on the same GPU.  The CPU baseline is the
+oracle's decode of a bounded sample of the same selection on this host's cores
+(and on one thread).
 """
 from __future__ import annotations
 
@@ -145,6 +147,9 @@ def main():
     sel_blob_bytes = sum(sizes[(c, q)] for c, q in enumerate(sel))
     dec_ms = [d for r in results for d in r["decode_ms"]]
     dec_avg_ms = sum(dec_ms) / len(dec_ms)
+    dec_sorted = sorted(dec_ms)
+    dec_median_ms = dec_sorted[len(dec_sorted) // 2]
+    copy_gbps = copy_bandwidth(torch, dev, stream)
     value = fp16_bytes / (dec_avg_ms * 1e-3) / 1e9
     achieved = (fp16_bytes + sel_blob_bytes) / (dec_avg_ms * 1e-3) / 1e9
     enc_ms = sum(r["encode_ms"] for r in results) / len(results)
@@ -196,6 +201,8 @@ def main():
         "compress_ratio_by_quality": {q: round(r, 4) for q, r in ratio_q.items()},
         "selection_blob_bytes": sel_blob_bytes,
         "decode_ms": round(dec_avg_ms, 4),
+        "decode_ms_median": round(dec_median_ms, 4),
+        "decode_ms_min": round(dec_sorted[0], 4),
         "decode_GBps_algorithmic": round(achieved, 2),
         "encode_ms_all_chunks_all_qualities": round(enc_ms, 3),
         "encode_GBps_fp16_in": round(nq * fp16_bytes / (enc_ms * 1e-3) / 1e9, 2),
@@ -203,7 +210,8 @@ def main():
         "build_tables_GBps_fp16_in": round(fp16_bytes / (build_ms * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "kernel": "k_decode", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "copy_GBps": round(copy_gbps, 1), "frac_of_copy": round(achieved / copy_gbps, 4)},
         "cpu_baseline": cpu,
         "encode_roofline": {"bound": "hbm", "kernel": "k_encode + k_pack (all 18 blobs)",
                             "achieved": round(enc_achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -377,6 +385,36 @@ def record_traffic(path, workload, fetch_csv, write_csv, copy_fetch_csv, copy_wr
     print(json.dumps(rec["workloads"][workload]))
 
 
+def copy_bandwidth(torch, dev, stream, nbytes=1 << 30, reps=5):
+    """HBM bandwidth a plain device-to-device copy reaches on this GPU: bytes read
+    plus bytes written per second (torch copy_ of nbytes, HIP events, best of reps)."""
+    a = torch.empty(nbytes // 4, dtype=torch.int32, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    b.copy_(a)
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        b.copy_(a)
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del a, b
+    return 2 * nbytes / (best * 1e-3) / 1e9
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, k, v, tab, bufs, sizes, sel, seconds):
     """The oracle decoding the selection (the same blobs the GPU decodes) on this
     host's cores, chunk after chunk, until about `seconds` have passed; GB/s of
@@ -402,11 +440,17 @@ def cpu_baseline(w, k, v, tab, bufs, sizes, sel, seconds):
         if dt >= seconds and n >= len(blobs):
             break
     out_bytes = 2 * 2 * w.layers * tok * w.channels
+    # one thread, on the first blob of the selection
+    t1 = time.perf_counter()
+    oracle.decode_blob(t, blobs[0], ko, vo, threads=1)
+    dt1 = time.perf_counter() - t1
+    one = 2 * 2 * w.layers * min(w.chunk_tokens, w.tokens) * w.channels / dt1 / 1e9
     return {"value": round(out_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"oracle decode of {n} chunk blobs of the selection "
                       f"({n // len(blobs)}+ passes, {2 * w.layers * tok * w.channels} elements, "
-                      f"{dt:.1f} s)"}
+                      f"{dt:.1f} s)",
+            "value_1_thread": round(one, 4), "cpu_model": cpu_model()}
 
 
 def cpu_baseline_encode(w, k, v, tab, seconds):
