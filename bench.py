@@ -47,6 +47,12 @@ def parse():
                     help="write the --workload's record of --traffic-json from rocprofv3 --pmc "
                          "counter_collection.csv files (FETCH_SIZE and WRITE_SIZE of the decoder, "
                          "then of a --copy-calibration run); no GPU work")
+    ap.add_argument("--adaptive", action="store_true",
+                    help="measure the bandwidth-adaptive version choice instead: every chunk of "
+                         "the workload encoded at H, M and L, streamed over a simulated "
+                         "fluctuating link; SLO violation rates, adaptive vs fixed versions")
+    ap.add_argument("--contexts", type=int, default=2000,
+                    help="contexts streamed per policy in --adaptive")
     ap.add_argument("--streamed", action="store_true",
                     help="measure the chunk pipeline instead: the Llama-70B-shape 16K schedule "
                          "decoded from pinned host memory (H2D on one stream, decode on another)")
@@ -79,6 +85,9 @@ def main():
     import kv_cache_compression_anchor_amd as cg
     import synth
 
+    if args.adaptive:
+        adaptive(args)
+        return
     if args.streamed:
         streamed(args)
         return
@@ -221,6 +230,137 @@ def main():
                            "unit": "GB/s", "frac": round(build_achieved / HBM_PEAK_GBPS, 4)},
         "cpu_baseline_encode": cpu_enc,
         "input_generation_s": round(t_gen, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def stream_context_lib(sizes, decode_ms, slo_ms, send, prior_bpms, policy="adaptive"):
+    """One context streamed chunk by chunk over a simulated link, each chunk's
+    version chosen by the library (cg_plan_chunk) from the throughput the
+    previous chunk saw.  sizes[c][q] / decode_ms[c][q]: bytes and decode time of
+    chunk c at version q (H, M, L); send(nbytes) -> ms on the link (advances its
+    clock).  Decoding of a chunk overlaps the transfer of the later ones.
+    Returns (load time in ms, versions)."""
+    import kv_cache_compression_anchor_amd as cg
+    n = len(sizes)
+    t = 0.0
+    decoded = 0.0
+    bw = prior_bpms
+    versions = []
+    for c in range(n):
+        if policy == "adaptive":
+            left = [sum(int(sizes[j][q]) for j in range(c, n)) for q in range(3)]
+            dleft = [sum(float(decode_ms[j][q]) for j in range(c, n)) for q in range(3)]
+            q, _ = cg.cg_plan_chunk(slo_ms - t, bw, left, dleft)
+        else:
+            q = "HML".index(policy)
+        dt = send(int(sizes[c][q]))
+        t += dt
+        bw = int(sizes[c][q]) / dt
+        decoded = max(decoded, t) + float(decode_ms[c][q])
+        versions.append(q)
+    return decoded, versions
+
+
+def adaptive(args):
+    """Bandwidth-adaptive streaming (CacheGen blog 2.2) on the workload: every
+    chunk encoded at H, M and L on the GPU; each blob's decode time measured
+    alone (HIP events, median of 5); then --contexts contexts streamed over a
+    simulated link whose bandwidth fluctuates around 3 Gbit/s (synth.netsim,
+    50 ms steps), one context every 2.5 s of the trace, under the fixed
+    versions and under the library's per-chunk choice.  The SLO is set from the
+    context's H size: SLO = f * (H bytes at the mean bandwidth) for f in 0.9,
+    1.0, 1.2.  The chosen versions of one context are then decoded together on
+    the GPU and checked for a clean status."""
+    import numpy as np
+    import torch
+
+    import kv_cache_compression_anchor_amd as cg
+    import synth
+    from synth.netsim import Link, bandwidth_trace
+    w = synth.workload(args.workload)
+    if len(w.qualities) != 3:
+        raise SystemExit(f"{w.name} builds only {len(w.qualities)} qualities; --adaptive needs H, M, L")
+    k, v = synth.gen_kv(w)
+    kd = torch.from_numpy(k).cuda()
+    vd = torch.from_numpy(v).cuda()
+    p = cg.make_params(w.layers, w.tokens, w.channels, w.chunk_tokens, w.group_tokens,
+                       w.layer_group_end, w.layer_step, w.quality_mult, w.quality_mask)
+    tab = cg.cg_build_tables(p, kd, vd)
+    nch = w.n_chunks
+    jobs = [(c, q) for c in range(nch) for q in range(3)]
+    outs = [torch.empty(cg.cg_encode_bound(tab, c), dtype=torch.uint8, device="cuda")
+            for c, q in jobs]
+    lens = cg.cg_encode_batch(tab, kd, vd, [c for c, q in jobs], [q for c, q in jobs], outs)
+    blob = {j: o[:n] for j, o, n in zip(jobs, outs, lens)}
+    sizes = [[int(lens[jobs.index((c, q))]) for q in range(3)] for c in range(nch)]
+    info = {j: cg.cg_chunk_info_parse(b[:64].cpu()) for j, b in blob.items()}
+    ko, vo = torch.empty_like(kd), torch.empty_like(vd)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    dec_ms = [[0.0] * 3 for _ in range(nch)]
+    for (c, q), b in blob.items():
+        ts = []
+        for _ in range(6):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            cg.cg_decode_async(tab, [b], [info[(c, q)]], ko, vo, st)
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        dec_ms[c][q] = sorted(ts[1:])[2]
+    mean_gbps, step_ms, every_ms = 3.0, 50.0, 2500.0
+    n_steps = int(args.contexts * every_ms / step_ms) + 4000
+    trace = bandwidth_trace(11, n_steps, mean_gbps=mean_gbps)
+    mean_bpms = mean_gbps * 1e9 / 8 / 1e3
+    h_bytes = sum(sz[0] for sz in sizes)
+    results = {}
+    mix = None
+    sample_versions = None
+    for f in (0.9, 1.0, 1.2):
+        slo = f * h_bytes / mean_bpms
+        res = {}
+        for pol in ("H", "M", "L", "adaptive"):
+            viol, total, counts = 0, 0.0, [0, 0, 0]
+            for i in range(args.contexts):
+                link = Link(trace, step_ms, start_ms=i * every_ms)
+                t, vs = stream_context_lib(sizes, dec_ms, slo, link.send, mean_bpms, pol)
+                viol += t > slo
+                total += t
+                for q in vs:
+                    counts[q] += 1
+                if pol == "adaptive" and f == 1.0 and i == 7:
+                    sample_versions = vs
+            res[pol] = {"violation_rate": round(viol / args.contexts, 4),
+                        "mean_load_ms": round(total / args.contexts, 2)}
+            if pol == "adaptive":
+                res[pol]["version_share"] = {n: round(c / sum(counts), 4) for n, c in zip("HML", counts)}
+        results[f"slo_{f:g}x"] = {"slo_ms": round(slo, 2), **res}
+    # the chosen versions of one context decode together on the GPU
+    sel = [blob[(c, q)] for c, q in enumerate(sample_versions)]
+    sinfo = [info[(c, q)] for c, q in enumerate(sample_versions)]
+    st.zero_()
+    cg.cg_decode_async(tab, sel, sinfo, ko, vo, st)
+    torch.cuda.synchronize()
+    if int(st.item()) != 0:
+        raise SystemExit("decode of an adaptive selection reported a corrupt stream")
+    main = results["slo_1x"]
+    line = {
+        "metric": "SLO violation rate under a fluctuating 3 Gbit/s link, adaptive versions vs fixed H",
+        "value": main["adaptive"]["violation_rate"],
+        "unit": "fraction of contexts",
+        "n_gpus": 1,
+        "higher_is_better": False,
+        "vs_baseline": None,
+        "data": "synthetic K/V (synth) and synthetic bandwidth trace (synth.netsim, seed 11)",
+        "config": {"workload": w.name, "chunks": nch, "contexts": args.contexts,
+                   "link": "log-AR(1) bandwidth, mean 3 Gbit/s, 50 ms steps",
+                   "bandwidth_estimate": "throughput of the previous chunk (3 Gbit/s prior)"},
+        "fixed_H_violation_rate": main["H"]["violation_rate"],
+        "chunk_bytes": {n: [sz[q] for sz in sizes] for q, n in enumerate("HML")},
+        "decode_ms_per_chunk": {n: [round(d[q], 4) for d in dec_ms] for q, n in enumerate("HML")},
+        "results": results,
+        "sample_adaptive_versions": "".join("HML"[q] for q in sample_versions),
     }
     print(json.dumps(line), flush=True)
 

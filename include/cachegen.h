@@ -167,6 +167,36 @@ int cg_decode_streamed(const cg_tables* tables, int32_t n, const void* const* bl
                        void* staging_dev, size_t staging_cap, uint32_t* status_dev,
                        void* copy_stream, void* compute_stream);
 
+/* Bandwidth-adaptive choice of the next chunk's version (CacheGen blog 2.2,
+ * the bandwidth-adaptive selection formula: each chunk's version is chosen
+ * from the measured bandwidth B and the service-level objective).  For every
+ * version q that exists (bytes_left[q] > 0) the ratio
+ *     r[q] = (budget_ms - decode_ms_left[q]) / (bytes_left[q] / bandwidth_bpms)
+ * is the SLO time left after decoding over the time to send the rest of the
+ * context at q.  The choice is the highest quality (H, then M, then L) with
+ * r[q] >= 1, i.e. whose transfer fits what is left of the SLO; when none fits,
+ * the version that is done soonest, the smallest bytes_left[q] / bandwidth_bpms
+ * + decode_ms_left[q] (the first in H, M, L order on a tie).
+ *   budget_ms        SLO minus the time this context has already taken (may be
+ *                    negative: then nothing fits)
+ *   bandwidth_bpms   bytes per millisecond, > 0 and finite (the throughput the
+ *                    previous chunk saw, or a prior for the first chunk)
+ *   bytes_left[q]    bytes of this chunk and all later ones at version q (H, M,
+ *                    L); 0 marks a version that was not encoded
+ *   decode_ms_left[q] their decode time, >= 0
+ * Host only; ratios are computed in binary64 in exactly this order.  Writes the
+ * chosen quality (CG_Q_H / CG_Q_M / CG_Q_L) to *quality_out and, when ratio_out
+ * is not NULL, r[q] for each version (0 for a missing one) to ratio_out[0..2].
+ * CG_E_INVAL: NULL in or quality_out, a NaN budget, a bandwidth that is not
+ * positive and finite, a negative or non-finite decode time, or no version. */
+typedef struct {
+  double budget_ms;
+  double bandwidth_bpms;
+  uint64_t bytes_left[3];
+  double decode_ms_left[3];
+} cg_chunk_plan_in;
+int cg_plan_chunk(const cg_chunk_plan_in* in, int32_t* quality_out, double* ratio_out);
+
 /* Message of the calling thread's last error ("" if none). */
 const char* cg_last_error(void);
 

@@ -5,7 +5,8 @@ from ._binding import (CG_E_CAPACITY, CG_E_CORRUPT, CG_E_HIP, CG_E_INVAL, CG_E_M
                        Tables, cg_build_tables, cg_chunk_info, cg_chunk_info_parse, cg_decode,
                        cg_decode_async, cg_decode_streamed, cg_encode, cg_encode_batch,
                        cg_encode_bound,
-                       cg_last_error, cg_num_chunks, cg_params, cg_tables_deserialize,
+                       cg_chunk_plan_in, cg_last_error, cg_num_chunks, cg_params,
+                       cg_plan_chunk, cg_tables_deserialize,
                        cg_tables_free, cg_tables_id, cg_tables_params, cg_tables_serialize, lib,
                        make_params)
 

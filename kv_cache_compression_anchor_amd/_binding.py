@@ -23,7 +23,7 @@ _NAMES = {0: "CG_OK", -1: "CG_E_INVAL", -2: "CG_E_NOMEM", -3: "CG_E_HIP", -4: "C
 EXPORTS = ["cg_build_tables", "cg_tables_free", "cg_tables_serialize", "cg_tables_deserialize",
            "cg_tables_id", "cg_tables_params", "cg_num_chunks", "cg_encode_bound", "cg_encode",
            "cg_encode_batch", "cg_chunk_info_parse", "cg_decode", "cg_decode_async", "cg_decode_streamed",
-           "cg_last_error"]
+           "cg_plan_chunk", "cg_last_error"]
 
 
 class CgError(RuntimeError):
@@ -38,6 +38,11 @@ class cg_params(C.Structure):
                 ("n_layer_groups", C.c_int32), ("layer_group_end", C.c_int32 * 3),
                 ("layer_step", C.c_float * 3), ("quality_mult", C.c_float * 3),
                 ("quality_mask", C.c_uint32)]
+
+
+class cg_chunk_plan_in(C.Structure):
+    _fields_ = [("budget_ms", C.c_double), ("bandwidth_bpms", C.c_double),
+                ("bytes_left", C.c_uint64 * 3), ("decode_ms_left", C.c_double * 3)]
 
 
 class cg_chunk_info(C.Structure):
@@ -77,6 +82,8 @@ def lib():
             "cg_decode_async": (I, [P, I32, C.POINTER(P), C.POINTER(cg_chunk_info), P, P, P, P]),
             "cg_decode_streamed": (I, [P, I32, C.POINTER(P), C.POINTER(cg_chunk_info), P, P, P,
                                        SZ, P, P, P]),
+            "cg_plan_chunk": (I, [C.POINTER(cg_chunk_plan_in), C.POINTER(I32),
+                                  C.POINTER(C.c_double)]),
             "cg_last_error": (C.c_char_p, []),
         }
         for name, (res, args) in sigs.items():
@@ -299,3 +306,19 @@ def cg_decode_streamed(t: Tables, host_blobs, infos, k_out, v_out, staging, stat
                                     _dev_ptr(staging, torch.uint8, "staging"), staging.numel(),
                                     _dev_ptr(status, torch.int32, "status"),
                                     _stream(copy_stream), _stream(compute_stream)))
+
+
+def cg_plan_chunk(budget_ms: float, bandwidth_bpms: float, bytes_left, decode_ms_left):
+    """The version (CG_Q_H / M / L) of the next chunk and the three ratios the
+    library computed; bytes_left / decode_ms_left are per version (H, M, L), 0
+    bytes marking a version that does not exist.  Host only."""
+    p = cg_chunk_plan_in()
+    p.budget_ms = float(budget_ms)
+    p.bandwidth_bpms = float(bandwidth_bpms)
+    for q in range(3):
+        p.bytes_left[q] = int(bytes_left[q])
+        p.decode_ms_left[q] = float(decode_ms_left[q])
+    q = C.c_int32(-1)
+    r = (C.c_double * 3)()
+    _check(lib().cg_plan_chunk(C.byref(p), C.byref(q), r))
+    return q.value, [r[0], r[1], r[2]]

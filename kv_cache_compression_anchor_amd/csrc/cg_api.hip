@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -356,6 +357,34 @@ int enqueue_decode(const cg_tables* h, int n, const void* const* blobs, const cg
 extern "C" {
 
 const char* cg_last_error(void) { return g_err.c_str(); }
+
+int cg_plan_chunk(const cg_chunk_plan_in* in, int32_t* quality_out, double* ratio_out) {
+  if (!in || !quality_out) return fail(CG_E_INVAL, "NULL argument");
+  if (!(in->bandwidth_bpms > 0.0) || !std::isfinite(in->bandwidth_bpms))
+    return fail(CG_E_INVAL, "bandwidth must be positive and finite");
+  if (std::isnan(in->budget_ms)) return fail(CG_E_INVAL, "budget is NaN");
+  double r[3] = {0.0, 0.0, 0.0};
+  double best_end = 0.0;
+  int best = -1, first_fit = -1;
+  for (int q = 0; q < 3; q++) {
+    const double d = in->decode_ms_left[q];
+    if (!(d >= 0.0) || !std::isfinite(d)) return fail(CG_E_INVAL, "bad decode time");
+    if (in->bytes_left[q] == 0) continue;
+    const double t_send = (double)in->bytes_left[q] / in->bandwidth_bpms;
+    r[q] = (in->budget_ms - d) / t_send;
+    if (first_fit < 0 && r[q] >= 1.0) first_fit = q;
+    const double end = t_send + d;  // when nothing fits: the version done soonest
+    if (best < 0 || end < best_end) {
+      best = q;
+      best_end = end;
+    }
+  }
+  if (best < 0) return fail(CG_E_INVAL, "no version of the chunk");
+  *quality_out = first_fit >= 0 ? first_fit : best;
+  if (ratio_out)
+    for (int q = 0; q < 3; q++) ratio_out[q] = r[q];
+  return CG_OK;
+}
 
 int cg_build_tables(const cg_params* params, const void* k_dev, const void* v_dev, void* stream,
                     cg_tables** out) {
