@@ -19,8 +19,8 @@ version's transfer fits in the time the SLO leaves after decoding, so
   no version fits, the one that is done soonest (smallest T_transmit + T_decode;
   an argmax of negative scores would pick the largest version instead).
 
-B is the throughput the previous chunk of the context saw (the first chunk of a
-context uses the throughput of the last chunk sent before it).
+B is the throughput the previous chunk of the context saw; the caller gives a
+prior for the first chunk.
 
 Parity status: the rule is pinned by closed-form cases and by monotonicity in
 bandwidth and budget (tests/test_oracle_controller.py); the pages give no
