@@ -1,14 +1,9 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
 benchmark times (one cg_encode_batch for all blobs, one cg_decode_async for the
-selection).  The Mistral-7B and Llama-7B shapes are compared in full; the 16 GB
-Llama-34B 80K shape and the streamed Llama-70B shape are compared on sampled
-streams, against oracle tables built from the sampled channels alone (the
-tables are per channel, so they equal the full tables' entries) and the
-oracle's own encoding and decoding of those streams."""
-import dataclasses
+selection, or the two-stream chunk pipeline): tables, every blob byte and every
+decoded value against the oracle's, for all four full-size workloads."""
 import time
 
-import numpy as np
 import pytest
 
 import oracle
@@ -87,81 +82,38 @@ def test_llama7b_full():
     full_parity("llama7b")
 
 
-def sampled_channels(C, rng, n=24):
-    return np.sort(rng.choice(C, n, replace=False))
-
-
-def check_sampled(w, k, v, tab, blobs_by_chunk, ko, vo, quality_of_chunk, rng, n_streams=40):
-    """Tables, streams and decoded values of sampled channels against the oracle."""
-    import kv_cache_compression_anchor_amd as cg
-    sel_c = sampled_channels(w.channels, rng)
-    ks = np.ascontiguousarray(k[:, :, sel_c])
-    vs = np.ascontiguousarray(v[:, :, sel_c])
-    wsub = dataclasses.replace(w, channels=len(sel_c))
-    ot = oracle.build_tables(oracle.params_for(wsub), ks, vs, threads=16)
-    otv = oracle.tables_view(ot)
-    gtv = oracle.tables_view(cg.cg_tables_serialize(tab))
-    assert np.array_equal(gtv.scale_a[:, :, sel_c], otv.scale_a)
-    assert np.array_equal(gtv.inv_a[:, :, sel_c], otv.inv_a)
-    for q in w.qualities:
-        assert np.array_equal(gtv.step[q][:, :, sel_c], otv.step[q])
-        assert np.array_equal(gtv.inv_step[q][:, :, sel_c], otv.inv_step[q])
-        assert np.array_equal(gtv.freq[q][:, :, sel_c], otv.freq[q])
-    log(f"[{w.name}] tables of {len(sel_c)} sampled channels equal")
-    chunks = [0, w.n_chunks - 1] + list(rng.integers(0, w.n_chunks, n_streams - 2))
-    for ch in chunks:
-        ch = int(ch)
-        q = quality_of_chunk[ch]
-        t0 = ch * w.chunk_tokens
-        tc = min(w.chunk_tokens, w.tokens - t0)
-        bv = oracle.blob_view(blobs_by_chunk[ch].cpu().numpy().tobytes())
-        kv, l, j = int(rng.integers(2)), int(rng.integers(w.layers)), int(rng.integers(len(sel_c)))
-        c = int(sel_c[j])
-        x = (ks, vs)[kv][l, t0:t0 + tc, j]
-        anchors, data = oracle.stream_encode(ot, kv, l, j, q, x)
-        assert np.array_equal(bv.anchors[kv, l, :, c], anchors), (ch, kv, l, c)
-        n = int(bv.lengths[kv, l, c])
-        assert oracle.stream_bytes(bv, kv, l, c)[: 4 * n] == data, (ch, kv, l, c)
-        y, bad = oracle.stream_decode(ot, kv, l, j, q, anchors, tc, data)
-        assert not bad
-        got = (ko, vo)[kv][l, t0:t0 + tc, c].cpu().numpy()
-        assert gu.same_bits(got, y), (ch, kv, l, c)
-    log(f"[{w.name}] {len(chunks)} sampled streams equal")
-
-
 @pytest.mark.timeout(1200)
-def test_llama34b_80k_sampled():
+def test_llama34b_80k_full():
     """16 GB of K/V, 54 chunks at quality M, everything on the GPU in the
-    benchmark's launch configuration; sampled against the oracle."""
-    w = synth.workload("llama34b_80k")
-    t0 = time.time()
-    k, v = synth.gen_kv(w)
-    log(f"[{w.name}] generated {k.shape} x2 in {time.time() - t0:.1f}s")
-    kd, vd = gu.to_dev(k), gu.to_dev(v)
-    tab = gu.gpu_tables(w, kd, vd)
-    jobs = [(ch, 1) for ch in range(w.n_chunks)]
-    blobs = encode_all_gpu(tab, kd, vd, jobs)
-    ko, vo = decode_selection_gpu(tab, blobs, k.shape)
-    del kd, vd
-    log(f"[{w.name}] encoded and decoded {len(blobs)} chunks, "
-        f"ratio {w.elements / sum(b.numel() for b in blobs):.3f}")
-    check_sampled(w, k, v, tab, blobs, ko, vo, [1] * w.n_chunks, np.random.default_rng(34))
+    benchmark's launch configuration: tables, all 54 blobs and the whole decoded
+    tensor bit-identical to the oracle's."""
+    full_parity("llama34b_80k")
 
 
 @pytest.mark.timeout(900)
 def test_llama70b_16k_streamed():
     """11 chunks at the seeded H/M/L schedule, blobs in pinned host memory,
-    decoded chunk by chunk with copies and decodes on two streams; equal to the
-    one-call decode from device memory and to the oracle on sampled streams."""
+    decoded chunk by chunk with copies and decodes on two streams: tables and
+    all 11 blobs equal the oracle's, the streamed decode equals the one-call
+    decode from device memory and the oracle's decode of the same blobs."""
     import kv_cache_compression_anchor_amd as cg
     t = gu.torch()
     w = synth.workload("llama70b_16k")
     k, v = synth.gen_kv(w)
     kd, vd = gu.to_dev(k), gu.to_dev(v)
     tab = gu.gpu_tables(w, kd, vd)
+    ot = oracle.build_tables(oracle.params_for(w), k, v, threads=16)
+    gt = cg.cg_tables_serialize(tab)
+    assert gt == ot, ("tables differ", gu.first_difference(gt, ot))
+    log(f"[{w.name}] tables equal ({len(ot)} B)")
     sched = list(w.selection())
     blobs = encode_all_gpu(tab, kd, vd, list(enumerate(sched)))
     del kd, vd
+    for ch, (b, q) in enumerate(zip(blobs, sched)):
+        ob = oracle.encode_chunk(ot, k, v, ch, q, threads=16)
+        gb = b.cpu().numpy().tobytes()
+        assert gb == ob, ("blob differs", ch, q, gu.first_difference(gb, ob))
+    log(f"[{w.name}] {len(blobs)} blobs equal")
     host = [b.cpu().pin_memory() for b in blobs]
     infos = [cg.cg_chunk_info_parse(h[:64]) for h in host]
     ko = t.empty((w.layers, w.tokens, w.channels), dtype=t.float16, device="cuda")
@@ -175,4 +127,8 @@ def test_llama70b_16k_streamed():
     k2, v2 = decode_selection_gpu(tab, blobs, ko.shape)
     assert t.equal(ko.view(t.int16), k2.view(t.int16)) and t.equal(vo.view(t.int16), v2.view(t.int16))
     log(f"[{w.name}] streamed decode equals the one-call decode")
-    check_sampled(w, k, v, tab, blobs, ko, vo, sched, np.random.default_rng(70))
+    del k2, v2
+    rk, rv, bad = gu.oracle_decode(ot, [b.cpu().numpy().tobytes() for b in blobs], k.shape)
+    assert not bad
+    assert gu.same_bits(ko.cpu().numpy(), rk) and gu.same_bits(vo.cpu().numpy(), rv)
+    log(f"[{w.name}] streamed decode equals the oracle's")
