@@ -170,8 +170,8 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
   // decoder state: ncode = ~code; range; bb = the next bits of the stream,
   // complemented, in its low `left` bits (most significant first, 32..64 of
   // them before every pair of symbols).  Words 0..2 start the state; words 3..
-  // reach bb through the wave's LDS ring: word 3 + i sits in slot i mod 8 of
-  // the lane's column, fetched 16 bytes at a time one group ahead of use.
+  // reach bb through the wave's LDS ring: word 3 + i sits in slot i mod 2 RB of
+  // the lane's column, fetched RB words at a time one group ahead of use.
   const uint32_t sbase = ch.off_pay + 4u * start;  // byte offset of word 0
   uint32_t ncode = ~ld32(rs, sbase);
   uint64_t bb = ((uint64_t)~ld32(rs, sbase + 4u) << 32) | ~ld32(rs, sbase + 8u);
