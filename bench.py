@@ -51,6 +51,10 @@ def parse():
                     help="measure the bandwidth-adaptive version choice instead: every chunk of "
                          "the workload encoded at H, M and L, streamed over a simulated "
                          "fluctuating link; SLO violation rates, adaptive vs fixed versions")
+    ap.add_argument("--grouping", action="store_true",
+                    help="measure what per-(layer, channel) symbol statistics are worth instead: "
+                         "coded size of every chunk and quality with tables pooled per layer, "
+                         "per channel and globally, and with tables profiled on another context")
     ap.add_argument("--contexts", type=int, default=2000,
                     help="contexts streamed per policy in --adaptive")
     ap.add_argument("--streamed", action="store_true",
@@ -87,6 +91,9 @@ def main():
 
     if args.adaptive:
         adaptive(args)
+        return
+    if args.grouping:
+        grouping(args)
         return
     if args.streamed:
         streamed(args)
@@ -260,6 +267,67 @@ def stream_context_lib(sizes, decode_ms, slo_ms, send, prior_bpms, policy="adapt
         decoded = max(decoded, t) + float(decode_ms[c][q])
         versions.append(q)
     return decoded, versions
+
+
+def grouping(args):
+    """Table granularity (CacheGen blog, section 1: symbol probabilities counted
+    per layer-channel combination): every chunk of the workload encoded at every
+    quality with tables pooled per (layer, channel), per layer, per channel and
+    globally (cg_build_tables_grouped), and with per-(layer, channel) tables
+    profiled on another context of the same synthetic model (same channel
+    scales, another token sequence); total coded bytes of each, on the GPU."""
+    import torch
+
+    import kv_cache_compression_anchor_amd as cg
+    import synth
+    w = synth.workload(args.workload)
+    k, v = synth.gen_kv(w)
+    kd, vd = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+    p = cg.make_params(w.layers, w.tokens, w.channels, w.chunk_tokens, w.group_tokens,
+                       w.layer_group_end, w.layer_step, w.quality_mult, w.quality_mask)
+    jobs = [(c, q) for c in range(w.n_chunks) for q in w.qualities]
+    tab0 = cg.cg_build_tables(p, kd, vd)
+    outs = [torch.empty(cg.cg_encode_bound(tab0, c), dtype=torch.uint8, device="cuda")
+            for c, q in jobs]
+    del tab0
+
+    def coded(tab):
+        lens = cg.cg_encode_batch(tab, kd, vd, [c for c, q in jobs], [q for c, q in jobs], outs)
+        by_q = {n: sum(b for (c, q), b in zip(jobs, lens) if q == i) for i, n in enumerate("HML")
+                if i in w.qualities}
+        return int(sum(lens)), by_q
+
+    names = {cg.CG_GROUP_LAYER_CHANNEL: "layer_channel", cg.CG_GROUP_LAYER: "layer",
+             cg.CG_GROUP_CHANNEL: "channel", cg.CG_GROUP_GLOBAL: "global"}
+    res = {}
+    for g, name in names.items():
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        tab = cg.cg_build_tables_grouped(p, g, kd, vd)
+        build_ms = (time.perf_counter() - t0) * 1e3
+        total, by_q = coded(tab)
+        res[name] = {"bytes": total, "bytes_by_quality": by_q, "build_ms": round(build_ms, 3)}
+    ko, vo = synth.gen_kv(w, context=1)
+    other = cg.cg_build_tables(p, torch.from_numpy(ko).cuda(), torch.from_numpy(vo).cuda())
+    total, by_q = coded(other)
+    res["layer_channel_other_context"] = {"bytes": total, "bytes_by_quality": by_q}
+    base = res["layer_channel"]["bytes"]
+    for r in res.values():
+        r["vs_layer_channel"] = round(r["bytes"] / base, 4)
+        r["bits_per_element"] = round(8 * r["bytes"] / (w.elements * len(w.qualities)), 4)
+    line = {
+        "metric": "coded size with per-(layer, channel) tables vs pooled tables",
+        "value": round(res["global"]["bytes"] / base - 1.0, 4),
+        "unit": "extra coded bytes with one global table, fraction",
+        "n_gpus": 1,
+        "higher_is_better": None,
+        "vs_baseline": None,
+        "data": "synthetic K/V (synth); other context: synth context=1 (same channel scales)",
+        "config": {"workload": w.name, "chunks": w.n_chunks,
+                   "qualities": "".join("HML"[q] for q in w.qualities)},
+        "results": res,
+    }
+    print(json.dumps(line), flush=True)
 
 
 def adaptive(args):

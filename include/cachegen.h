@@ -93,6 +93,26 @@ typedef struct cg_tables cg_tables; /* opaque, library-owned */
 int cg_build_tables(const cg_params* params, const void* k_dev, const void* v_dev,
                     void* stream, cg_tables** out);
 
+/* Table groupings: which (kv, quality, layer, channel) tables share pooled
+ * symbol statistics.  CG_GROUP_LAYER_CHANNEL (one table per layer and channel,
+ * the pages' choice: CacheGen blog, section 1) is what cg_build_tables builds;
+ * the coarser ones exist to measure what that choice is worth. */
+enum {
+  CG_GROUP_LAYER_CHANNEL = 0, /* per (kv, quality, layer, channel) */
+  CG_GROUP_LAYER = 1,         /* counts pooled over the channels of a layer */
+  CG_GROUP_CHANNEL = 2,       /* counts pooled over the layers of a channel */
+  CG_GROUP_GLOBAL = 3         /* counts pooled over all layers and channels */
+};
+
+/* cg_build_tables with the delta-symbol counts pooled over a coarser group
+ * before they are turned into frequency tables: every table of a group is then
+ * the group's table (scales and steps stay per layer and channel, and the
+ * tables keep their layout, so encoding and decoding are unchanged).
+ * CG_E_INVAL also for an unknown grouping and for a pooled count of one symbol
+ * that does not fit 32 bits. */
+int cg_build_tables_grouped(const cg_params* params, int32_t grouping, const void* k_dev,
+                            const void* v_dev, void* stream, cg_tables** out);
+
 /* Releases a handle and its device memory (NULL is allowed).  The caller makes
  * sure no enqueued work still uses it. */
 void cg_tables_free(cg_tables* tables);

@@ -17,11 +17,12 @@ LIB_PATH = os.path.join(HERE, "libcachegen.so")
 CG_OK, CG_E_INVAL, CG_E_NOMEM, CG_E_HIP, CG_E_CORRUPT, CG_E_CAPACITY, CG_E_MISMATCH = (
     0, -1, -2, -3, -4, -5, -6)
 CG_Q_H, CG_Q_M, CG_Q_L = 0, 1, 2
+CG_GROUP_LAYER_CHANNEL, CG_GROUP_LAYER, CG_GROUP_CHANNEL, CG_GROUP_GLOBAL = 0, 1, 2, 3
 _NAMES = {0: "CG_OK", -1: "CG_E_INVAL", -2: "CG_E_NOMEM", -3: "CG_E_HIP", -4: "CG_E_CORRUPT",
           -5: "CG_E_CAPACITY", -6: "CG_E_MISMATCH"}
 
-EXPORTS = ["cg_build_tables", "cg_tables_free", "cg_tables_serialize", "cg_tables_deserialize",
-           "cg_tables_id", "cg_tables_params", "cg_num_chunks", "cg_encode_bound", "cg_encode",
+EXPORTS = ["cg_build_tables", "cg_build_tables_grouped", "cg_tables_free", "cg_tables_serialize",
+           "cg_tables_deserialize", "cg_tables_id", "cg_tables_params", "cg_num_chunks", "cg_encode_bound", "cg_encode",
            "cg_encode_batch", "cg_chunk_info_parse", "cg_decode", "cg_decode_async", "cg_decode_streamed",
            "cg_plan_chunk", "cg_last_error"]
 
@@ -67,6 +68,7 @@ def lib():
         P, SZ, I, I32 = C.c_void_p, C.c_size_t, C.c_int, C.c_int32
         sigs = {
             "cg_build_tables": (I, [C.POINTER(cg_params), P, P, P, C.POINTER(P)]),
+            "cg_build_tables_grouped": (I, [C.POINTER(cg_params), I32, P, P, P, C.POINTER(P)]),
             "cg_tables_free": (None, [P]),
             "cg_tables_serialize": (I, [P, P, SZ, C.POINTER(SZ)]),
             "cg_tables_deserialize": (I, [P, SZ, C.POINTER(P)]),
@@ -172,6 +174,19 @@ def cg_build_tables(params: cg_params, k, v, stream=None) -> Tables:
         raise ValueError(f"k and v must both be {want}")
     out = C.c_void_p()
     _check(lib().cg_build_tables(C.byref(params), kp, vp, _stream(stream), C.byref(out)))
+    return Tables(out.value)
+
+
+def cg_build_tables_grouped(params: cg_params, grouping: int, k, v, stream=None) -> Tables:
+    import torch
+    kp = _dev_ptr(k, torch.float16, "k")
+    vp = _dev_ptr(v, torch.float16, "v")
+    want = (params.layers, params.tokens, params.channels)
+    if tuple(k.shape) != want or tuple(v.shape) != want:
+        raise ValueError(f"k and v must both be {want}")
+    out = C.c_void_p()
+    _check(lib().cg_build_tables_grouped(C.byref(params), int(grouping), kp, vp, _stream(stream),
+                                         C.byref(out)))
     return Tables(out.value)
 
 

@@ -388,8 +388,15 @@ int cg_plan_chunk(const cg_chunk_plan_in* in, int32_t* quality_out, double* rati
 
 int cg_build_tables(const cg_params* params, const void* k_dev, const void* v_dev, void* stream,
                     cg_tables** out) {
+  return cg_build_tables_grouped(params, CG_GROUP_LAYER_CHANNEL, k_dev, v_dev, stream, out);
+}
+
+int cg_build_tables_grouped(const cg_params* params, int32_t grouping, const void* k_dev,
+                            const void* v_dev, void* stream, cg_tables** out) {
   int rc = check_params(params);
   if (rc) return rc;
+  if (grouping < CG_GROUP_LAYER_CHANNEL || grouping > CG_GROUP_GLOBAL)
+    return fail(CG_E_INVAL, "unknown table grouping");
   if (!k_dev || !v_dev || !out) return fail(CG_E_INVAL, "NULL argument");
   *out = nullptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -408,17 +415,19 @@ int cg_build_tables(const cg_params* params, const void* k_dev, const void* v_de
   }
   const size_t n = t.lay.n;
   const size_t counts_words = (size_t)n * t.lay.nq * kNSym;
-  // workspace: [s1 | sa | sc] u64, amax u32, 4 flag words (the last two hold
-  // the tables id), counts; then the id digests
-  const size_t tmp_bytes = 3 * 8 * n + 4 * n + 16 + 4 * counts_words;
+  // workspace: [s1 | sa | sc] u64, amax u32, 8 flag words (2 and 3 hold the
+  // tables id), counts; then the id digests, then pooled counts
+  const size_t tmp_bytes = 3 * 8 * n + 4 * n + 32 + 4 * counts_words;
   const size_t dig_off = align256(tmp_bytes);
+  const size_t pool_off = align256(dig_off + id_digest_bytes(t));
+  const size_t pool_bytes = grouping ? 4 * pooled_words(t, grouping) : 0;
   BuildWs* ws = build_ws(h->dev);
   if (!ws) {
     free_tables(h);
     return fail(CG_E_INVAL, "device index beyond the supported range");
   }
   std::lock_guard<std::mutex> lock(ws->mu);
-  if ((rc = reserve_ws(ws, dig_off + id_digest_bytes(t)))) {
+  if ((rc = reserve_ws(ws, pool_off + pool_bytes))) {
     free_tables(h);
     return rc;
   }
@@ -430,8 +439,9 @@ int cg_build_tables(const cg_params* params, const void* k_dev, const void* v_de
   sb.amax = reinterpret_cast<uint32_t*>(sb.sc + n);
   sb.flags = sb.amax + n;
   uint64_t* id_dev = reinterpret_cast<uint64_t*>(sb.flags + 2);
-  uint32_t* counts = sb.flags + 4;
+  uint32_t* counts = sb.flags + 8;
   uint64_t* dig = reinterpret_cast<uint64_t*>(tmp + dig_off);
+  uint32_t* pooled = reinterpret_cast<uint32_t*>(tmp + pool_off);
   uint8_t hdr[kTabHdr];
   write_header(hdr, *params);
   const uint16_t* k = static_cast<const uint16_t*>(k_dev);
@@ -443,11 +453,12 @@ int cg_build_tables(const cg_params* params, const void* k_dev, const void* v_de
   if (e == hipSuccess) e = launch_finalize(*params, sb, t, st);
   if (e == hipSuccess) e = launch_histogram(k, 0, t, counts, st);
   if (e == hipSuccess) e = launch_histogram(v, 1, t, counts, st);
+  if (e == hipSuccess && grouping) e = launch_pool(t, counts, grouping, pooled, sb.flags + 4, st);
   if (e == hipSuccess) e = launch_normalize(t, counts, st);
   if (e == hipSuccess) e = launch_images(t, st);
   // the id of whatever was built; discarded below when the build failed
   if (e == hipSuccess) e = launch_tables_id(t, dig, id_dev, st);
-  if (e == hipSuccess) e = hipMemcpyAsync(ws->host, sb.flags, 16, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(ws->host, sb.flags, 32, hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) {
     free_tables(h);
@@ -460,6 +471,10 @@ int cg_build_tables(const cg_params* params, const void* k_dev, const void* v_de
   if (ws->host[1]) {
     free_tables(h);
     return fail(CG_E_INVAL, "a delta step is not a normal binary32 value");
+  }
+  if (ws->host[4]) {
+    free_tables(h);
+    return fail(CG_E_INVAL, "a pooled symbol count does not fit 32 bits");
   }
   memcpy(&h->id, ws->host + 2, 8);
   *out = h;

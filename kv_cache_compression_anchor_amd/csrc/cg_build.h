@@ -37,7 +37,8 @@ struct StatsBuf {
   uint64_t* sa;    // sum over workgroups of (their sum of X^2) >> 40
   uint64_t* sc;    // sum over workgroups of (their sum of X^2) mod 2^40
   uint32_t* amax;  // max |x| as binary16 magnitude bits
-  uint32_t* flags; // [0]: non-finite input, [1]: degenerate step
+  uint32_t* flags; // [0]: non-finite input, [1]: degenerate step, [2..3]: tables id,
+                   // [4]: pooled count too large
 };
 
 hipError_t launch_stats(const uint16_t* x, int kv, int L, int T, int C, const StatsBuf& sb,
@@ -46,6 +47,12 @@ hipError_t launch_finalize(const cg_params& p, const StatsBuf& sb, DevTables& t,
 hipError_t launch_histogram(const uint16_t* x, int kv, const DevTables& t, uint32_t* counts,
                             hipStream_t st);
 hipError_t launch_normalize(const DevTables& t, const uint32_t* counts, hipStream_t st);
+// pooled counts for a coarser table grouping (1 per layer, 2 per channel, 3 per
+// (kv, quality)); pooled needs pooled_words() words; sets *overflow if a
+// pooled count does not fit 32 bits
+size_t pooled_words(const DevTables& t, int grouping);
+hipError_t launch_pool(const DevTables& t, uint32_t* counts, int grouping, uint32_t* pooled,
+                       uint32_t* overflow, hipStream_t st);
 hipError_t launch_images(DevTables& t, hipStream_t st);
 // digests the tables id needs: leaves, then middle digests
 inline size_t id_leaves(size_t bytes) { return (bytes + kIdLeaf - 1) / kIdLeaf; }

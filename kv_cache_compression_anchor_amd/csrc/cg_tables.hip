@@ -305,6 +305,50 @@ __global__ __launch_bounds__(256) void k_normalize(NormArgs a) {
   out[k] = (uint16_t)f;
 }
 
+// Pooled symbol statistics (a coarser grouping than per layer and channel):
+// grouping 1 sums the counts of a (kv, quality, layer) over its channels, 2 of
+// a (kv, quality, channel) over its layers, 3 of a (kv, quality) over both;
+// every member then takes the pooled counts, so its frequency table is the
+// group's.  One thread per (kv, quality, group, symbol); a sum that does not
+// fit 32 bits sets *overflow.
+__global__ __launch_bounds__(256) void k_pool_sum(const uint32_t* counts, int L, int C, int nq,
+                                                  int grouping, uint32_t* pooled,
+                                                  uint32_t* overflow) {
+  const int G = grouping == 1 ? L : grouping == 2 ? C : 1;
+  const size_t n = (size_t)2 * nq * G * kNSym;
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int sym = (int)(i % kNSym);
+  const int g = (int)((i / kNSym) % G);
+  const size_t ks = i / ((size_t)kNSym * G);  // kv * nq + slot
+  const uint32_t* base = counts + ks * L * C * kNSym + sym;
+  uint64_t sum = 0;
+  if (grouping == 1) {
+    for (int c = 0; c < C; c++) sum += base[((size_t)g * C + c) * kNSym];
+  } else if (grouping == 2) {
+    for (int l = 0; l < L; l++) sum += base[((size_t)l * C + g) * kNSym];
+  } else {
+    for (size_t j = 0; j < (size_t)L * C; j++) sum += base[j * kNSym];
+  }
+  if (sum > 0xFFFFFFFFull) atomicOr(overflow, 1u);
+  pooled[i] = (uint32_t)sum;
+}
+
+__global__ __launch_bounds__(256) void k_pool_broadcast(uint32_t* counts, int L, int C, int nq,
+                                                        int grouping, const uint32_t* pooled) {
+  const int G = grouping == 1 ? L : grouping == 2 ? C : 1;
+  const size_t n = (size_t)2 * nq * L * C * kNSym;
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int sym = (int)(i % kNSym);
+  const size_t tab = i / kNSym;  // ((kv * nq + slot) * L + l) * C + c
+  const int c = (int)(tab % C);
+  const int l = (int)((tab / C) % L);
+  const size_t ks = tab / ((size_t)L * C);
+  const int g = grouping == 1 ? l : grouping == 2 ? c : 0;
+  counts[i] = pooled[(ks * G + g) * kNSym + sym];
+}
+
 struct ImgArgs {
   const uint8_t* ser;
   uint16_t* img[3];
@@ -483,6 +527,22 @@ hipError_t launch_normalize(const DevTables& t, const uint32_t* counts, hipStrea
   }
   const size_t ntab = (size_t)2 * a.nq * t.L * t.C;
   k_normalize<<<blocks_for(ntab * kLanes, 256), 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+size_t pooled_words(const DevTables& t, int grouping) {
+  const int G = grouping == 1 ? t.L : grouping == 2 ? t.C : 1;
+  return (size_t)2 * t.lay.nq * G * kNSym;
+}
+
+hipError_t launch_pool(const DevTables& t, uint32_t* counts, int grouping, uint32_t* pooled,
+                       uint32_t* overflow, hipStream_t st) {
+  const size_t np = pooled_words(t, grouping);
+  k_pool_sum<<<blocks_for(np, 256), 256, 0, st>>>(counts, t.L, t.C, t.lay.nq, grouping, pooled,
+                                                  overflow);
+  const size_t n = (size_t)2 * t.lay.nq * t.L * t.C * kNSym;
+  k_pool_broadcast<<<blocks_for(n, 256), 256, 0, st>>>(counts, t.L, t.C, t.lay.nq, grouping,
+                                                       pooled);
   return hipGetLastError();
 }
 

@@ -75,6 +75,7 @@ def lib():
             "cgo_rc_encode": (I, [P, I64, P, I, P, SZ, C.POINTER(SZ)]),
             "cgo_rc_decode": (I, [P, SZ, I64, P, I, P, C.POINTER(SZ), C.POINTER(I)]),
             "cgo_normalize": (None, [P, I, P]),
+            "cgo_normalize_tables": (None, [P, C.c_int64, P]),
             "cgo_channel_stats": (None, [P, I, I, I, P, P, C.POINTER(I)]),
             "cgo_tables_size": (SZ, [C.POINTER(cgo_params)]),
             "cgo_build_tables": (I, [C.POINTER(cgo_params), P, P, I, P, SZ, C.POINTER(SZ), P]),
@@ -167,6 +168,14 @@ def normalize(counts) -> np.ndarray:
     return f
 
 
+def normalize_tables(counts) -> np.ndarray:
+    """One 64-entry frequency table per row of counts [..., 64]."""
+    c = np.ascontiguousarray(counts, dtype=np.uint32)
+    f = np.zeros(c.shape, np.uint16)
+    lib().cgo_normalize_tables(_ptr(c), c.size // NSYM, _ptr(f))
+    return f
+
+
 # --------------------------------------------------------------------------- #
 # statistics, tables, chunks                                                  #
 # --------------------------------------------------------------------------- #
@@ -216,6 +225,43 @@ def build_tables(p: cgo_params, k: np.ndarray, v: np.ndarray, threads: Optional[
                                   _ptr(counts) if with_counts else None), "build_tables")
     t = out.tobytes()
     return (t, counts) if with_counts else t
+
+
+GROUP_LAYER_CHANNEL, GROUP_LAYER, GROUP_CHANNEL, GROUP_GLOBAL = 0, 1, 2, 3
+
+
+def pool_counts(counts: np.ndarray, grouping: int) -> np.ndarray:
+    """Symbol counts [nq, 2, L, C, 64] pooled over a coarser group and handed back
+    to every member: 1 sums over the channels of a layer, 2 over the layers of a
+    channel, 3 over both (per kv and quality).  A pooled count must fit 32 bits."""
+    c = counts.astype(np.uint64)
+    if grouping == GROUP_LAYER_CHANNEL:
+        pooled = c
+    elif grouping == GROUP_LAYER:
+        pooled = c.sum(axis=3, keepdims=True)
+    elif grouping == GROUP_CHANNEL:
+        pooled = c.sum(axis=2, keepdims=True)
+    elif grouping == GROUP_GLOBAL:
+        pooled = c.sum(axis=(2, 3), keepdims=True)
+    else:
+        raise ValueError("unknown grouping")
+    if pooled.max(initial=0) > 0xFFFFFFFF:
+        raise ValueError("a pooled symbol count does not fit 32 bits")
+    return np.broadcast_to(pooled, counts.shape).astype(np.uint32)
+
+
+def build_tables_grouped(p: cgo_params, k: np.ndarray, v: np.ndarray, grouping: int,
+                         threads: Optional[int] = None) -> bytes:
+    """Tables whose frequency tables come from counts pooled by ``grouping``
+    (scales and steps stay per layer and channel): the per-(layer, channel)
+    counts, pooled, each member's table normalised from the pooled counts."""
+    t, counts = build_tables(p, k, v, threads=threads, with_counts=True)
+    pooled = pool_counts(counts, grouping)
+    buf = bytearray(t)
+    tv = tables_view(buf)
+    for i, q in enumerate(q for q in range(3) if (p.quality_mask >> q) & 1):
+        tv.freq[q][...] = normalize_tables(pooled[i])
+    return bytes(buf)
 
 
 def fnv1a64(data: bytes) -> int:

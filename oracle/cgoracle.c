@@ -222,6 +222,11 @@ void cgo_normalize(const uint32_t* counts, int nsym, uint16_t* freq) {
   freq[best] = (uint16_t)(freq[best] + (PTOT - total));
 }
 
+/* ntab consecutive tables of NSYM counts each */
+void cgo_normalize_tables(const uint32_t* counts, int64_t ntab, uint16_t* freq) {
+  for (int64_t i = 0; i < ntab; i++) cgo_normalize(counts + i * NSYM, NSYM, freq + i * NSYM);
+}
+
 /* ------------------------------------------------------------------------- */
 /* Channel statistics                                                         */
 /* ------------------------------------------------------------------------- */

@@ -51,6 +51,7 @@ int cgo_rc_encode(const uint8_t* sym, int64_t n, const uint16_t* freq, int nsym,
 int cgo_rc_decode(const uint8_t* buf, size_t buflen, int64_t n, const uint16_t* freq,
                   int nsym, uint8_t* sym, size_t* consumed, int* corrupt);
 void cgo_normalize(const uint32_t* counts, int nsym, uint16_t* freq);
+void cgo_normalize_tables(const uint32_t* counts, int64_t ntab, uint16_t* freq);
 
 /* per (l, c) statistics of one [L][T][C] fp16 tensor */
 void cgo_channel_stats(const uint16_t* x, int L, int T, int C, double* sigma,

@@ -132,8 +132,13 @@ def quality_schedule(w: Workload) -> np.ndarray:
 
 
 def gen_row(seed: int, kv: int, layer: int, tokens: int, channels: int, rho: float,
-            outlier_frac: float, out: Optional[np.ndarray] = None) -> np.ndarray:
-    """One [tokens, channels] fp16 slice (kv, layer) of the synthetic cache."""
+            outlier_frac: float, out: Optional[np.ndarray] = None,
+            context: Optional[int] = None) -> np.ndarray:
+    """One [tokens, channels] fp16 slice (kv, layer) of the synthetic cache.
+
+    ``context`` draws the token sequence from its own stream,
+    ``PCG64(SeedSequence([seed, kv, layer, context]))``, keeping the channel
+    scales and outliers of ``seed``: another context of the same model."""
     from scipy.signal import lfilter
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, kv, layer])))
     scale = np.exp(0.5 * rng.standard_normal(channels))
@@ -141,6 +146,8 @@ def gen_row(seed: int, kv: int, layer: int, tokens: int, channels: int, rho: flo
     if n_out > 0:
         perm = rng.permutation(channels)[:n_out]
         scale[perm] *= 8.0
+    if context is not None:
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, kv, layer, context])))
     drive = np.empty((tokens, channels), dtype=np.float64)
     drive[0] = rng.standard_normal(channels) / math.sqrt(1.0 - rho * rho)
     if tokens > 1:
@@ -156,10 +163,11 @@ def gen_row(seed: int, kv: int, layer: int, tokens: int, channels: int, rho: flo
 
 def gen_kv(w: Workload, out_k: Optional[np.ndarray] = None,
            out_v: Optional[np.ndarray] = None, layers: Optional[Sequence[int]] = None,
-           threads: Optional[int] = None):
+           threads: Optional[int] = None, context: Optional[int] = None):
     """K and V, each [layers, tokens, channels] fp16, written into out_k / out_v if given.
 
-    ``layers`` restricts generation to some layers (others are left untouched).
+    ``layers`` restricts generation to some layers (others are left untouched);
+    ``context`` gives another context of the same model (see gen_row).
     Rows are generated in parallel; each row has its own seeded stream, so the
     result does not depend on the thread count.
     """
@@ -174,7 +182,8 @@ def gen_kv(w: Workload, out_k: Optional[np.ndarray] = None,
 
     def one(item):
         kv, l = item
-        gen_row(w.seed, kv, l, T, C, float(rhos[l]), w.outlier_frac, out=outs[kv][l])
+        gen_row(w.seed, kv, l, T, C, float(rhos[l]), w.outlier_frac, out=outs[kv][l],
+                context=context)
 
     n = threads or min(16, os.cpu_count() or 1)
     if n <= 1 or len(todo) <= 1:
