@@ -2,15 +2,15 @@
  * cachegen.h — C ABI of the MI355X (gfx950) KV-cache codec library libcachegen.so.
  *
  * The codec follows CacheGen (arXiv 2310.07240):
- *   - the encoder turns a KV cache into a compact bitstream
- *     (gptget abstract; CacheGen blog, section 2.1 "compress_kv_cache(kv_tensor)
- *     -> bitstream");
+ *   - the encoder turns a KV cache into a compact bitstream (gptget abstract;
+ *     CacheGen blog, section 2.1 pseudocode: a function from a KV tensor to a
+ *     bitstream);
  *   - tokens are coded as deltas against an 8-bit anchor token, one anchor per
- *     group of ten (CacheGen blog, section 2.1 pseudocode; sciencestack TL;DR
- *     "token-wise locality");
+ *     group of ten (CacheGen blog, section 2.1 pseudocode; sciencestack TL;DR on
+ *     the locality of neighbouring tokens);
  *   - the delta step depends on the layer group, 0.5 / 1.0 / 1.5 channel stds for
  *     shallow / medium / deep layers (CacheGen blog, sections 1 and 2.1;
- *     sciencestack "layer-sensitive quantization");
+ *     sciencestack TL;DR on quantisation that depends on the layer);
  *   - the symbols are arithmetic-coded with probability tables kept per
  *     (layer, channel) (CacheGen blog, section 1; sciencestack Figure 5);
  *   - the context is cut into 1.5K-token chunks, each pre-encoded at quality
@@ -22,8 +22,11 @@
  *
  * Memory ownership: every pointer argument is owned by the caller, except the
  * cg_tables handle, which the library allocates (device copies of the tables,
- * encode scratch) and cg_tables_free releases.  Device buffers passed to an
- * *_async / streamed call must stay valid until the stream has executed the work.
+ * encode scratch) and cg_tables_free releases.  Building tables also uses one
+ * workspace per device (statistics, symbol counts, digests; it grows to the
+ * largest build and is kept until the process ends; builds on one device take
+ * turns on it).  Device buffers passed to an *_async / streamed call must stay
+ * valid until the stream has executed the work.
  *
  * Streams: a `void* stream` is a hipStream_t (NULL = the legacy default stream).
  * A handle is used on the device that built or deserialized it; the library
