@@ -1,8 +1,8 @@
 """Seeded synthetic K/V tensors shaped like the workloads the CacheGen pages evaluate.
 
 The pages measure on real KV caches of Llama-7B / Mistral-7B / Llama-34B / Llama-70B
-contexts drawn from LongChat, TriviaQA and NarrativeQA (CacheGen blog, section 3.1
-"实验设置与评估指标"; gptget summary, 实验设计).  None of those weights or datasets
+contexts drawn from LongChat, TriviaQA and NarrativeQA (CacheGen blog, section 3.1,
+experiment setup and metrics; gptget summary, experiment design).  None of those weights or datasets
 exist here, so every tensor is synthetic: per (kv, layer) an AR(1) process over
 tokens (token-wise locality, the property the method exploits — sciencestack TL;DR
 and CacheGen blog section 1) times a lognormal per-channel scale, with a few
