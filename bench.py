@@ -224,7 +224,7 @@ def main():
         "encode_GBps_fp16_in": round(nq * fp16_bytes / (enc_ms * 1e-3) / 1e9, 2),
         "build_tables_ms": round(build_ms, 3),
         "build_tables_GBps_fp16_in": round(fp16_bytes / (build_ms * 1e-3) / 1e9, 2),
-        "roofline": {"bound": "hbm", "kernel": "k_decode", "achieved": round(achieved, 2),
+        "roofline": {"bound": "hbm", "kernel": decode_kernel_name(sel), "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "copy_GBps": round(copy_gbps, 1), "frac_of_copy": round(achieved / copy_gbps, 4)},
@@ -523,6 +523,13 @@ DECODE_SOURCES = ["kv_cache_compression_anchor_amd/csrc/cg_decode.hip",
                   "kv_cache_compression_anchor_amd/csrc/cg_internal.h"]
 
 
+def decode_kernel_name(sel):
+    """The decoder kernel one cg_decode_async of the selection launches: the
+    LDS-window kernel when some quality holds several chunks (workgroups of
+    several chunks), else the register-buffer kernel."""
+    return "k_decode_win" if any(sel.count(q) > 1 for q in set(sel)) else "k_decode_reg"
+
+
 def decode_traffic(path, workload):
     """HBM bytes per decode launch from the committed FETCH_SIZE / WRITE_SIZE
     counter runs (scaled by the same counters on a plain copy of known size);
@@ -560,7 +567,7 @@ def record_traffic(path, workload, fetch_csv, write_csv, copy_fetch_csv, copy_wr
     WRITE_SIZE (KiB per dispatch, averaged over the decoder's dispatches), each
     scaled so that the same counter reads the true byte count of a plain copy
     (the largest copy dispatches of a --copy-calibration run)."""
-    dec = "void cg::(anonymous namespace)::k_decode<"
+    dec = "void cg::(anonymous namespace)::k_decode_"
     fk = list(_counter_per_dispatch(fetch_csv, dec).values())
     wk = list(_counter_per_dispatch(write_csv, dec).values())
     cf = list(_counter_per_dispatch(copy_fetch_csv, "__amd_rocclr_copyBuffer").values())
@@ -578,7 +585,7 @@ def record_traffic(path, workload, fetch_csv, write_csv, copy_fetch_csv, copy_wr
         rec = {}
     sha = decoder_source_sha256()
     if rec.get("kernel_source_sha256") != sha:
-        rec = {"kernel": "k_decode", "kernel_source_sha256": sha, "workloads": {}}
+        rec = {"kernel": "k_decode_win / k_decode_reg", "kernel_source_sha256": sha, "workloads": {}}
     rec["copy_calibration"] = {"bytes": copy_bytes, "fetch_kib": cf_kib, "write_kib": cw_kib,
                                "fetch_scale": fetch_scale, "write_scale": write_scale}
     rec.setdefault("workloads", {})[workload] = {

@@ -4,11 +4,27 @@
 // One lane per stream (kv, layer, channel), one wave per (chunk, kv), one
 // workgroup per (group of chunks with the same quality, layer, 64-channel
 // block): the workgroup stages the block's 2 x 64 cumulative tables (K and V)
-// in LDS once and every wave decodes its chunk's K or V streams against them.  All lanes of a wave sit on the same token,
-// so each reconstructed token row is one coalesced 128-byte store.  Blob bytes
-// are read through a buffer resource bounded by the blob size: a corrupt blob
-// reads zeros past its end instead of faulting.
+// in LDS once and every wave decodes its chunk's K or V streams against them.
+// All lanes of a wave sit on the same token, so each reconstructed token row is
+// one coalesced 128-byte store.  Blob bytes are read through a buffer resource
+// bounded by the blob size: a corrupt blob reads zeros past its end instead of
+// faulting.
+//
+// Two kernels differ only in how stream bits reach the code register:
+//  * k_decode_win (workgroups of several chunks): each lane's words go through
+//    an 8-word LDS ring and three symbols at a time take their bits from one
+//    64-bit window of it (two v_alignbit), shifted into the code a whole byte
+//    at a time with v_perm_b32;
+//  * k_decode_reg (one chunk per workgroup, where the LDS holds eight
+//    workgroups and so only a 4-word ring): a 64-bit register buffer refilled a
+//    word at a time from the ring.
+// Both level the waves' progress with s_setprio: a SIMD issues from its oldest
+// ready wave first, so waves dispatched later fall behind and finish with few
+// waves left to hide the LDS latency; a wave that has done more of its groups
+// steps its priority down.
 #include "cg_internal.h"
+
+#include <type_traits>
 
 namespace cg {
 namespace {
@@ -52,7 +68,7 @@ struct Block<4> {
   }
 };
 
-// The kernel's LDS is all dynamic, so it starts at LDS address 0: pointers are
+// The kernels' LDS is all dynamic, so it starts at LDS address 0: pointers are
 // formed from byte addresses directly (constant parts of an address then fold
 // into the instructions' offset fields).
 template <typename T>
@@ -62,20 +78,6 @@ __device__ __forceinline__ __attribute__((address_space(3))) T* lds_at(uint32_t 
 
 __device__ __forceinline__ uint32_t lds32(uint32_t addr) { return *lds_at<uint32_t>(addr); }
 __device__ __forceinline__ uint32_t lds16(uint32_t addr) { return *lds_at<uint16_t>(addr); }
-
-// a block's words into consecutive ring slots (slots are 256 bytes apart)
-__device__ __forceinline__ void lds_put(uint32_t lane_addr, uint32_t slot_off, const Block<2>& b) {
-  auto p = lds_at<uint32_t>(lane_addr + slot_off);
-  p[0] = b.v.x;
-  p[64] = b.v.y;
-}
-__device__ __forceinline__ void lds_put(uint32_t lane_addr, uint32_t slot_off, const Block<4>& b) {
-  auto p = lds_at<uint32_t>(lane_addr + slot_off);
-  p[0] = b.v.x;
-  p[64] = b.v.y;
-  p[128] = b.v.z;
-  p[192] = b.v.w;
-}
 
 // (float)((x >> 8) & 0xFF) in one instruction
 __device__ __forceinline__ float byte1_to_float(uint32_t x) {
@@ -90,13 +92,7 @@ __device__ __forceinline__ float byte1_to_float(uint32_t x) {
 // k * 256 + (kv * 128 + 2 * slot) and bits 8..15 of it are k itself.
 constexpr uint32_t kRow = 4 * kLanes;
 constexpr uint32_t kTabBytes = kImgRows * kRow;        // 16,640
-// A wave's word ring: 2 * RB slots (two blocks of RB words) x 64 lanes x 4 B.
-// The first wave's ring is aligned to the ring size, so a slot address is the
-// lane's ring address with the slot number in the bits above 7.
-__host__ __device__ constexpr uint32_t ring_bytes(int rb) { return 2u * rb * 4u * kLanes; }
-__host__ __device__ constexpr uint32_t ring_base(int rb) {
-  return (kTabBytes + ring_bytes(rb) - 1) / ring_bytes(rb) * ring_bytes(rb);
-}
+constexpr uint32_t kSlot = 4 * kLanes;                 // a ring slot: one word per lane
 
 // All ones when r * key <= code, else zero.  ncode is ~code, so the 64-bit sum
 // r * key + (2^64 - code - 1) stays within [2^64 - 2^32, 2^64) when
@@ -107,16 +103,48 @@ __device__ __forceinline__ uint32_t le_mask(uint32_t r, uint32_t key, uint32_t n
   return (uint32_t)(((uint64_t)r * key + c) >> 32);
 }
 
-// GS: group size fixed at compile time (0 = the runtime a.G only).
-// RB: words per fetched block (4 in workgroups of several chunks; 2 when a
-// workgroup holds one chunk, so that eight of them fit a CU's LDS).
-template <int GS, int RB>
-__global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
-  // LDS: the tables at 0 ([65 rows][K: 64 u16 | V: 64 u16]), then one word
-  // ring per wave ([2 RB slots][64 lanes] u32)
+// One symbol's search and interval update.  Returns the LDS address of
+// cum[s] (bits 8..13 are s); leaves ncode = ~(code - r cum[s]) and range =
+// r freq[s] shifted left by sh bits, sh = 0, 8 or 16 (whole bytes until range
+// >= 2^24; r freq >= 2^9), and the caller shifts sh stream bits into ncode.
+__device__ __forceinline__ uint32_t search(uint32_t& ncode, uint32_t& range, uint32_t& sh,
+                                           uint32_t lane_addr, uint32_t key32) {
+  const uint32_t r = range >> kProbBits;
+  // largest s with r * cum[s] <= code, as the LDS address of cum[s]
+  uint32_t ad = lane_addr | (le_mask(r, key32, ncode) & (32u * kRow));
+#pragma unroll
+  for (uint32_t stp = 16; stp; stp >>= 1) ad |= le_mask(r, lds16(ad + stp * kRow), ncode) & (stp * kRow);
+  const uint32_t c0 = lds16(ad), c1 = lds16(ad + kRow);
+  ncode += mul24(r, c0);  // code -= r * cum[s]
+  const uint32_t rn = mul24(r, c1 - c0);
+  sh = (uint32_t)__builtin_clz(rn) & 24u;
+  range = rn << sh;
+  return ad;
+}
+
+// v_perm_b32 selector that picks the high word of {hi:lo} << sh (sh = 0, 8, 16
+// or 24): byte i of the result is byte i + 4 - sh / 8 of the pair
+__device__ __forceinline__ uint32_t shift_sel(uint32_t sh) {
+  return (uint32_t)((0x0706050403020100ull << sh) >> 32);
+}
+
+// Per-lane state both kernels set up the same way.
+struct Lane {
+  __amdgpu_buffer_rsrc_t rs, ro;
+  uint32_t sbase;      // byte offset of the stream's word 0 in the blob
+  uint32_t bad;        // stream extends past the payload
+  float scale_a, step;
+  uint32_t lane_addr;  // LDS address of the lane's cum[0]
+  uint32_t key32;      // cum[32], the root of every search
+  uint32_t row_bytes, lane_off, anc_base;
+  int C;
+  DecChunk ch;
+};
+
+// Stages the tables and sets up the lane; false for a lane without a stream.
+__device__ __forceinline__ bool setup(const DecodeArgs& a, int wave, int lane, Lane& s) {
   auto tab = lds_at<uint32_t>(0);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tid = threadIdx.x;
   const int per_grp = a.L * a.nblk;
   const int grp = blockIdx.x / per_grp, rem = blockIdx.x % per_grp;
   const int l = rem / a.nblk, cb = rem % a.nblk;
@@ -135,91 +163,277 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
   __syncthreads();
   const int kv = wave & 1;
   const int ci = a.groups[grp].chunk[wave >> 1];
-  if (ci < 0) return;
-  const DecChunk ch = a.chunks[ci];
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)ch.blob, 0, (int)ch.blob_bytes, kBufRsrcWord3);
+  if (ci < 0) return false;
+  s.ch = a.chunks[ci];
+  s.rs = __builtin_amdgcn_make_buffer_rsrc((void*)s.ch.blob, 0, (int)s.ch.blob_bytes, kBufRsrcWord3);
   const int row = kv * a.L + l;
-
   const int c = cb * kLanes + lane;
   const bool active = c < a.C;
 
   // start of this lane's stream: row offset + lengths of the streams before it
   // (the whole wave takes part in the prefix sums)
-  const uint32_t len_base = ch.off_len + 2u * (uint32_t)row * (uint32_t)a.C;
+  const uint32_t len_base = s.ch.off_len + 2u * (uint32_t)row * (uint32_t)a.C;
   uint32_t before = 0;
-  for (int j = lane; j < cb * kLanes; j += kLanes) before += ld16(rs, len_base + 2u * j);
+  for (int j = lane; j < cb * kLanes; j += kLanes) before += ld16(s.rs, len_base + 2u * j);
   for (int o = 32; o; o >>= 1) before += __shfl_xor(before, o);
-  const uint32_t my_len = active ? ld16(rs, len_base + 2u * c) : 0u;
+  const uint32_t my_len = active ? ld16(s.rs, len_base + 2u * c) : 0u;
   uint32_t incl = my_len;
   for (int o = 1; o < 64; o <<= 1) {
     const uint32_t y = __shfl_up(incl, o);
     if (lane >= o) incl += y;
   }
-  if (!active) return;  // no cross-lane work below
-  const uint32_t start = ld32(rs, 64u + 4u * row) + before + incl - my_len;
-  uint32_t bad = ((uint64_t)start + my_len > ch.W) ? 1u : 0u;
+  if (!active) return false;  // no cross-lane work after this
+  const uint32_t start = ld32(s.rs, 64u + 4u * row) + before + incl - my_len;
+  s.bad = ((uint64_t)start + my_len > s.ch.W) ? 1u : 0u;
+  s.sbase = s.ch.off_pay + 4u * start;
 
   const size_t pi = (size_t)row * a.C + c;
-  const float scale_a = a.scale_a[pi];
-  const float step = a.step[q][pi];
+  s.scale_a = a.scale_a[pi];
+  s.step = a.step[q][pi];
+  s.lane_addr = (uint32_t)kv * (2u * kLanes) + 2u * lane_slot(lane);
+  s.key32 = lds16(s.lane_addr + 32u * kRow);
 
-  const uint32_t lane_addr = (uint32_t)kv * (2u * kLanes) + 2u * lane_slot(lane);
-  const uint32_t key32 = lds16(lane_addr + 32u * kRow);  // root of the search
+  // output rows of this (kv, layer, chunk) through a buffer resource: the lane's
+  // channel is the vector offset, the token row a wave-uniform scalar offset
+  uint16_t* const out_base = (kv ? a.v_out : a.k_out) + ((size_t)l * a.T + s.ch.t0) * a.C;
+  s.ro = __builtin_amdgcn_make_buffer_rsrc(out_base, 0, (int)((uint32_t)s.ch.tc * (uint32_t)a.C * 2u),
+                                           kBufRsrcWord3);
+  s.row_bytes = 2u * (uint32_t)a.C;
+  s.lane_off = 2u * (uint32_t)c;
+  s.anc_base = s.ch.off_anchor + (uint32_t)row * (uint32_t)s.ch.ng * (uint32_t)a.C + c;
+  s.C = a.C;
+  return true;
+}
+
+__device__ __forceinline__ void put_half(const Lane& s, float y, uint32_t t) {
+  __builtin_amdgcn_raw_buffer_store_b16(float_to_half_bits(y), s.ro, s.lane_off, t * s.row_bytes, kStoreNT);
+}
+
+// ---------------------------------------------------------------------------
+// LDS-window kernel.  Per lane, ring word k (stream word 1 + k) sits,
+// complemented, in slot 2 + M - (k mod 8) (M = 7: later words in lower slots)
+// and slots 1 and 0 repeat the words with k mod 8 = 0 and 1, so words j, j + 1,
+// j + 2 are always the three consecutive slots s + 2, s + 1, s with
+// s = M - (j mod 8).  Blocks of four words land once per group, fetched one
+// group ahead.
+constexpr int kWinRB = 4;
+constexpr uint32_t kWinM = 2u * kWinRB - 1u;
+__host__ __device__ constexpr uint32_t win_ring_bytes() { return (2u * kWinRB + 2u) * kSlot; }
+
+// a block's words, complemented, into their slots; first = the ring index of
+// its first word (a multiple of 4)
+__device__ __forceinline__ void win_put(uint32_t ring, uint32_t first, const Block<kWinRB>& b) {
+  const uint32_t top = 2u + kWinM - (first & kWinM);  // slot of the block's first word
+  auto p = lds_at<uint32_t>(ring + (top - (kWinRB - 1u)) * kSlot);
+  const uint32_t w0 = ~b.v.x, w1 = ~b.v.y, w2 = ~b.v.z, w3 = ~b.v.w;
+  p[3 * kLanes] = w0;
+  p[2 * kLanes] = w1;
+  p[kLanes] = w2;
+  p[0] = w3;
+  if ((first & kWinM) == 0) {
+    auto m = lds_at<uint32_t>(ring);
+    m[kLanes] = w0;
+    m[0] = w1;
+  }
+}
+
+template <int GS>
+__global__ __launch_bounds__(512) void k_decode_win(DecodeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  Lane s;
+  if (!setup(a, wave, lane, s)) return;
+  constexpr int RB = kWinRB;
+  constexpr uint32_t M = kWinM;
+
+  // decoder state: ncode = ~code, range, and nc = -(stream bits shifted into
+  // the code after its first word)
+  uint32_t ncode = ~ld32(s.rs, s.sbase);
+  uint32_t range = 0xFFFFFFFFu;
+  uint32_t nc = 0;
+  const uint32_t ring = kTabBytes + (uint32_t)wave * win_ring_bytes() + 4u * (uint32_t)lane;
+  uint32_t landed = 2u * RB;                   // ring words 0 .. landed - 1 have been written
+  int lim = 64 - 32 * (int)landed;             // nc < lim: a window's words are not all landed
+  uint32_t fetch_off = s.sbase + 4u + 8u * RB;  // the next block
+  {
+    const Block<RB> b0 = Block<RB>::load(s.rs, s.sbase + 4u);
+    const Block<RB> b1 = Block<RB>::load(s.rs, s.sbase + 4u + 4u * RB);
+    win_put(ring, 0u, b0);
+    win_put(ring, RB, b1);
+  }
+  Block<RB> pend = {};  // block in flight
+  bool inflight = false;
+  int anc_next = ld8s(s.rs, s.anc_base);
+
+  // one symbol, its new bits x (the next stream bits, most significant first);
+  // returns sh and the selector that shifted them in
+  auto symbol = [&](uint32_t t, float base, uint32_t x, uint32_t& sel) -> uint32_t {
+    uint32_t sh;
+    const uint32_t ad = search(ncode, range, sh, s.lane_addr, s.key32);
+    sel = shift_sel(sh);
+    ncode = __builtin_amdgcn_perm(ncode, x, sel);
+    put_half(s, __builtin_fmaf(byte1_to_float(ad), s.step, base), t);
+    return sh;
+  };
+
+  // N (1..3) symbols from one 64-bit window of the stream (they take at most
+  // 48 bits)
+  auto run = [&](auto n_c, uint32_t t, float base) {
+    constexpr int N = decltype(n_c)::value;
+    if ((int)nc < lim) {
+      // the ring has run dry (more bits taken than fetched, which typical data
+      // never does): the missing words straight from the blob
+      const uint32_t j = ~nc >> 5;
+#pragma unroll
+      for (uint32_t d = 0; d < 3; d++) {
+        const uint32_t k = j + d;
+        if (k >= landed) {
+          const uint32_t w = ~ld32(s.rs, s.sbase + 4u + 4u * k);
+          const uint32_t sl = k & M;
+          *lds_at<uint32_t>(ring + (2u + M - sl) * kSlot) = w;
+          if (sl < 2u) *lds_at<uint32_t>(ring + (1u - sl) * kSlot) = w;
+        }
+      }
+    }
+    // words j, j + 1, j + 2 with j = ceil(bits / 32) - 1: the window starts
+    // (-bits) mod 32 bits into word j
+    const uint32_t ba = ring + __builtin_amdgcn_ubfe(nc, 5u, 3u) * kSlot;
+    const uint32_t w0 = lds32(ba + 2u * kSlot), w1 = lds32(ba + kSlot), w2 = lds32(ba);
+    const uint32_t hi = __builtin_amdgcn_alignbit(w0, w1, nc);
+    const uint32_t lo = __builtin_amdgcn_alignbit(w1, w2, nc);
+    uint32_t sel1, sel2, sel3;
+    uint32_t tot = symbol(t, base, hi, sel1);
+    if constexpr (N >= 2) {
+      const uint64_t win = (((uint64_t)hi << 32) | lo) << tot;
+      const uint32_t h2 = (uint32_t)(win >> 32), l2 = (uint32_t)win;
+      const uint32_t sh2 = symbol(t + 1, base, h2, sel2);
+      tot += sh2;
+      if constexpr (N >= 3) tot += symbol(t + 2, base, __builtin_amdgcn_perm(h2, l2, sel2), sel3);
+    }
+    nc -= tot;
+  };
+
+  // once per group: write the block fetched one group earlier into the ring,
+  // then fetch the next one if the words it lands over are taken (lanes
+  // without room point their load past the blob end: no memory access)
+  auto ring_step = [&]() {
+    if (inflight) {
+      win_put(ring, landed, pend);
+      landed += RB;
+      lim -= 32 * RB;
+    }
+    inflight = (int)nc <= lim + 32 * RB - 64;
+    pend = Block<RB>::load(s.rs, inflight ? fetch_off : 0xFFFFFFF0u);
+    if (inflight) fetch_off += 4u * RB;
+  };
+
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  auto group = [&](int g, int ta, int te) {
+    ring_step();
+    const int anc = anc_next;
+    anc_next = ld8s(s.rs, s.anc_base + (uint32_t)(g + 1) * s.C);  // past the last group: unused
+    const float ahat = anchor_value(anc, s.scale_a);
+    put_half(s, ahat, (uint32_t)ta);
+    const float base = __builtin_fmaf(-32.0f, s.step, ahat);
+    int t = ta + 1;
+#pragma unroll
+    for (; t + 2 < te; t += 3) {
+      __builtin_amdgcn_sched_barrier(0);
+      run(I3{}, (uint32_t)t, base);
+    }
+    if (t + 1 < te) {
+      __builtin_amdgcn_sched_barrier(0);
+      run(I2{}, (uint32_t)t, base);
+    } else if (t < te) {
+      __builtin_amdgcn_sched_barrier(0);
+      run(I1{}, (uint32_t)t, base);
+    }
+  };
+
+  // everything loaded so far (scale, step, first words, first anchor) is in
+  // registers before the loop, so no wait inside it is for those loads
+  __builtin_amdgcn_s_waitcnt(0);
+  // Full groups of the compile-time size GS run the same unrolled code, and a
+  // wave's priority steps 3 -> 2 -> 1 -> 0 at half, three quarters and seven
+  // eighths of them; the rest (a last partial group, or every group when
+  // GS = 0) follow at the priority reached.
+  int g = 0;
+  if constexpr (GS > 0) {
+    const int nfull = s.ch.tc / GS;
+    const int q1 = nfull >> 1, q2 = nfull - (nfull >> 2), q3 = nfull - (nfull >> 3);
+    __builtin_amdgcn_s_setprio(3);
+    for (; g < nfull; g++) {
+      if (g == q1) __builtin_amdgcn_s_setprio(2);
+      if (g == q2) __builtin_amdgcn_s_setprio(1);
+      if (g == q3) __builtin_amdgcn_s_setprio(0);
+      group(g, g * GS, g * GS + GS);
+    }
+  }
+  for (; g < s.ch.ng; g++) group(g, g * a.G, min(g * a.G + a.G, s.ch.tc));
+  // a valid stream keeps code < range throughout; a corrupt one breaks it for good
+  s.bad |= (~ncode >= range) ? 1u : 0u;
+  if (s.bad) atomicOr(a.status, 1u);
+}
+
+// ---------------------------------------------------------------------------
+// Register-buffer kernel.  A wave's word ring: 4 slots x 64 lanes; the first
+// wave's ring is aligned to the ring size, so a slot address is the lane's ring
+// address with the slot number in the bits above 7.
+constexpr int kRegRB = 2;
+__host__ __device__ constexpr uint32_t reg_ring_bytes() { return 2u * kRegRB * kSlot; }
+__host__ __device__ constexpr uint32_t reg_ring_base() {
+  return (kTabBytes + reg_ring_bytes() - 1) / reg_ring_bytes() * reg_ring_bytes();
+}
+
+__device__ __forceinline__ void reg_put(uint32_t lane_addr, uint32_t slot_off, const Block<kRegRB>& b) {
+  auto p = lds_at<uint32_t>(lane_addr + slot_off);
+  p[0] = b.v.x;
+  p[64] = b.v.y;
+}
+
+template <int GS>
+__global__ __launch_bounds__(512) void k_decode_reg(DecodeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  Lane s;
+  if (!setup(a, wave, lane, s)) return;
+  constexpr int RB = kRegRB;
 
   // decoder state: ncode = ~code; range; bb = the next bits of the stream,
   // complemented, in its low `left` bits (most significant first, 32..64 of
   // them before every pair of symbols).  Words 0..2 start the state; words 3..
   // reach bb through the wave's LDS ring: word 3 + i sits in slot i mod 2 RB of
   // the lane's column, fetched RB words at a time one group ahead of use.
-  const uint32_t sbase = ch.off_pay + 4u * start;  // byte offset of word 0
-  uint32_t ncode = ~ld32(rs, sbase);
-  uint64_t bb = ((uint64_t)~ld32(rs, sbase + 4u) << 32) | ~ld32(rs, sbase + 8u);
+  uint32_t ncode = ~ld32(s.rs, s.sbase);
+  uint64_t bb = ((uint64_t)~ld32(s.rs, s.sbase + 4u) << 32) | ~ld32(s.rs, s.sbase + 8u);
   uint32_t left = 64;
   uint32_t range = 0xFFFFFFFFu;
   constexpr uint32_t kSlotMask = (2u * RB - 1u) << 8;
-  const uint32_t ring = ring_base(RB) + (uint32_t)wave * ring_bytes(RB) + 4u * (uint32_t)lane;
+  const uint32_t ring = reg_ring_base() + (uint32_t)wave * reg_ring_bytes() + 4u * (uint32_t)lane;
   // ring words taken and written, counted in units of 256 (one slot's size)
   uint32_t taken = 0;
   uint32_t landed = (2u * RB) << 8;                  // words 3 .. 2 RB + 2, written below
-  uint32_t fetch_off = sbase + 12u + 8u * RB;        // the next block
+  uint32_t fetch_off = s.sbase + 12u + 8u * RB;      // the next block
   {
-    const Block<RB> b0 = Block<RB>::load(rs, sbase + 12u);
-    const Block<RB> b1 = Block<RB>::load(rs, sbase + 12u + 4u * RB);
-    lds_put(ring, 0u, b0);
-    lds_put(ring, (uint32_t)RB << 8, b1);
+    const Block<RB> b0 = Block<RB>::load(s.rs, s.sbase + 12u);
+    const Block<RB> b1 = Block<RB>::load(s.rs, s.sbase + 12u + 4u * RB);
+    reg_put(ring, 0u, b0);
+    reg_put(ring, (uint32_t)RB << 8, b1);
   }
   Block<RB> pend = {};  // block in flight
   bool inflight = false;
-
-  // output rows of this (kv, layer, chunk) through a buffer resource: the lane's
-  // channel is the vector offset, the token row a wave-uniform scalar offset
-  uint16_t* const out_base = (kv ? a.v_out : a.k_out) + ((size_t)l * a.T + ch.t0) * a.C;
-  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-      out_base, 0, (int)((uint32_t)ch.tc * (uint32_t)a.C * 2u), kBufRsrcWord3);
-  const uint32_t row_bytes = 2u * (uint32_t)a.C;
-  const uint32_t lane_off = 2u * (uint32_t)c;
-  const uint32_t anc_base = ch.off_anchor + (uint32_t)row * (uint32_t)ch.ng * (uint32_t)a.C + c;
-  int anc_next = ld8s(rs, anc_base);
+  int anc_next = ld8s(s.rs, s.anc_base);
 
   // one symbol: search, interval update, renormalisation, reconstruction
-  auto symbol = [&](uint32_t soff, float base) {
-    const uint32_t r = range >> kProbBits;
-    // largest s with r * cum[s] <= code, as the LDS address of cum[s]
-    uint32_t ad = lane_addr | (le_mask(r, key32, ncode) & (32u * kRow));
-#pragma unroll
-    for (uint32_t stp = 16; stp; stp >>= 1) ad |= le_mask(r, lds16(ad + stp * kRow), ncode) & (stp * kRow);
-    const uint32_t c0 = lds16(ad), c1 = lds16(ad + kRow);
-    ncode += mul24(r, c0);  // code -= r * cum[s]
-    const uint32_t rn = mul24(r, c1 - c0);
-    // shift in whole bytes until range >= 2^24 (0, 1 or 2 bytes; rn >= 2^9)
-    const uint32_t sh = (uint32_t)__builtin_clz(rn) & 24u;
-    range = rn << sh;
-    const uint32_t t = left - sh;
-    ncode = (ncode << sh) | __builtin_amdgcn_ubfe((uint32_t)(bb >> (t & 63u)), 0u, sh);
-    left = t;
-    const float y = __builtin_fmaf(byte1_to_float(ad), step, base);
-    __builtin_amdgcn_raw_buffer_store_b16(float_to_half_bits(y), ro, lane_off, soff, kStoreNT);
+  auto symbol = [&](uint32_t t, float base) {
+    uint32_t sh;
+    const uint32_t ad = search(ncode, range, sh, s.lane_addr, s.key32);
+    const uint32_t tl = left - sh;
+    ncode = (ncode << sh) | __builtin_amdgcn_ubfe((uint32_t)(bb >> (tl & 63u)), 0u, sh);
+    left = tl;
+    put_half(s, __builtin_fmaf(byte1_to_float(ad), s.step, base), t);
   };
 
   // A lane takes a word when fewer than 32 bits remain (two symbols need at
@@ -230,7 +444,7 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
     const bool take = left < 32;
     const uint32_t slot = (taken & kSlotMask) | ring;
     if (take && taken >= landed)
-      *lds_at<uint32_t>(slot) = ld32(rs, sbase + 12u + (taken >> 6));
+      *lds_at<uint32_t>(slot) = ld32(s.rs, s.sbase + 12u + (taken >> 6));
     const uint32_t w = lds32(slot);
     if (take) {
       bb = (bb << 32) | ~w;
@@ -243,11 +457,11 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
   // without room point their load past the blob end: no memory access)
   auto ring_step = [&]() {
     if (inflight) {
-      lds_put(ring, landed & ((uint32_t)RB << 8), pend);
+      reg_put(ring, landed & ((uint32_t)RB << 8), pend);
       landed += (uint32_t)RB << 8;
     }
     inflight = landed + ((uint32_t)RB << 8) <= taken + ((2u * RB) << 8);
-    pend = Block<RB>::load(rs, inflight ? fetch_off : 0xFFFFFFF0u);
+    pend = Block<RB>::load(s.rs, inflight ? fetch_off : 0xFFFFFFF0u);
     if (inflight) fetch_off += 4u * RB;
   };
 
@@ -256,11 +470,10 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
   auto group = [&](int g, int ta, int te) {
     ring_step();
     const int anc = anc_next;
-    anc_next = ld8s(rs, anc_base + (uint32_t)(g + 1) * a.C);  // past the last group: unused
-    const float ahat = anchor_value(anc, scale_a);
-    __builtin_amdgcn_raw_buffer_store_b16(float_to_half_bits(ahat), ro, lane_off,
-                                          (uint32_t)ta * row_bytes, kStoreNT);
-    const float base = __builtin_fmaf(-32.0f, step, ahat);
+    anc_next = ld8s(s.rs, s.anc_base + (uint32_t)(g + 1) * s.C);  // past the last group: unused
+    const float ahat = anchor_value(anc, s.scale_a);
+    put_half(s, ahat, (uint32_t)ta);
+    const float base = __builtin_fmaf(-32.0f, s.step, ahat);
     int t = ta + 1;
 #pragma unroll
     for (; t + 1 < te; t += 2) {
@@ -268,31 +481,36 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
       // leaves those two stores in flight
       __builtin_amdgcn_sched_barrier(0);
       refill();
-      symbol((uint32_t)t * row_bytes, base);
-      symbol((uint32_t)(t + 1) * row_bytes, base);
+      symbol((uint32_t)t, base);
+      symbol((uint32_t)(t + 1), base);
     }
     if (t < te) {
       __builtin_amdgcn_sched_barrier(0);
       refill();
-      symbol((uint32_t)t * row_bytes, base);
+      symbol((uint32_t)t, base);
     }
   };
 
-  // everything loaded so far (scale, step, first words, first anchor) is in
-  // registers before the loop, so no wait inside it is for those loads
   __builtin_amdgcn_s_waitcnt(0);
+  // Full groups of the compile-time size GS run the same unrolled code, and a
+  // wave's priority steps 3 -> 2 -> 1 -> 0 at half, three quarters and seven
+  // eighths of them; the rest (a last partial group, or every group when
+  // GS = 0) follow at the priority reached.
   int g = 0;
   if constexpr (GS > 0) {
-    // full groups of the compile-time size: the same loads and stores every
-    // iteration, so the anchor loaded one group ahead is waited for without
-    // waiting for the stores issued since
-    const int nfull = ch.tc / GS;
-    for (; g < nfull; g++) group(g, g * GS, g * GS + GS);
+    const int nfull = s.ch.tc / GS;
+    const int q1 = nfull >> 1, q2 = nfull - (nfull >> 2), q3 = nfull - (nfull >> 3);
+    __builtin_amdgcn_s_setprio(3);
+    for (; g < nfull; g++) {
+      if (g == q1) __builtin_amdgcn_s_setprio(2);
+      if (g == q2) __builtin_amdgcn_s_setprio(1);
+      if (g == q3) __builtin_amdgcn_s_setprio(0);
+      group(g, g * GS, g * GS + GS);
+    }
   }
-  for (; g < ch.ng; g++) group(g, g * a.G, min(g * a.G + a.G, ch.tc));
-  // a valid stream keeps code < range throughout; a corrupt one breaks it for good
-  bad |= (~ncode >= range) ? 1u : 0u;
-  if (bad) atomicOr(a.status, 1u);
+  for (; g < s.ch.ng; g++) group(g, g * a.G, min(g * a.G + a.G, s.ch.tc));
+  s.bad |= (~ncode >= range) ? 1u : 0u;
+  if (s.bad) atomicOr(a.status, 1u);
 }
 
 }  // namespace
@@ -300,18 +518,18 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   const unsigned blocks = (unsigned)(a.n_groups * a.L * a.nblk);
   const dim3 grid(blocks), block(2 * kLanes * a.waves);
-  if (a.waves == 1) {  // one chunk per workgroup: small rings
-    const size_t lds = ring_base(2) + (size_t)2 * a.waves * ring_bytes(2);
+  if (a.waves == 1) {  // one chunk per workgroup: small rings, eight workgroups per CU
+    const size_t lds = reg_ring_base() + (size_t)2 * reg_ring_bytes();
     if (a.G == 10)
-      k_decode<10, 2><<<grid, block, lds, st>>>(a);
+      k_decode_reg<10><<<grid, block, lds, st>>>(a);
     else
-      k_decode<0, 2><<<grid, block, lds, st>>>(a);
+      k_decode_reg<0><<<grid, block, lds, st>>>(a);
   } else {
-    const size_t lds = ring_base(4) + (size_t)2 * a.waves * ring_bytes(4);
+    const size_t lds = kTabBytes + (size_t)2 * a.waves * win_ring_bytes();
     if (a.G == 10)
-      k_decode<10, 4><<<grid, block, lds, st>>>(a);
+      k_decode_win<10><<<grid, block, lds, st>>>(a);
     else
-      k_decode<0, 4><<<grid, block, lds, st>>>(a);
+      k_decode_win<0><<<grid, block, lds, st>>>(a);
   }
   return hipGetLastError();
 }

@@ -11,7 +11,7 @@ import pytest
 import bench
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-DEC = "void cg::(anonymous namespace)::k_decode<10, 4>(cg::DecodeArgs)"
+DEC = "void cg::(anonymous namespace)::k_decode_win<10>(cg::DecodeArgs)"
 ENC = "void cg::(anonymous namespace)::k_encode<10>(cg::EncodeArgs)"
 COPY = "__amd_rocclr_copyBuffer"
 
@@ -53,6 +53,12 @@ def test_traffic_is_dropped_when_the_decoder_changes(tmp_path):
                "workloads": {"wl": {"bytes_per_launch": 1}}}, open(out, "w"))
     assert bench.decode_traffic(str(out), "wl") is None
     assert bench.decode_traffic(str(tmp_path / "missing.json"), "wl") is None
+
+
+def test_decoder_kernel_name():
+    assert bench.decode_kernel_name((0, 1, 2, 0, 1, 2)) == "k_decode_win"
+    assert bench.decode_kernel_name((0,)) == "k_decode_reg"
+    assert bench.decode_kernel_name((0, 1, 2)) == "k_decode_reg"
 
 
 def test_more_than_one_gpu_is_refused():
