@@ -599,6 +599,17 @@ int cg_encode_bound(const cg_tables* h, int32_t chunk, size_t* max_bytes) {
 // Scratch memory the encoder may hold: the blobs of one launch share it.
 constexpr size_t kEncScratchBudget = (size_t)3 << 30;
 
+// Waves the device can hold at once: compute units x threads per compute unit
+// / 64 (the encoder's VGPR and LDS use leave this bound the binding one).
+size_t resident_waves(int dev) {
+  int cus = 0, threads = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&threads, hipDeviceAttributeMaxThreadsPerMultiProcessor, dev) != hipSuccess ||
+      cus <= 0 || threads <= 0)
+    return (size_t)1 << 30;  // unknown: no cap from this bound
+  return (size_t)cus * (size_t)threads / kLanes;
+}
+
 int cg_encode_batch(const cg_tables* ch, const void* k_dev, const void* v_dev, int32_t n,
                     const int32_t* chunks, const int32_t* qualities, void* const* outs_dev,
                     const size_t* caps, size_t* out_lens, void* stream) {
@@ -623,8 +634,17 @@ int cg_encode_batch(const cg_tables* ch, const void* k_dev, const void* v_dev, i
   // a stream's words plus the placeholder word in front of them
   const size_t swb = std::max<size_t>(stream_words_bound(t.CH - (t.CH + t.G - 1) / t.G), 1) + 1;
   const size_t slot_words = (size_t)2 * t.L * t.nblk * kLanes * swb;  // whole 64-stream blocks
-  const int slots = (int)std::max<size_t>(
+  // Blobs per launch: at most what the scratch budget holds.  When one more
+  // launch is enough to make every launch fit the device at once (a blob is
+  // 2 L nblk waves), take that, so that no second round of a few waves per
+  // SIMD trails a launch and the waves' progress can be levelled.
+  const size_t cap = resident_waves(h->dev);
+  const size_t wpb = (size_t)2 * t.L * t.nblk;
+  const size_t budget = std::max<size_t>(
       1, std::min<size_t>({(size_t)kEncMaxBlobs, (size_t)n, kEncScratchBudget / (4 * slot_words)}));
+  const size_t fit = std::max<size_t>(1, std::min(budget, cap / wpb));
+  const bool one_round = (n + fit - 1) / fit <= (n + budget - 1) / budget + 1;
+  const int slots = (int)(one_round ? fit : budget);
   if (h->enc_slots < slots) {
     if (h->scratch) (void)hipFree(h->scratch);
     if (h->lens) (void)hipFree(h->lens);
@@ -670,6 +690,7 @@ int cg_encode_batch(const cg_tables* ch, const void* k_dev, const void* v_dev, i
     a.G = t.G;
     a.nblk = t.nblk;
     a.nblobs = std::min(per_launch, n - i0);
+    a.prio = (size_t)a.nblobs * wpb <= cap ? 1 : 0;
     a.swb = swb;
     a.scale_a = reinterpret_cast<const float*>(t.ser + t.lay.off_scale_a);
     a.inv_a = reinterpret_cast<const float*>(t.ser + t.lay.off_inv_a);

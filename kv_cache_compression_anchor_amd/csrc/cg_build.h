@@ -82,6 +82,7 @@ struct EncodeArgs {
   const uint16_t* v;
   int L, T, C, G, nblk, nblobs;
   int n_groups, waves;  // workgroups per (kv, layer, block) and their widest group
+  int prio;             // 1: the launch's waves are all resident at once; level their progress
   size_t swb;
   const float* scale_a;
   const float* inv_a;

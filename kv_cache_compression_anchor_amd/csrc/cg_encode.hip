@@ -240,7 +240,20 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
     };
     load(xa, 0);
     load(xb, 1);
+    // In a launch whose waves are all resident at once, waves that have done
+    // less run first: a SIMD issues from its oldest ready wave, so otherwise
+    // the last-dispatched waves run last with few waves left beside them.
+    // Each wave steps its priority down at half, three quarters and seven
+    // eighths of its pairs of groups.  (In a launch of several rounds of waves
+    // the oldest-first order lets the next round start sooner, so it is kept.)
+    const bool prio = a.prio != 0;
+    const int np = nfull >> 1;
+    const int p1 = np >> 1, p2 = np - (np >> 2), p3 = np - (np >> 3);
+    if (prio) __builtin_amdgcn_s_setprio(3);
     for (; g + 2 <= nfull; g += 2) {
+      if (prio && (g >> 1) == p1) __builtin_amdgcn_s_setprio(2);
+      if (prio && (g >> 1) == p2) __builtin_amdgcn_s_setprio(1);
+      if (prio && (g >> 1) == p3) __builtin_amdgcn_s_setprio(0);
       code_group(g, GS, [&](int j) { return xa[j]; });
       load(xa, g + 2);
       code_group(g + 1, GS, [&](int j) { return xb[j]; });

@@ -1,11 +1,12 @@
 """Decoding is a pure function of the blobs and tables: the same selection
 decoded several times in a row, into fresh buffers, gives bitwise the same K and
-V every time and never flags a stream.  Run at full size on both decoder
-kernels: the register-buffer one (one chunk per workgroup, Llama-7B shape) and
-the LDS-window one (several chunks of a quality per workgroup, the Mistral-7B
-9K selection).  Parity of the values themselves with the oracle is the subject
-of the full-size test; this one catches a decoder whose result changes from
-run to run, which a single comparison can miss."""
+V every time and never flags a stream; encoding the chunks twice gives the same
+blobs.  Run at full size on both decoder kernels: the register-buffer one (one
+chunk per workgroup, Llama-7B shape) and the LDS-window one (several chunks of
+a quality per workgroup, the Mistral-7B 9K selection).  Parity of the values
+themselves with the oracle is the subject of the full-size test; this one
+catches a kernel whose result changes from run to run, which a single
+comparison can miss."""
 import pytest
 
 import synth
@@ -28,6 +29,11 @@ def test_repeated_decodes_are_identical(name):
     outs = [t.empty(cg.cg_encode_bound(tab, c), dtype=t.uint8, device="cuda") for c in range(len(sel))]
     sizes = cg.cg_encode_batch(tab, kd, vd, list(range(len(sel))), list(sel), outs)
     blobs = [o[:n] for o, n in zip(outs, sizes)]
+    again = [t.empty(cg.cg_encode_bound(tab, c), dtype=t.uint8, device="cuda") for c in range(len(sel))]
+    sizes2 = cg.cg_encode_batch(tab, kd, vd, list(range(len(sel))), list(sel), again)
+    assert list(sizes2) == list(sizes)
+    for b, o, n in zip(blobs, again, sizes2):
+        assert t.equal(b, o[:n]), (name, "encode differs")
     infos = [cg.cg_chunk_info_parse(b[:64].cpu()) for b in blobs]
     first = None
     for rep in range(REPEATS):
