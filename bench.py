@@ -47,6 +47,11 @@ def parse():
                     help="write the --workload's record of --traffic-json from rocprofv3 --pmc "
                          "counter_collection.csv files (FETCH_SIZE and WRITE_SIZE of the decoder, "
                          "then of a --copy-calibration run); no GPU work")
+    ap.add_argument("--record-valu", nargs="+", metavar="CSV",
+                    help="write the --workload's VALU-issue record in --traffic-json from rocprofv3 "
+                         "--pmc counter_collection.csv files holding SQ_INSTS_VALU and "
+                         "GRBM_GUI_ACTIVE of the decoder, then the run's agent_info.csv (last "
+                         "argument); no GPU work")
     ap.add_argument("--adaptive", action="store_true",
                     help="measure the bandwidth-adaptive version choice instead: every chunk of "
                          "the workload encoded at H, M and L, streamed over a simulated "
@@ -67,6 +72,10 @@ def main():
     args = parse()
     if args.record_traffic:
         record_traffic(args.traffic_json, args.workload, *args.record_traffic)
+    if args.record_valu:
+        if len(args.record_valu) < 2:
+            raise SystemExit("--record-valu: counter files, then the agent_info.csv")
+        record_valu(args.traffic_json, args.workload, args.record_valu[:-1], args.record_valu[-1])
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -179,6 +188,12 @@ def main():
     ratio_q = {("HML"[q]): eight_bit / sum(sizes[(c, q)] for c in range(nch)) for q in w.qualities}
 
     traffic = decode_traffic(args.traffic_json, w.name)
+    # delta symbols per lane-wave of the decode launch: every chunk of the selection
+    wave_symbols = 0
+    for c in range(nch):
+        tc = min(w.chunk_tokens, w.tokens - c * w.chunk_tokens)
+        wave_symbols += 2 * w.layers * (tc - (tc + w.group_tokens - 1) // w.group_tokens) * w.channels // 64
+    valu = decode_valu(args.traffic_json, w.name, wave_symbols)
     # algorithmic bytes of the other two steps: every encoded blob reads its
     # chunk's fp16 K/V once and writes the blob; building reads K/V twice
     # (statistics, then the histogram)
@@ -227,7 +242,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": decode_kernel_name(sel), "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "copy_GBps": round(copy_gbps, 1), "frac_of_copy": round(achieved / copy_gbps, 4)},
+                     "copy_GBps": round(copy_gbps, 1), "frac_of_copy": round(achieved / copy_gbps, 4),
+                     "valu_issue": valu},
         "cpu_baseline": cpu,
         "encode_roofline": {"bound": "hbm", "kernel": "k_encode + k_pack (all 18 blobs)",
                             "achieved": round(enc_achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -543,6 +559,92 @@ def decode_traffic(path, workload):
         return None
 
 
+def _load_record(path):
+    """The counter record for the decoder source as it is now (a fresh one if
+    the file is missing or was taken on another version of the decoder)."""
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        rec = {}
+    sha = decoder_source_sha256()
+    if rec.get("kernel_source_sha256") != sha:
+        rec = {"kernel": "k_decode_win / k_decode_reg", "kernel_source_sha256": sha, "workloads": {}}
+    return rec
+
+
+def record_valu(path, workload, counter_csvs, agent_csv):
+    """Store the decoder's VALU issue for `workload`: SQ_INSTS_VALU and
+    GRBM_GUI_ACTIVE per decoder dispatch (averaged over its dispatches), the
+    dispatch's duration from its timestamps, and the device's SIMD and XCD
+    counts and peak engine clock from the agent file.  A wave64 VALU
+    instruction takes 4 cycles of its SIMD, so
+    busy = instructions x 4 / (SIMDs x GRBM cycles per XCD)."""
+    import csv
+    dec = "void cg::(anonymous namespace)::k_decode_"
+    per = {}   # (dispatch, counter) -> value
+    dur = {}   # dispatch -> ns
+    for p in counter_csvs:
+        with open(p, newline="") as f:
+            for r in csv.DictReader(f):
+                if not r["Kernel_Name"].startswith(dec):
+                    continue
+                d = int(r["Dispatch_Id"])
+                key = (d, r["Counter_Name"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+                dur[d] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+
+    def mean(name):
+        v = [x for (d, c), x in per.items() if c == name]
+        if not v:
+            raise SystemExit(f"record-valu: no {name} for the decoder in the counter files")
+        return sum(v) / len(v)
+
+    insts, grbm = mean("SQ_INSTS_VALU"), mean("GRBM_GUI_ACTIVE")
+    launch_ns = sum(dur.values()) / len(dur)
+    agent = None
+    with open(agent_csv, newline="") as f:
+        for r in csv.DictReader(f):
+            if int(r.get("Simd_Count") or 0) > 0:
+                agent = r
+                break
+    if agent is None:
+        raise SystemExit("record-valu: no GPU agent in the agent file")
+    simds, xcc = int(agent["Simd_Count"]), int(agent["Num_Xcc"])
+    peak_ghz = int(agent["Max_Engine_Clk_Fcompute"]) / 1000.0
+    cycles = grbm / xcc
+    rec = _load_record(path)
+    rec.setdefault("workloads", {}).setdefault(workload, {})["valu"] = {
+        "valu_insts_per_launch": insts,
+        "launch_ns": launch_ns,
+        "cycles_per_launch": cycles,
+        "simds": simds,
+        "busy_frac": insts * 4 / (simds * cycles),
+        "clock_GHz": cycles / launch_ns,
+        "peak_clock_GHz": peak_ghz,
+        "issue_frac_at_peak_clock": insts * 4 / (simds * peak_ghz * launch_ns),
+    }
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec["workloads"][workload]["valu"]))
+
+
+def decode_valu(path, workload, wave_symbols):
+    """The committed VALU-issue record of the decoder for `workload` (None when
+    there is none or the decoder changed since), with VALU instructions per
+    delta symbol of a lane for a launch of `wave_symbols` wave-symbols."""
+    try:
+        rec = json.load(open(path))
+        if rec.get("kernel_source_sha256") != decoder_source_sha256():
+            return None
+        v = dict(rec["workloads"][workload]["valu"])
+    except (OSError, ValueError, KeyError):
+        return None
+    out = {k: round(v[k], 4) for k in ("busy_frac", "clock_GHz", "peak_clock_GHz", "issue_frac_at_peak_clock")}
+    out["insts_per_symbol"] = round(v["valu_insts_per_launch"] / wave_symbols, 2) if wave_symbols else None
+    return out
+
+
 def decoder_source_sha256():
     import hashlib
     src = b"".join(open(os.path.join(ROOT, p), "rb").read() for p in DECODE_SOURCES)
@@ -579,21 +681,15 @@ def record_traffic(path, workload, fetch_csv, write_csv, copy_fetch_csv, copy_wr
     fetch_scale = copy_bytes / 1024 / cf_kib
     write_scale = copy_bytes / 1024 / cw_kib
     f_kib, w_kib = sum(fk) / len(fk), sum(wk) / len(wk)
-    try:
-        rec = json.load(open(path))
-    except (OSError, ValueError):
-        rec = {}
-    sha = decoder_source_sha256()
-    if rec.get("kernel_source_sha256") != sha:
-        rec = {"kernel": "k_decode_win / k_decode_reg", "kernel_source_sha256": sha, "workloads": {}}
+    rec = _load_record(path)
     rec["copy_calibration"] = {"bytes": copy_bytes, "fetch_kib": cf_kib, "write_kib": cw_kib,
                                "fetch_scale": fetch_scale, "write_scale": write_scale}
-    rec.setdefault("workloads", {})[workload] = {
+    rec.setdefault("workloads", {}).setdefault(workload, {}).update({
         "dispatches": len(fk),
         "fetch_kib_per_dispatch": f_kib,
         "write_kib_per_dispatch": w_kib,
         "bytes_per_launch": int(round(1024 * (f_kib * fetch_scale + w_kib * write_scale))),
-    }
+    })
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")

@@ -66,3 +66,44 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def _sq(path, rows):
+    """A counter_collection.csv with timestamps: rows are (dispatch id, kernel
+    name, counter, value, start ns, end ns)."""
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value",
+                    "Start_Timestamp", "End_Timestamp"])
+        for r in rows:
+            w.writerow(r)
+    return str(path)
+
+
+def test_record_then_read_valu(tmp_path):
+    # 2e8 VALU instructions over 1,024 SIMDs in 8e5 GRBM cycles per XCD (8 XCDs),
+    # in a launch of 400 us: busy = 2e8 * 4 / (1024 * 8e5), clock 2 GHz
+    sq1 = _sq(tmp_path / "s1.csv", [(3, DEC, "SQ_INSTS_VALU", 2e8, 1000, 401000),
+                                    (2, ENC, "SQ_INSTS_VALU", 9e9, 0, 5)])
+    sq2 = _sq(tmp_path / "s2.csv", [(3, DEC, "GRBM_GUI_ACTIVE", 6.4e6, 1000, 401000)])
+    agent = tmp_path / "agent.csv"
+    with open(agent, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Simd_Count", "Num_Xcc", "Max_Engine_Clk_Fcompute"])
+        w.writerow([0, 0, 0])          # a CPU agent
+        w.writerow([1024, 8, 2400])
+    out = tmp_path / "traffic.json"
+    bench.record_valu(str(out), "wl", [sq1, sq2], str(agent))
+    v = bench.decode_valu(str(out), "wl", 1e7)
+    assert v["busy_frac"] == pytest.approx(2e8 * 4 / (1024 * 8e5), abs=1e-4)
+    assert v["clock_GHz"] == pytest.approx(2.0)
+    assert v["issue_frac_at_peak_clock"] == pytest.approx(2e8 * 4 / (1024 * 2.4 * 4e5), abs=1e-4)
+    assert v["insts_per_symbol"] == 20.0
+    # a traffic record for the same workload keeps the VALU record beside it
+    fetch = _counters(tmp_path / "f.csv", [(7, DEC, 500.0)])
+    write = _counters(tmp_path / "w.csv", [(7, DEC, 1500.0)])
+    cf = _counters(tmp_path / "cf.csv", [(2, COPY, 524288.0)])
+    cw = _counters(tmp_path / "cw.csv", [(2, COPY, 1048576.0)])
+    bench.record_traffic(str(out), "wl", fetch, write, cf, cw)
+    assert bench.decode_valu(str(out), "wl", 1e7) is not None
+    assert bench.decode_traffic(str(out), "wl") == 1024 * 2500
