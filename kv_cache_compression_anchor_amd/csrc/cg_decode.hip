@@ -220,22 +220,25 @@ constexpr int kWinRB = 4;
 constexpr uint32_t kWinM = 2u * kWinRB - 1u;
 __host__ __device__ constexpr uint32_t win_ring_bytes() { return (2u * kWinRB + 2u) * kSlot; }
 
-// a block's words, complemented, into their slots; first = the ring index of
-// its first word (a multiple of 4)
-__device__ __forceinline__ void win_put(uint32_t ring, uint32_t first, const Block<kWinRB>& b) {
-  const uint32_t top = 2u + kWinM - (first & kWinM);  // slot of the block's first word
-  auto p = lds_at<uint32_t>(ring + (top - (kWinRB - 1u)) * kSlot);
+// a block's words, complemented, into their slots.  A block starts at a ring
+// index that is 0 or 4 mod 8, so it fills slots 6..9 ("high": its first two
+// words are also repeated in slots 1 and 0) or slots 2..5; at = the byte
+// address of its lowest slot.
+__device__ __forceinline__ void win_put(uint32_t ring, uint32_t at, bool high, const Block<kWinRB>& b) {
+  auto p = lds_at<uint32_t>(at);
   const uint32_t w0 = ~b.v.x, w1 = ~b.v.y, w2 = ~b.v.z, w3 = ~b.v.w;
   p[3 * kLanes] = w0;
   p[2 * kLanes] = w1;
   p[kLanes] = w2;
   p[0] = w3;
-  if ((first & kWinM) == 0) {
+  if (high) {
     auto m = lds_at<uint32_t>(ring);
     m[kLanes] = w0;
     m[0] = w1;
   }
 }
+constexpr uint32_t kWinHigh = (2u + kWinM - (kWinRB - 1u)) * kSlot;  // lowest slot of a high block
+constexpr uint32_t kWinLow = kWinHigh - kWinRB * kSlot;
 
 template <int GS>
 __global__ __launch_bounds__(512) void k_decode_win(DecodeArgs a) {
@@ -252,14 +255,19 @@ __global__ __launch_bounds__(512) void k_decode_win(DecodeArgs a) {
   uint32_t range = 0xFFFFFFFFu;
   uint32_t nc = 0;
   const uint32_t ring = kTabBytes + (uint32_t)wave * win_ring_bytes() + 4u * (uint32_t)lane;
-  uint32_t landed = 2u * RB;                   // ring words 0 .. landed - 1 have been written
-  int lim = 64 - 32 * (int)landed;             // nc < lim: a window's words are not all landed
-  uint32_t fetch_off = s.sbase + 4u + 8u * RB;  // the next block
+  // Ring words 0 .. n - 1 have been written, n = (64 - lim) / 32: nc < lim
+  // means a window's words have not all landed.  fetch_off = the blob offset of
+  // ring word n, where the next block starts; land = where it lands (the high
+  // and low halves alternate, so land toggles as flip - land).
+  int lim = 64 - 32 * (int)(2u * RB);
+  uint32_t fetch_off = s.sbase + 4u + 8u * RB;
+  const uint32_t flip = 2u * ring + kWinHigh + kWinLow;
+  uint32_t land = ring + kWinHigh;
   {
     const Block<RB> b0 = Block<RB>::load(s.rs, s.sbase + 4u);
     const Block<RB> b1 = Block<RB>::load(s.rs, s.sbase + 4u + 4u * RB);
-    win_put(ring, 0u, b0);
-    win_put(ring, RB, b1);
+    win_put(ring, ring + kWinHigh, true, b0);
+    win_put(ring, ring + kWinLow, false, b1);
   }
   Block<RB> pend = {};  // block in flight
   bool inflight = false;
@@ -284,6 +292,9 @@ __global__ __launch_bounds__(512) void k_decode_win(DecodeArgs a) {
       // the ring has run dry (more bits taken than fetched, which typical data
       // never does): the missing words straight from the blob
       const uint32_t j = ~nc >> 5;
+      int l = lim;
+      asm volatile("" : "+v"(l));  // computed here, not in every group
+      const uint32_t landed = (uint32_t)(64 - l) >> 5;
 #pragma unroll
       for (uint32_t d = 0; d < 3; d++) {
         const uint32_t k = j + d;
@@ -297,7 +308,9 @@ __global__ __launch_bounds__(512) void k_decode_win(DecodeArgs a) {
     }
     // words j, j + 1, j + 2 with j = ceil(bits / 32) - 1: the window starts
     // (-bits) mod 32 bits into word j
-    const uint32_t ba = ring + __builtin_amdgcn_ubfe(nc, 5u, 3u) * kSlot;
+    uint32_t sl = __builtin_amdgcn_ubfe(nc, 5u, 3u);
+    asm volatile("" : "+v"(sl));  // keeps the address one shift-add of the slot
+    const uint32_t ba = ring + (sl << 8);
     const uint32_t w0 = lds32(ba + 2u * kSlot), w1 = lds32(ba + kSlot), w2 = lds32(ba);
     const uint32_t hi = __builtin_amdgcn_alignbit(w0, w1, nc);
     const uint32_t lo = __builtin_amdgcn_alignbit(w1, w2, nc);
@@ -318,13 +331,13 @@ __global__ __launch_bounds__(512) void k_decode_win(DecodeArgs a) {
   // without room point their load past the blob end: no memory access)
   auto ring_step = [&]() {
     if (inflight) {
-      win_put(ring, landed, pend);
-      landed += RB;
+      win_put(ring, land, land == ring + kWinHigh, pend);
+      land = flip - land;
       lim -= 32 * RB;
+      fetch_off += 4u * RB;
     }
     inflight = (int)nc <= lim + 32 * RB - 64;
     pend = Block<RB>::load(s.rs, inflight ? fetch_off : 0xFFFFFFF0u);
-    if (inflight) fetch_off += 4u * RB;
   };
 
   using I1 = std::integral_constant<int, 1>;
@@ -335,8 +348,8 @@ __global__ __launch_bounds__(512) void k_decode_win(DecodeArgs a) {
     const int anc = anc_next;
     anc_next = ld8s(s.rs, s.anc_base + (uint32_t)(g + 1) * s.C);  // past the last group: unused
     const float ahat = anchor_value(anc, s.scale_a);
-    put_half(s, ahat, (uint32_t)ta);
     const float base = __builtin_fmaf(-32.0f, s.step, ahat);
+    put_half(s, ahat, (uint32_t)ta);
     int t = ta + 1;
 #pragma unroll
     for (; t + 2 < te; t += 3) {
