@@ -62,11 +62,14 @@ def test_selection_of_mixed_qualities_in_one_call():
     kd, vd = gu.to_dev(k), gu.to_dev(v)
     tab = gu.gpu_tables(w, kd, vd)
     import kv_cache_compression_anchor_amd as cg
-    ot = cg.cg_tables_serialize(tab)
+    ot = oracle.build_tables(oracle.params_for(w), k, v)
+    assert cg.cg_tables_serialize(tab) == ot
     sel = [(ch, (ch * 7) % 3) for ch in range(w.n_chunks)]
     dblobs, hblobs = zip(*[gu.gpu_encode(tab, kd, vd, ch, q) for ch, q in sel])
+    obs = [oracle.encode_chunk(ot, k, v, ch, q) for ch, q in sel]
+    assert list(hblobs) == obs
     kg, vg, st = gu.gpu_decode(tab, list(dblobs), k.shape)
-    ko, vo, bad = gu.oracle_decode(ot, hblobs, k.shape)
+    ko, vo, bad = gu.oracle_decode(ot, obs, k.shape)
     assert st == 0 and not bad
     assert gu.same_bits(kg, ko) and gu.same_bits(vg, vo)
     # and the synchronous entry point gives the same
@@ -93,10 +96,9 @@ def test_cross_decoding_both_ways():
         kg, vg, st = gu.gpu_decode(tab2, dev, k.shape)
         ko, vo, _ = gu.oracle_decode(ot, obs, k.shape)
         assert st == 0 and gu.same_bits(kg, ko) and gu.same_bits(vg, vo)
-        # GPU blobs decoded by the oracle
+        # and the GPU encodes exactly the oracle's blobs, which the oracle decodes
         gbs = [gu.gpu_encode(tab, kd, vd, ch, q)[1] for ch in range(w.n_chunks)]
-        ko2, vo2, bad = gu.oracle_decode(ot, gbs, k.shape)
-        assert not bad and gu.same_bits(ko2, ko) and gu.same_bits(vo2, vo)
+        assert gbs == obs
 
 
 @pytest.mark.parametrize("group_tokens", [10, 7])
@@ -133,6 +135,40 @@ def test_costly_symbols_drain_the_word_ring(group_tokens):
             ko, vo, bad = gu.oracle_decode(ot, [ob], k.shape)
             assert st == 0 and not bad
             assert gu.same_bits(kg, ko) and gu.same_bits(vg, vo), ("decode differs", ch, q)
+    # both chunks of a quality in one call: a workgroup of two chunks, the
+    # LDS-window decoder, whose ring these streams also outrun
+    for q in w.qualities:
+        dev = [gu.gpu_encode(tab, kd2, vd2, ch, q)[0] for ch in range(w.n_chunks)]
+        obs = [oracle.encode_chunk(ot, k2, v2, ch, q) for ch in range(w.n_chunks)]
+        kg, vg, st = gu.gpu_decode(tab, dev, k.shape)
+        ko, vo, bad = gu.oracle_decode(ot, obs, k.shape)
+        assert st == 0 and not bad
+        assert gu.same_bits(kg, ko) and gu.same_bits(vg, vo), ("window decode differs", q)
+
+
+@pytest.mark.parametrize("group_tokens", [1, 2, 3, 4, 7, 10, 13])
+def test_several_chunks_of_a_quality_every_group_size(group_tokens):
+    """All chunks of a quality decoded by one call (workgroups of several
+    chunks: the LDS-window decoder), for group sizes whose deltas split into
+    windows of 1, 2 and 3 symbols, a ragged last chunk and last group, and
+    channels that end inside a 64-channel block."""
+    w = gu.workload(layers=2, tokens=700, channels=100, chunk_tokens=128,
+                    group_tokens=group_tokens, layer_group_end=(1, 2), layer_step=(0.5, 1.5),
+                    qualities=(0, 2))
+    k, v = synth.gen_kv(w)
+    kd, vd = gu.to_dev(k), gu.to_dev(v)
+    tab = gu.gpu_tables(w, kd, vd)
+    import kv_cache_compression_anchor_amd as cg
+    ot = oracle.build_tables(oracle.params_for(w), k, v)
+    assert cg.cg_tables_serialize(tab) == ot
+    for q in w.qualities:
+        dev, host = zip(*[gu.gpu_encode(tab, kd, vd, ch, q) for ch in range(w.n_chunks)])
+        obs = [oracle.encode_chunk(ot, k, v, ch, q) for ch in range(w.n_chunks)]
+        assert list(host) == obs, ("blob differs", group_tokens, q)
+        kg, vg, st = gu.gpu_decode(tab, list(dev), k.shape)
+        ko, vo, bad = gu.oracle_decode(ot, obs, k.shape)
+        assert st == 0 and not bad
+        assert gu.same_bits(kg, ko) and gu.same_bits(vg, vo), ("decode differs", group_tokens, q)
 
 
 def test_degenerate_channels():
@@ -151,9 +187,10 @@ def test_degenerate_channels():
     ot = oracle.build_tables(oracle.params_for(w), k, v)
     assert cg.cg_tables_serialize(tab) == ot
     dblob, gb = gu.gpu_encode(tab, kd, vd, 0, 0)
-    assert gb == oracle.encode_chunk(ot, k, v, 0, 0)
+    ob = oracle.encode_chunk(ot, k, v, 0, 0)
+    assert gb == ob
     kg, vg, st = gu.gpu_decode(tab, [dblob], k.shape)
-    ko, vo, _ = gu.oracle_decode(ot, [gb], k.shape)
+    ko, vo, _ = gu.oracle_decode(ot, [ob], k.shape)
     assert st == 0 and gu.same_bits(kg, ko) and gu.same_bits(vg, vo)
 
 

@@ -52,15 +52,18 @@ def full_parity(name, threads=16):
     log(f"[{name}] tables equal ({len(ot)} B)")
     jobs = [(ch, q) for ch in range(w.n_chunks) for q in w.qualities]
     blobs = encode_all_gpu(tab, kd, vd, jobs)
+    sel = w.selection()
+    sel_obs = {}
     for (ch, q), b in zip(jobs, blobs):
         ob = oracle.encode_chunk(ot, k, v, ch, q, threads=threads)
         gb = b.cpu().numpy().tobytes()
         assert gb == ob, ("blob differs", ch, q, gu.first_difference(gb, ob))
+        if sel[ch] == q:
+            sel_obs[ch] = ob
     log(f"[{name}] {len(jobs)} blobs equal")
-    sel = w.selection()
     dsel = [blobs[jobs.index((ch, q))] for ch, q in enumerate(sel)]
     ko, vo = decode_selection_gpu(tab, dsel, k.shape)
-    rk, rv, bad = gu.oracle_decode(ot, [b.cpu().numpy().tobytes() for b in dsel], k.shape)
+    rk, rv, bad = gu.oracle_decode(ot, [sel_obs[ch] for ch in range(len(sel))], k.shape)
     assert not bad
     assert gu.same_bits(ko.cpu().numpy(), rk) and gu.same_bits(vo.cpu().numpy(), rv)
     log(f"[{name}] decoded selection equal")
@@ -109,10 +112,12 @@ def test_llama70b_16k_streamed():
     sched = list(w.selection())
     blobs = encode_all_gpu(tab, kd, vd, list(enumerate(sched)))
     del kd, vd
+    obs = []
     for ch, (b, q) in enumerate(zip(blobs, sched)):
         ob = oracle.encode_chunk(ot, k, v, ch, q, threads=16)
         gb = b.cpu().numpy().tobytes()
         assert gb == ob, ("blob differs", ch, q, gu.first_difference(gb, ob))
+        obs.append(ob)
     log(f"[{w.name}] {len(blobs)} blobs equal")
     host = [b.cpu().pin_memory() for b in blobs]
     infos = [cg.cg_chunk_info_parse(h[:64]) for h in host]
@@ -128,7 +133,7 @@ def test_llama70b_16k_streamed():
     assert t.equal(ko.view(t.int16), k2.view(t.int16)) and t.equal(vo.view(t.int16), v2.view(t.int16))
     log(f"[{w.name}] streamed decode equals the one-call decode")
     del k2, v2
-    rk, rv, bad = gu.oracle_decode(ot, [b.cpu().numpy().tobytes() for b in blobs], k.shape)
+    rk, rv, bad = gu.oracle_decode(ot, obs, k.shape)
     assert not bad
     assert gu.same_bits(ko.cpu().numpy(), rk) and gu.same_bits(vo.cpu().numpy(), rv)
     log(f"[{w.name}] streamed decode equals the oracle's")
