@@ -72,6 +72,7 @@ def main():
     args = parse()
     if args.record_traffic:
         record_traffic(args.traffic_json, args.workload, *args.record_traffic)
+        return
     if args.record_valu:
         if len(args.record_valu) < 2:
             raise SystemExit("--record-valu: counter files, then the agent_info.csv")
@@ -245,7 +246,7 @@ def main():
                      "copy_GBps": round(copy_gbps, 1), "frac_of_copy": round(achieved / copy_gbps, 4),
                      "valu_issue": valu},
         "cpu_baseline": cpu,
-        "encode_roofline": {"bound": "hbm", "kernel": "k_encode + k_pack (all 18 blobs)",
+        "encode_roofline": {"bound": "hbm", "kernel": f"k_encode + k_pack (all {len(sizes)} blobs)",
                             "achieved": round(enc_achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                             "frac": round(enc_achieved / HBM_PEAK_GBPS, 4)},
         "build_roofline": {"bound": "hbm", "kernel": "cg_build_tables (all kernels)",

@@ -107,3 +107,29 @@ def test_record_then_read_valu(tmp_path):
     bench.record_traffic(str(out), "wl", fetch, write, cf, cw)
     assert bench.decode_valu(str(out), "wl", 1e7) is not None
     assert bench.decode_traffic(str(out), "wl") == 1024 * 2500
+
+
+def test_record_modes_do_no_gpu_work(tmp_path):
+    # each record mode writes its record and exits before any GPU or input work
+    fetch = _counters(tmp_path / "f.csv", [(7, DEC, 500.0)])
+    write = _counters(tmp_path / "w.csv", [(7, DEC, 1500.0)])
+    cf = _counters(tmp_path / "cf.csv", [(2, COPY, 524288.0)])
+    cw = _counters(tmp_path / "cw.csv", [(2, COPY, 1048576.0)])
+    out = tmp_path / "t.json"
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny",
+                        "--traffic-json", str(out), "--record-traffic", fetch, write, cf, cw],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    sq = _sq(tmp_path / "s.csv", [(3, DEC, "SQ_INSTS_VALU", 2e8, 0, 400000),
+                                  (3, DEC, "GRBM_GUI_ACTIVE", 6.4e6, 0, 400000)])
+    agent = tmp_path / "agent.csv"
+    with open(agent, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Simd_Count", "Num_Xcc", "Max_Engine_Clk_Fcompute"])
+        w.writerow([1024, 8, 2400])
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny",
+                        "--traffic-json", str(out), "--record-valu", sq, str(agent)],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    rec = json.load(open(out))["workloads"]["tiny"]
+    assert "bytes_per_launch" in rec and "valu" in rec
