@@ -60,6 +60,10 @@ def parse():
                     help="measure what per-(layer, channel) symbol statistics are worth instead: "
                          "coded size of every chunk and quality with tables pooled per layer, "
                          "per channel and globally, and with tables profiled on another context")
+    ap.add_argument("--format-study", action="store_true",
+                    help="measure what a later format could save instead: the empirical entropy of "
+                         "the blobs' 8-bit anchors under tables pooled per layer or per channel, "
+                         "and the bytes of per-stream fields")
     ap.add_argument("--contexts", type=int, default=2000,
                     help="contexts streamed per policy in --adaptive")
     ap.add_argument("--streamed", action="store_true",
@@ -101,6 +105,9 @@ def main():
 
     if args.adaptive:
         adaptive(args)
+        return
+    if args.format_study:
+        print(json.dumps(format_study(args)))
         return
     if args.grouping:
         grouping(args)
@@ -284,6 +291,77 @@ def stream_context_lib(sizes, decode_ms, slo_ms, send, prior_bpms, policy="adapt
         decoded = max(decoded, t) + float(decode_ms[c][q])
         versions.append(q)
     return decoded, versions
+
+
+def _entropy_bits(counts):
+    """Sum over rows of a count matrix of n H(row), in bits: the code length of
+    the symbols under each row's own empirical distribution."""
+    import numpy as np
+    c = np.asarray(counts, dtype=np.float64)
+    n = c.sum(axis=-1, keepdims=True)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.where(c > 0, c * np.log2(np.where(c > 0, n / c, 1.0)), 0.0)
+    return float(t.sum())
+
+
+def format_study(args):
+    """What the format could still save (the next format variants the pages'
+    pipeline suggests: entropy-coded anchors, streams over groups of channels),
+    measured on the blobs the GPU codes: every chunk of the workload at quality
+    H, anchors read back from the blobs.  The anchors' empirical entropy pooled
+    per (kv, layer, channel), per (kv, layer) and globally is what coding them
+    with a 256-symbol table of that granularity would approach (tables not
+    counted); the lengths' bytes are the per-stream field that channel groups
+    would divide."""
+    import numpy as np
+    import torch
+
+    import kv_cache_compression_anchor_amd as cg
+    import synth
+    w = synth.workload(args.workload)
+    k, v = synth.gen_kv(w)
+    kd, vd = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+    p = cg.make_params(w.layers, w.tokens, w.channels, w.chunk_tokens, w.group_tokens,
+                       w.layer_group_end, w.layer_step, w.quality_mult, w.quality_mask)
+    tab = cg.cg_build_tables(p, kd, vd)
+    q = w.qualities[0]
+    chunks = list(range(w.n_chunks))
+    outs = [torch.empty(cg.cg_encode_bound(tab, c), dtype=torch.uint8, device="cuda") for c in chunks]
+    sizes = cg.cg_encode_batch(tab, kd, vd, chunks, [q] * len(chunks), outs)
+    L, C = w.layers, w.channels
+    hist = np.zeros((2, L, C, 256), np.int64)
+    total = anchors = lengths = streams = 0
+    for o, n in zip(outs, sizes):
+        b = o[:n].cpu().numpy()
+        ng = cg.cg_chunk_info_parse(torch.from_numpy(b[:64].copy())).n_groups
+        off_a = 64 + 8 * L
+        a = b[off_a:off_a + 2 * L * ng * C].view(np.int8).reshape(2, L, ng, C).astype(np.int64) + 128
+        for kv in range(2):
+            for l in range(L):
+                np.add.at(hist[kv, l], (np.arange(C)[None, :].repeat(ng, 0), a[kv, l]), 1)
+        total += n
+        anchors += a.size
+        lengths += 2 * 2 * L * C
+        streams += 2 * L * C
+    h_lc = _entropy_bits(hist)
+    h_l = _entropy_bits(hist.sum(axis=2))
+    h_g = _entropy_bits(hist.sum(axis=(0, 1, 2))[None])
+    elems = 2 * L * w.tokens * C
+    return {
+        "study": "format", "workload": w.name, "quality": "HML"[q], "blob_bytes": int(total),
+        "elements": elems, "coded_bits_per_element": round(8 * total / elems, 4),
+        "anchors": anchors, "anchor_bits_per_element_now": round(8 * anchors / elems, 4),
+        "anchor_entropy_bits": {"per_layer_channel": round(h_lc / anchors, 3),
+                                "per_layer": round(h_l / anchors, 3), "global": round(h_g / anchors, 3)},
+        "anchor_saving_bits_per_element": {"per_layer_channel": round((8 * anchors - h_lc) / elems, 4),
+                                           "per_layer": round((8 * anchors - h_l) / elems, 4),
+                                           "global": round((8 * anchors - h_g) / elems, 4)},
+        "anchor_saving_fraction_of_blobs": {"per_layer": round((8 * anchors - h_l) / 8 / total, 4)},
+        "per_layer_tables_bytes": 2 * L * 256 * 2,
+        "per_layer_channel_tables_bytes": 2 * L * C * 256 * 2,
+        "streams": streams, "length_field_bytes": lengths,
+        "length_fraction_of_blobs": round(lengths / total, 4),
+    }
 
 
 def grouping(args):

@@ -133,3 +133,11 @@ def test_record_modes_do_no_gpu_work(tmp_path):
     assert r.returncode == 0, r.stderr
     rec = json.load(open(out))["workloads"]["tiny"]
     assert "bytes_per_launch" in rec and "valu" in rec
+
+
+def test_entropy_of_count_rows():
+    import numpy as np
+    # a fair coin over four symbols, and a certain symbol: 4 x 1 bit + 0
+    assert bench._entropy_bits(np.array([[2, 2, 0, 0], [4, 0, 0, 0]])) == pytest.approx(4.0)
+    # three equiprobable symbols, 3 each: 9 log2 3
+    assert bench._entropy_bits(np.array([[3, 3, 3]])) == pytest.approx(9 * np.log2(3))
