@@ -330,6 +330,35 @@ def decode_blob(tables: bytes, blob: bytes, k_out: np.ndarray, v_out: np.ndarray
     return bool(bad.value)
 
 
+def decode_blob_paged(tables: bytes, blob: bytes, k_pool: np.ndarray, v_pool: np.ndarray,
+                      page_tokens: int, block_table: np.ndarray,
+                      threads: Optional[int] = None):
+    """Decode one chunk blob into paged K/V pools (the receiver hands the decoded
+    cache to the model: gptget 方法详解, GPU decoding on the receiving end).
+
+    Pools are fp16 [L, num_pages, page_tokens, C].  Context token t lives in
+    row t % page_tokens of page block_table[t // page_tokens]; an entry outside
+    [0, num_pages) is not written and is reported.  The blob is decoded into a
+    plain [L, T, C] tensor first, then its tokens are placed one by one.
+    Returns (corrupt, bad_page)."""
+    h = parse_blob_header(blob)
+    L, T, Cc = h["layers"], h["total_tokens"], h["channels"]
+    num_pages = k_pool.shape[1]
+    assert k_pool.shape == v_pool.shape == (L, num_pages, page_tokens, Cc)
+    k = np.zeros((L, T, Cc), np.float16)
+    v = np.zeros((L, T, Cc), np.float16)
+    corrupt = decode_blob(tables, blob, k, v, threads)
+    bad_page = False
+    for t in range(h["token_offset"], h["token_offset"] + h["chunk_tokens"]):
+        page = int(block_table[t // page_tokens])
+        if not 0 <= page < num_pages:
+            bad_page = True
+            continue
+        k_pool[:, page, t % page_tokens, :] = k[:, t, :]
+        v_pool[:, page, t % page_tokens, :] = v[:, t, :]
+    return corrupt, bad_page
+
+
 def decode_blob_symbols(tables: bytes, blob: bytes):
     t = np.frombuffer(tables, np.uint8)
     b = np.frombuffer(blob, np.uint8)
