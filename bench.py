@@ -69,6 +69,11 @@ def parse():
     ap.add_argument("--streamed", action="store_true",
                     help="measure the chunk pipeline instead: the Llama-70B-shape 16K schedule "
                          "decoded from pinned host memory (H2D on one stream, decode on another)")
+    ap.add_argument("--paged", action="store_true",
+                    help="measure the decode into paged K/V pools instead: the selection decoded "
+                         "through a shuffled block table of --page-tokens pages, beside the "
+                         "decode into [L, T, C] and that decode followed by a copy into the pages")
+    ap.add_argument("--page-tokens", type=int, default=16)
     return ap.parse_args()
 
 
@@ -114,6 +119,9 @@ def main():
         return
     if args.streamed:
         streamed(args)
+        return
+    if args.paged:
+        paged(args)
         return
 
     w = synth.workload(args.workload)
@@ -610,6 +618,103 @@ def streamed(args):
         "decode_GBps_fp16_out": round(out_bytes / (ms["decode"] * 1e-3) / 1e9, 2),
         "pipeline_ms": round(ms["pipeline"], 3),
         "overlap": round((ms["h2d"] + ms["decode"]) / ms["pipeline"], 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def paged(args):
+    """Decode into paged pools [L, num_pages, P, C] on the --workload selection:
+    pages of --page-tokens tokens named by a seeded shuffled block table with
+    1/16 spare pages.  Times (HIP events on the launch stream, mean and min of
+    --steps runs): the decode into [L, T, C], the paged decode, and the [L, T, C]
+    decode followed by a copy of its rows into the pages (torch index_put), what a
+    caller without the paged entry point would run."""
+    import numpy as np
+    import torch
+
+    import kv_cache_compression_anchor_amd as cg
+    import synth
+    w = synth.workload(args.workload)
+    P = args.page_tokens
+    if w.tokens % P:
+        raise SystemExit("--page-tokens must divide the context")
+    k, v = synth.gen_kv(w)
+    kd = torch.from_numpy(k).cuda()
+    vd = torch.from_numpy(v).cuda()
+    p = cg.make_params(w.layers, w.tokens, w.channels, w.chunk_tokens, w.group_tokens,
+                       w.layer_group_end, w.layer_step, w.quality_mult, w.quality_mask)
+    tab = cg.cg_build_tables(p, kd, vd)
+    sel = list(w.selection())
+    outs = [torch.empty(cg.cg_encode_bound(tab, c), dtype=torch.uint8, device="cuda")
+            for c in range(len(sel))]
+    sizes = cg.cg_encode_batch(tab, kd, vd, list(range(len(sel))), sel, outs)
+    blobs = [o[:n] for o, n in zip(outs, sizes)]
+    infos = [cg.cg_chunk_info_parse(b[:64].cpu()) for b in blobs]
+    del kd, vd
+    nb = w.tokens // P
+    n_pages = nb + nb // 16
+    table_h = np.random.default_rng(12345).permutation(n_pages)[:nb].astype(np.int32)
+    table = torch.from_numpy(table_h).cuda()
+    idx = table.long()
+    ko = torch.empty((w.layers, w.tokens, w.channels), dtype=torch.float16, device="cuda")
+    vo = torch.empty_like(ko)
+    kp = torch.zeros((w.layers, n_pages, P, w.channels), dtype=torch.float16, device="cuda")
+    vp = torch.zeros_like(kp)
+    kq, vq = torch.zeros_like(kp), torch.zeros_like(vp)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    def flat():
+        cg.cg_decode_async(tab, blobs, infos, ko, vo, st)
+
+    def pg():
+        cg.cg_decode_paged_async(tab, blobs, infos, kp, vp, P, table, st)
+
+    def flat_then_copy():
+        cg.cg_decode_async(tab, blobs, infos, ko, vo, st)
+        kq[:, idx] = ko.view(w.layers, nb, P, w.channels)
+        vq[:, idx] = vo.view(w.layers, nb, P, w.channels)
+
+    res = {"flat": [], "paged": [], "flat_then_copy": []}
+    for it in range(args.warmup + args.steps):
+        a, b, c = timed(flat), timed(pg), timed(flat_then_copy)
+        if it >= args.warmup:
+            res["flat"].append(a)
+            res["paged"].append(b)
+            res["flat_then_copy"].append(c)
+    if int(st.item()) != 0:
+        raise SystemExit(f"decode reported status {int(st.item())}")
+    # the paged pools hold the [L, T, C] decode's rows where the table says
+    same = bool(torch.equal(kp[:, idx].view(torch.int16), ko.view(w.layers, nb, P, w.channels).view(torch.int16))
+                and torch.equal(vp[:, idx].view(torch.int16), vo.view(w.layers, nb, P, w.channels).view(torch.int16)))
+    if not same:
+        raise SystemExit("paged pools differ from the [L, T, C] decode")
+    mean = {key: sum(x) / len(x) for key, x in res.items()}
+    low = {key: min(x) for key, x in res.items()}
+    out_bytes = 2 * w.elements
+    alg = sum(sizes) + out_bytes
+    line = {
+        "metric": "paged decode: fp16 KV out GB/s (into pages through a block table)",
+        "value": round(out_bytes / (mean["paged"] * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(mean["paged"], 4), "higher_is_better": True,
+        "config": {"workload": w.name, "selection": ",".join("HML"[q] for q in sel),
+                   "page_tokens": P, "blocks": nb, "pages": n_pages},
+        "kernel": decode_kernel_name(sel) + " (paged instance)",
+        "paged_ms": round(mean["paged"], 4), "paged_min_ms": round(low["paged"], 4),
+        "flat_ms": round(mean["flat"], 4), "flat_min_ms": round(low["flat"], 4),
+        "paged_over_flat": round(mean["paged"] / mean["flat"], 4),
+        "flat_then_copy_ms": round(mean["flat_then_copy"], 4),
+        "paged_roofline_frac": round(alg / (mean["paged"] * 1e-3) / 8e12, 4),
+        "pools_equal_flat_decode": same,
     }
     print(json.dumps(line), flush=True)
 

@@ -178,6 +178,29 @@ int cg_decode_async(const cg_tables* tables, int32_t n, const void* const* blobs
                     const cg_chunk_info* infos, void* k_out_dev, void* v_out_dev,
                     uint32_t* status_dev, void* stream);
 
+/* Enqueue-only decode straight into paged K/V pools (gptget 方法详解: the
+ * receiver's GPU decoder hands the cache to the model; a serving engine keeps
+ * that cache in fixed-size pages).  The pools k_pool_dev / v_pool_dev are fp16
+ * [layers][num_pages][page_tokens][channels] (each layer's pages contiguous),
+ * caller-owned.  Context token t is written to row t % page_tokens of page
+ * block_table_dev[t / page_tokens]; block_table_dev is a caller-owned device
+ * int32 array of n_blocks entries, read while the decode runs, which must name
+ * distinct pages for the blocks the blobs cover (rows of two blocks that share
+ * a page overwrite each other).  Rows and pages no blob writes keep their
+ * contents.  An entry outside [0, num_pages) is not written: its rows are
+ * skipped and bit 1 of *status_dev is set; bit 0 is set as in cg_decode_async.
+ * The decoded values equal cg_decode_async's bit for bit.
+ * CG_E_INVAL: NULL argument; page_tokens not a power of two in [1, 65536];
+ * num_pages or n_blocks < 1; a layer's pool of 2 GiB or more; a block table
+ * shorter than ceil((token_offset + chunk_tokens) / page_tokens) for some blob;
+ * group_tokens > 64, or a last 64-channel block with fewer than group_tokens
+ * channels (channels % 64 in [1, group_tokens)).  Header mismatches as in
+ * cg_decode_async. */
+int cg_decode_paged_async(const cg_tables* tables, int32_t n, const void* const* blobs_dev,
+                          const cg_chunk_info* infos, void* k_pool_dev, void* v_pool_dev,
+                          int64_t num_pages, int32_t page_tokens, const int32_t* block_table_dev,
+                          int64_t n_blocks, uint32_t* status_dev, void* stream);
+
 /* Chunk pipeline (gptget 方法详解: decoding pipelined with the transfer; CacheGen
  * blog 2.2: chunk-by-chunk streaming).  blobs_host[i] are host blobs (pinned
  * memory gives asynchronous copies); each is copied into a slot of the device

@@ -23,7 +23,8 @@ _NAMES = {0: "CG_OK", -1: "CG_E_INVAL", -2: "CG_E_NOMEM", -3: "CG_E_HIP", -4: "C
 
 EXPORTS = ["cg_build_tables", "cg_build_tables_grouped", "cg_tables_free", "cg_tables_serialize",
            "cg_tables_deserialize", "cg_tables_id", "cg_tables_params", "cg_num_chunks", "cg_encode_bound", "cg_encode",
-           "cg_encode_batch", "cg_chunk_info_parse", "cg_decode", "cg_decode_async", "cg_decode_streamed",
+           "cg_encode_batch", "cg_chunk_info_parse", "cg_decode", "cg_decode_async", "cg_decode_paged_async",
+           "cg_decode_streamed",
            "cg_plan_chunk", "cg_last_error"]
 
 
@@ -82,6 +83,8 @@ def lib():
             "cg_chunk_info_parse": (I, [P, SZ, C.POINTER(cg_chunk_info)]),
             "cg_decode": (I, [P, I32, C.POINTER(P), C.POINTER(SZ), P, P, P]),
             "cg_decode_async": (I, [P, I32, C.POINTER(P), C.POINTER(cg_chunk_info), P, P, P, P]),
+            "cg_decode_paged_async": (I, [P, I32, C.POINTER(P), C.POINTER(cg_chunk_info), P, P,
+                                          C.c_int64, I32, P, C.c_int64, P, P]),
             "cg_decode_streamed": (I, [P, I32, C.POINTER(P), C.POINTER(cg_chunk_info), P, P, P,
                                        SZ, P, P, P]),
             "cg_plan_chunk": (I, [C.POINTER(cg_chunk_plan_in), C.POINTER(I32),
@@ -302,6 +305,29 @@ def cg_decode_async(t: Tables, blobs, infos, k_out, v_out, status, stream=None):
                                  _dev_ptr(k_out, torch.float16, "k_out"),
                                  _dev_ptr(v_out, torch.float16, "v_out"),
                                  _dev_ptr(status, torch.int32, "status"), _stream(stream)))
+
+
+def cg_decode_paged_async(t: Tables, blobs, infos, k_pool, v_pool, page_tokens, block_table,
+                          status, stream=None):
+    """Decode into paged pools k_pool / v_pool (fp16 [L, num_pages, page_tokens,
+    C] device tensors) through block_table (int32 device tensor, one entry per
+    block of page_tokens context tokens)."""
+    import torch
+    bp = [_dev_ptr(b, torch.uint8, "blob") for b in blobs]
+    if len(infos) != len(bp):
+        raise ValueError("one info per blob")
+    prm = t.params
+    if (k_pool.dim() != 4 or k_pool.shape != v_pool.shape or k_pool.shape[2] != page_tokens
+            or k_pool.shape[0] != prm.layers or k_pool.shape[3] != prm.channels):
+        raise ValueError("pools must both be [layers, num_pages, page_tokens, channels] of the tables")
+    iarr = (cg_chunk_info * max(1, len(infos)))(*infos)
+    _check(lib().cg_decode_paged_async(t.handle, len(bp), _ptr_array(bp), iarr,
+                                       _dev_ptr(k_pool, torch.float16, "k_pool"),
+                                       _dev_ptr(v_pool, torch.float16, "v_pool"),
+                                       int(k_pool.shape[1]), int(page_tokens),
+                                       _dev_ptr(block_table, torch.int32, "block_table"),
+                                       int(block_table.numel()),
+                                       _dev_ptr(status, torch.int32, "status"), _stream(stream)))
 
 
 def cg_decode_streamed(t: Tables, host_blobs, infos, k_out, v_out, staging, status,

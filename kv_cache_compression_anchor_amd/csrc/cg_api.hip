@@ -288,9 +288,17 @@ int check_info_against(const cg_tables* h, const cg_chunk_info& in) {
   return CG_OK;
 }
 
-// Enqueues the decode of n blobs whose headers are already checked.
+// Where a paged decode writes (arguments already checked).
+struct PagedOut {
+  const int32_t* table;
+  uint32_t n_blocks, num_pages, shift;
+};
+
+// Enqueues the decode of n blobs whose headers are already checked, into
+// [L][T][C] tensors or, with pg, into paged pools.
 int enqueue_decode(const cg_tables* h, int n, const void* const* blobs, const cg_chunk_info* infos,
-                   void* k_out, void* v_out, uint32_t* status, hipStream_t st) {
+                   void* k_out, void* v_out, uint32_t* status, hipStream_t st,
+                   const PagedOut* pg = nullptr) {
   const DevTables& t = h->t;
   // chunks grouped by quality, up to 4 per workgroup (one wave each)
   std::vector<int> byq[3];
@@ -319,6 +327,13 @@ int enqueue_decode(const cg_tables* h, int n, const void* const* blobs, const cg
     a.k_out = static_cast<uint16_t*>(k_out);
     a.v_out = static_cast<uint16_t*>(v_out);
     a.status = status;
+    if (pg) {
+      a.paged = 1;
+      a.block_table = pg->table;
+      a.n_blocks = pg->n_blocks;
+      a.num_pages = pg->num_pages;
+      a.page_shift = pg->shift;
+    }
     int nc = 0, ngrp = 0, waves = 1;
     while (gi < groups.size() && ngrp < kDecMaxChunks &&
            nc + (int)groups[gi].size() <= kDecMaxChunks) {
@@ -770,6 +785,46 @@ int cg_decode_async(const cg_tables* h, int32_t n, const void* const* blobs_dev,
   if (!dg.ok) return fail(CG_E_HIP, "cannot select the tables' device");
   return enqueue_decode(h, n, blobs_dev, infos, k_out_dev, v_out_dev, status_dev,
                         static_cast<hipStream_t>(stream));
+}
+
+int cg_decode_paged_async(const cg_tables* h, int32_t n, const void* const* blobs_dev,
+                          const cg_chunk_info* infos, void* k_pool_dev, void* v_pool_dev,
+                          int64_t num_pages, int32_t page_tokens, const int32_t* block_table_dev,
+                          int64_t n_blocks, uint32_t* status_dev, void* stream) {
+  if (!h || n < 0 || (n > 0 && (!blobs_dev || !infos)) || !k_pool_dev || !v_pool_dev ||
+      !status_dev || !block_table_dev)
+    return fail(CG_E_INVAL, "NULL argument");
+  const DevTables& t = h->t;
+  if (page_tokens < 1 || page_tokens > kMaxChunk || (page_tokens & (page_tokens - 1)))
+    return fail(CG_E_INVAL, "page_tokens must be a power of two in [1, 65536]");
+  if (num_pages < 1 || num_pages > (int64_t)1 << 31 || n_blocks < 1 || n_blocks > (int64_t)1 << 30)
+    return fail(CG_E_INVAL, "num_pages or n_blocks out of range");
+  if ((uint64_t)num_pages * (uint64_t)page_tokens * (uint64_t)t.C * 2u >= (uint64_t)1 << 31)
+    return fail(CG_E_INVAL, "a layer's pool must be smaller than 2 GiB");
+  // lane j of a wave holds the row of token j of a group: every 64-channel
+  // block needs at least a group's worth of channels
+  const int last_blk = t.C - (t.nblk - 1) * 64;
+  if (t.G > 64 || last_blk < t.G)
+    return fail(CG_E_INVAL, "paged decode needs group_tokens <= 64 and at least group_tokens "
+                            "channels in every 64-channel block");
+  for (int i = 0; i < n; i++) {
+    if (!blobs_dev[i]) return fail(CG_E_INVAL, "NULL blob");
+    int rc = check_info_against(h, infos[i]);
+    if (rc) return rc;
+    const int64_t end = (int64_t)infos[i].token_offset + infos[i].chunk_tokens;
+    if ((end + page_tokens - 1) / page_tokens > n_blocks)
+      return fail(CG_E_INVAL, "block table shorter than the blobs' token ranges");
+  }
+  if (n == 0) return CG_OK;
+  DeviceGuard dg(h->dev);
+  if (!dg.ok) return fail(CG_E_HIP, "cannot select the tables' device");
+  PagedOut pg;
+  pg.table = block_table_dev;
+  pg.n_blocks = (uint32_t)n_blocks;
+  pg.num_pages = (uint32_t)num_pages;
+  pg.shift = (uint32_t)__builtin_ctz((unsigned)page_tokens);
+  return enqueue_decode(h, n, blobs_dev, infos, k_pool_dev, v_pool_dev, status_dev,
+                        static_cast<hipStream_t>(stream), &pg);
 }
 
 int cg_decode(const cg_tables* ch, int32_t n, const void* const* blobs_dev, const size_t* lens,

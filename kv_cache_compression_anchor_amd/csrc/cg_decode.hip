@@ -139,9 +139,16 @@ struct Lane {
   uint32_t row_bytes, lane_off, anc_base;
   int C;
   DecChunk ch;
+  // paged output: the layer's pool, its size in bytes, the block table and the
+  // chunk's first context token
+  uint16_t* pool;
+  uint32_t pool_bytes;
+  __amdgpu_buffer_rsrc_t rt;
+  uint32_t tok0;
 };
 
 // Stages the tables and sets up the lane; false for a lane without a stream.
+template <bool PG>
 __device__ __forceinline__ bool setup(const DecodeArgs& a, int wave, int lane, Lane& s) {
   auto tab = lds_at<uint32_t>(0);
   const int tid = threadIdx.x;
@@ -195,9 +202,18 @@ __device__ __forceinline__ bool setup(const DecodeArgs& a, int wave, int lane, L
 
   // output rows of this (kv, layer, chunk) through a buffer resource: the lane's
   // channel is the vector offset, the token row a wave-uniform scalar offset
-  uint16_t* const out_base = (kv ? a.v_out : a.k_out) + ((size_t)l * a.T + s.ch.t0) * a.C;
-  s.ro = __builtin_amdgcn_make_buffer_rsrc(out_base, 0, (int)((uint32_t)s.ch.tc * (uint32_t)a.C * 2u),
-                                           kBufRsrcWord3);
+  if constexpr (PG) {
+    const size_t layer_elems = ((size_t)a.num_pages << a.page_shift) * (size_t)a.C;
+    s.pool = (kv ? a.v_out : a.k_out) + (size_t)l * layer_elems;
+    s.pool_bytes = (uint32_t)(2u * layer_elems);
+    s.rt = __builtin_amdgcn_make_buffer_rsrc((void*)a.block_table, 0, (int)(4u * a.n_blocks),
+                                             kBufRsrcWord3);
+    s.tok0 = (uint32_t)s.ch.t0;
+  } else {
+    uint16_t* const out_base = (kv ? a.v_out : a.k_out) + ((size_t)l * a.T + s.ch.t0) * a.C;
+    s.ro = __builtin_amdgcn_make_buffer_rsrc(out_base, 0, (int)((uint32_t)s.ch.tc * (uint32_t)a.C * 2u),
+                                             kBufRsrcWord3);
+  }
   s.row_bytes = 2u * (uint32_t)a.C;
   s.lane_off = 2u * (uint32_t)c;
   s.anc_base = s.ch.off_anchor + (uint32_t)row * (uint32_t)s.ch.ng * (uint32_t)a.C + c;
@@ -208,6 +224,42 @@ __device__ __forceinline__ bool setup(const DecodeArgs& a, int wave, int lane, L
 __device__ __forceinline__ void put_half(const Lane& s, float y, uint32_t t) {
   __builtin_amdgcn_raw_buffer_store_b16(float_to_half_bits(y), s.ro, s.lane_off, t * s.row_bytes, kStoreNT);
 }
+
+// ---------------------------------------------------------------------------
+// Paged output.  Lane j of a wave holds the byte offset, in the layer's pool,
+// of the row of token j of the current group (groups are at most 64 tokens),
+// computed from the block-table entry it loaded one group earlier; a token's
+// store reads it with one v_readlane.  An entry outside the pool gives kNoRow:
+// that row's stores get a resource of size zero, so they write nothing.
+constexpr uint32_t kNoRow = 0xFFFFFFFFu;
+
+struct Pager {
+  uint32_t po = 0;    // this lane's token row offset in the current group, or kNoRow
+  uint32_t ent = 0;   // block-table entry of this lane's token in the next group (in flight)
+  uint32_t bad = 0;   // an entry this lane needed was outside the pool
+  int ta = 0;         // first token (in the chunk) of the current group
+
+  // issues the load of the entry for token ta + lane (lanes past the group
+  // point their load past the table: no memory access, zero)
+  __device__ __forceinline__ void fetch(const DecodeArgs& a, const Lane& s, int lane, int ta_next) {
+    const uint32_t tok = s.tok0 + (uint32_t)ta_next + (uint32_t)lane;
+    ent = ld32(s.rt, lane < a.G ? 4u * (tok >> a.page_shift) : 0xFFFFFFF0u);
+  }
+  // the current group [ta, te) takes the entries fetched for it
+  __device__ __forceinline__ void begin(const DecodeArgs& a, const Lane& s, int lane, int ta_, int te) {
+    ta = ta_;
+    const uint32_t tok = s.tok0 + (uint32_t)ta + (uint32_t)lane;
+    const bool ok = ent < a.num_pages;
+    if (!ok && lane < te - ta) bad = 1u;
+    po = ok ? ((ent << a.page_shift) | (tok & ((1u << a.page_shift) - 1u))) * s.row_bytes : kNoRow;
+  }
+  __device__ __forceinline__ void put(const Lane& s, float y, uint32_t t) const {
+    const uint32_t ro = (uint32_t)__builtin_amdgcn_readlane((int)po, (int)t - ta);
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(s.pool, 0, ro != kNoRow ? (int)s.pool_bytes : 0, kBufRsrcWord3);
+    __builtin_amdgcn_raw_buffer_store_b16(float_to_half_bits(y), r, s.lane_off, ro, kStoreNT);
+  }
+};
 
 // ---------------------------------------------------------------------------
 // LDS-window kernel.  Per lane, ring word k (stream word 1 + k) sits,
@@ -240,12 +292,17 @@ __device__ __forceinline__ void win_put(uint32_t ring, uint32_t at, bool high, c
 constexpr uint32_t kWinHigh = (2u + kWinM - (kWinRB - 1u)) * kSlot;  // lowest slot of a high block
 constexpr uint32_t kWinLow = kWinHigh - kWinRB * kSlot;
 
-template <int GS>
+template <int GS, bool PG>
 __global__ __launch_bounds__(512) void k_decode_win(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   Lane s;
-  if (!setup(a, wave, lane, s)) return;
+  if (!setup<PG>(a, wave, lane, s)) return;
+  Pager pg;
+  auto out = [&](uint32_t t, float y) {
+    if constexpr (PG) pg.put(s, y, t);
+    else put_half(s, y, t);
+  };
   constexpr int RB = kWinRB;
   constexpr uint32_t M = kWinM;
 
@@ -280,7 +337,7 @@ __global__ __launch_bounds__(512) void k_decode_win(DecodeArgs a) {
     const uint32_t ad = search(ncode, range, sh, s.lane_addr, s.key32);
     sel = shift_sel(sh);
     ncode = __builtin_amdgcn_perm(ncode, x, sel);
-    put_half(s, __builtin_fmaf(byte1_to_float(ad), s.step, base), t);
+    out(t, __builtin_fmaf(byte1_to_float(ad), s.step, base));
     return sh;
   };
 
@@ -345,11 +402,15 @@ __global__ __launch_bounds__(512) void k_decode_win(DecodeArgs a) {
   using I3 = std::integral_constant<int, 3>;
   auto group = [&](int g, int ta, int te) {
     ring_step();
+    if constexpr (PG) {
+      pg.begin(a, s, lane, ta, te);
+      pg.fetch(a, s, lane, ta + (GS > 0 ? GS : a.G));
+    }
     const int anc = anc_next;
     anc_next = ld8s(s.rs, s.anc_base + (uint32_t)(g + 1) * s.C);  // past the last group: unused
     const float ahat = anchor_value(anc, s.scale_a);
     const float base = __builtin_fmaf(-32.0f, s.step, ahat);
-    put_half(s, ahat, (uint32_t)ta);
+    out((uint32_t)ta, ahat);
     int t = ta + 1;
 #pragma unroll
     for (; t + 2 < te; t += 3) {
@@ -367,6 +428,7 @@ __global__ __launch_bounds__(512) void k_decode_win(DecodeArgs a) {
 
   // everything loaded so far (scale, step, first words, first anchor) is in
   // registers before the loop, so no wait inside it is for those loads
+  if constexpr (PG) pg.fetch(a, s, lane, 0);
   __builtin_amdgcn_s_waitcnt(0);
   // Full groups of the compile-time size GS run the same unrolled code, and a
   // wave's priority steps 3 -> 2 -> 1 -> 0 at half, three quarters and seven
@@ -388,6 +450,7 @@ __global__ __launch_bounds__(512) void k_decode_win(DecodeArgs a) {
   // a valid stream keeps code < range throughout; a corrupt one breaks it for good
   s.bad |= (~ncode >= range) ? 1u : 0u;
   if (s.bad) atomicOr(a.status, 1u);
+  if (PG && pg.bad) atomicOr(a.status, 2u);
 }
 
 // ---------------------------------------------------------------------------
@@ -406,12 +469,17 @@ __device__ __forceinline__ void reg_put(uint32_t lane_addr, uint32_t slot_off, c
   p[64] = b.v.y;
 }
 
-template <int GS>
+template <int GS, bool PG>
 __global__ __launch_bounds__(512) void k_decode_reg(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   Lane s;
-  if (!setup(a, wave, lane, s)) return;
+  if (!setup<PG>(a, wave, lane, s)) return;
+  Pager pg;
+  auto out = [&](uint32_t t, float y) {
+    if constexpr (PG) pg.put(s, y, t);
+    else put_half(s, y, t);
+  };
   constexpr int RB = kRegRB;
 
   // decoder state: ncode = ~code; range; bb = the next bits of the stream,
@@ -446,7 +514,7 @@ __global__ __launch_bounds__(512) void k_decode_reg(DecodeArgs a) {
     const uint32_t tl = left - sh;
     ncode = (ncode << sh) | __builtin_amdgcn_ubfe((uint32_t)(bb >> (tl & 63u)), 0u, sh);
     left = tl;
-    put_half(s, __builtin_fmaf(byte1_to_float(ad), s.step, base), t);
+    out(t, __builtin_fmaf(byte1_to_float(ad), s.step, base));
   };
 
   // A lane takes a word when fewer than 32 bits remain (two symbols need at
@@ -482,10 +550,14 @@ __global__ __launch_bounds__(512) void k_decode_reg(DecodeArgs a) {
   // the group has an even number of tokens)
   auto group = [&](int g, int ta, int te) {
     ring_step();
+    if constexpr (PG) {
+      pg.begin(a, s, lane, ta, te);
+      pg.fetch(a, s, lane, ta + (GS > 0 ? GS : a.G));
+    }
     const int anc = anc_next;
     anc_next = ld8s(s.rs, s.anc_base + (uint32_t)(g + 1) * s.C);  // past the last group: unused
     const float ahat = anchor_value(anc, s.scale_a);
-    put_half(s, ahat, (uint32_t)ta);
+    out((uint32_t)ta, ahat);
     const float base = __builtin_fmaf(-32.0f, s.step, ahat);
     int t = ta + 1;
 #pragma unroll
@@ -504,6 +576,7 @@ __global__ __launch_bounds__(512) void k_decode_reg(DecodeArgs a) {
     }
   };
 
+  if constexpr (PG) pg.fetch(a, s, lane, 0);
   __builtin_amdgcn_s_waitcnt(0);
   // Full groups of the compile-time size GS run the same unrolled code, and a
   // wave's priority steps 3 -> 2 -> 1 -> 0 at half, three quarters and seven
@@ -524,26 +597,37 @@ __global__ __launch_bounds__(512) void k_decode_reg(DecodeArgs a) {
   for (; g < s.ch.ng; g++) group(g, g * a.G, min(g * a.G + a.G, s.ch.tc));
   s.bad |= (~ncode >= range) ? 1u : 0u;
   if (s.bad) atomicOr(a.status, 1u);
+  if (PG && pg.bad) atomicOr(a.status, 2u);
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
+namespace {
+template <bool PG>
+void launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   const unsigned blocks = (unsigned)(a.n_groups * a.L * a.nblk);
   const dim3 grid(blocks), block(2 * kLanes * a.waves);
   if (a.waves == 1) {  // one chunk per workgroup: small rings, eight workgroups per CU
     const size_t lds = reg_ring_base() + (size_t)2 * reg_ring_bytes();
     if (a.G == 10)
-      k_decode_reg<10><<<grid, block, lds, st>>>(a);
+      k_decode_reg<10, PG><<<grid, block, lds, st>>>(a);
     else
-      k_decode_reg<0><<<grid, block, lds, st>>>(a);
+      k_decode_reg<0, PG><<<grid, block, lds, st>>>(a);
   } else {
     const size_t lds = kTabBytes + (size_t)2 * a.waves * win_ring_bytes();
     if (a.G == 10)
-      k_decode_win<10><<<grid, block, lds, st>>>(a);
+      k_decode_win<10, PG><<<grid, block, lds, st>>>(a);
     else
-      k_decode_win<0><<<grid, block, lds, st>>>(a);
+      k_decode_win<0, PG><<<grid, block, lds, st>>>(a);
   }
+}
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
+  if (a.paged)
+    launch_decode_t<true>(a, st);
+  else
+    launch_decode_t<false>(a, st);
   return hipGetLastError();
 }
 

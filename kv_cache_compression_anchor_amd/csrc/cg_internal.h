@@ -146,9 +146,14 @@ struct DecodeArgs {
   const uint16_t* img[3];
   const float* scale_a;
   const float* step[3];
-  uint16_t* k_out;
+  uint16_t* k_out;  // [L][T][C], or when paged the pools [L][num_pages][page][C]
   uint16_t* v_out;
   uint32_t* status;
+  // paged output: context token t goes to row t mod page of page
+  // block_table[t / page], page = 1 << page_shift
+  int paged;
+  const int32_t* block_table;
+  uint32_t n_blocks, num_pages, page_shift;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 
