@@ -103,20 +103,60 @@ __device__ __forceinline__ uint32_t le_mask(uint32_t r, uint32_t key, uint32_t n
   return (uint32_t)(((uint64_t)r * key + c) >> 32);
 }
 
+// (m & a) | (~m & b) as one v_bfi_b32 (left to itself the compiler picks
+// v_bitop3_b32, which a miscompiled decoder variant used on the result of the
+// v_mad_u64_u32 just before it)
+__device__ __forceinline__ uint32_t bit_select(uint32_t m, uint32_t a, uint32_t b) {
+  uint32_t d;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(d) : "v"(m), "v"(a), "v"(b));
+  return d;
+}
+
+// The lanes in which a + b carries out of 32 bits, as a wave mask (one
+// v_add_co_u32 with its carry in a scalar register pair)
+__device__ __forceinline__ uint64_t carry_mask(uint32_t a, uint32_t b) {
+  uint32_t sum;
+  uint64_t c;
+  asm("v_add_co_u32 %0, %1, %2, %3" : "=v"(sum), "=s"(c) : "v"(a), "v"(b));
+  return c;
+}
+
 // One symbol's search and interval update.  Returns the LDS address of
 // cum[s] (bits 8..13 are s); leaves ncode = ~(code - r cum[s]) and range =
 // r freq[s] shifted left by sh bits, sh = 0, 8 or 16 (whole bytes until range
 // >= 2^24; r freq >= 2^9), and the caller shifts sh stream bits into ncode.
+//
+// s is the largest symbol with r cum[s] <= code.  Delta symbols crowd around
+// the zero delta (symbol 32), so the search first bisects the 16 symbols
+// [24, 40) only: the root cum[32] is in a register, then three levels from
+// LDS.  The result is the answer exactly when code - r cum[s] lies in
+// [0, r freq[s]), i.e. when ~(code - r cum[s]) + r freq[s] carries out of 32
+// bits; a lane whose symbol lies outside the window (or whose stream is
+// corrupt) fails that test, and then the wave redoes the symbol with the full
+// six-level bisection (valid lanes find the same symbol again).
 __device__ __forceinline__ uint32_t search(uint32_t& ncode, uint32_t& range, uint32_t& sh,
                                            uint32_t lane_addr, uint32_t key32) {
   const uint32_t r = range >> kProbBits;
-  // largest s with r * cum[s] <= code, as the LDS address of cum[s]
-  uint32_t ad = lane_addr | (le_mask(r, key32, ncode) & (32u * kRow));
+  const uint32_t m = le_mask(r, key32, ncode);
+  // cum[32] <= code: window [32, 40), else [24, 32)
+  uint32_t ad = bit_select(m, lane_addr + 32u * kRow, lane_addr + 24u * kRow);
 #pragma unroll
-  for (uint32_t stp = 16; stp; stp >>= 1) ad |= le_mask(r, lds16(ad + stp * kRow), ncode) & (stp * kRow);
-  const uint32_t c0 = lds16(ad), c1 = lds16(ad + kRow);
-  ncode += mul24(r, c0);  // code -= r * cum[s]
-  const uint32_t rn = mul24(r, c1 - c0);
+  for (uint32_t stp = 4; stp; stp >>= 1) ad |= le_mask(r, lds16(ad + stp * kRow), ncode) & (stp * kRow);
+  uint32_t c0 = lds16(ad), c1 = lds16(ad + kRow);
+  uint32_t nc2 = ncode + mul24(r, c0);  // code -= r * cum[s]
+  uint32_t rn = mul24(r, c1 - c0);
+  // no carry in some lane: redo the whole wave with the full search (a
+  // wave-uniform branch, laid out away from the common path)
+  if (__builtin_expect(carry_mask(nc2, rn) != __builtin_amdgcn_read_exec(), 0)) {
+    ad = lane_addr | (m & (32u * kRow));
+#pragma unroll
+    for (uint32_t stp = 16; stp; stp >>= 1) ad |= le_mask(r, lds16(ad + stp * kRow), ncode) & (stp * kRow);
+    c0 = lds16(ad);
+    c1 = lds16(ad + kRow);
+    nc2 = ncode + mul24(r, c0);
+    rn = mul24(r, c1 - c0);
+  }
+  ncode = nc2;
   sh = (uint32_t)__builtin_clz(rn) & 24u;
   range = rn << sh;
   return ad;
