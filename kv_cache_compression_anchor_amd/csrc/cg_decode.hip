@@ -128,20 +128,23 @@ __device__ __forceinline__ uint64_t carry_mask(uint32_t a, uint32_t b) {
 //
 // s is the largest symbol with r cum[s] <= code.  Delta symbols crowd around
 // the zero delta (symbol 32), so the search first bisects the 16 symbols
-// [24, 40) only: the root cum[32] is in a register, then three levels from
-// LDS.  The result is the answer exactly when code - r cum[s] lies in
+// [24, 40) only: the root cum[32] and the second level's cum[28] and cum[36]
+// are in registers, then two levels from LDS.  The result is the answer exactly when code - r cum[s] lies in
 // [0, r freq[s]), i.e. when ~(code - r cum[s]) + r freq[s] carries out of 32
 // bits; a lane whose symbol lies outside the window (or whose stream is
 // corrupt) fails that test, and then the wave redoes the symbol with the full
 // six-level bisection (valid lanes find the same symbol again).
 __device__ __forceinline__ uint32_t search(uint32_t& ncode, uint32_t& range, uint32_t& sh,
-                                           uint32_t lane_addr, uint32_t key32) {
+                                           uint32_t lane_addr, uint32_t key32, uint32_t key28,
+                                           uint32_t key36) {
   const uint32_t r = range >> kProbBits;
   const uint32_t m = le_mask(r, key32, ncode);
-  // cum[32] <= code: window [32, 40), else [24, 32)
-  uint32_t ad = bit_select(m, lane_addr + 32u * kRow, lane_addr + 24u * kRow);
+  // cum[32] <= code: window [32, 40), else [24, 32); its middle key is in a
+  // register too
+  const uint32_t m2 = le_mask(r, bit_select(m, key36, key28), ncode);
+  uint32_t ad = bit_select(m, lane_addr + 32u * kRow, lane_addr + 24u * kRow) | (m2 & (4u * kRow));
 #pragma unroll
-  for (uint32_t stp = 4; stp; stp >>= 1) ad |= le_mask(r, lds16(ad + stp * kRow), ncode) & (stp * kRow);
+  for (uint32_t stp = 2; stp; stp >>= 1) ad |= le_mask(r, lds16(ad + stp * kRow), ncode) & (stp * kRow);
   uint32_t c0 = lds16(ad), c1 = lds16(ad + kRow);
   uint32_t nc2 = ncode + mul24(r, c0);  // code -= r * cum[s]
   uint32_t rn = mul24(r, c1 - c0);
@@ -176,6 +179,7 @@ struct Lane {
   float scale_a, step;
   uint32_t lane_addr;  // LDS address of the lane's cum[0]
   uint32_t key32;      // cum[32], the root of every search
+  uint32_t key28, key36;  // cum[28] and cum[36], the keys of its second level
   uint32_t row_bytes, lane_off, anc_base;
   int C;
   DecChunk ch;
@@ -239,6 +243,8 @@ __device__ __forceinline__ bool setup(const DecodeArgs& a, int wave, int lane, L
   s.step = a.step[q][pi];
   s.lane_addr = (uint32_t)kv * (2u * kLanes) + 2u * lane_slot(lane);
   s.key32 = lds16(s.lane_addr + 32u * kRow);
+  s.key28 = lds16(s.lane_addr + 28u * kRow);
+  s.key36 = lds16(s.lane_addr + 36u * kRow);
 
   // output rows of this (kv, layer, chunk) through a buffer resource: the lane's
   // channel is the vector offset, the token row a wave-uniform scalar offset
@@ -374,7 +380,7 @@ __global__ __launch_bounds__(512) void k_decode_win(DecodeArgs a) {
   // returns sh and the selector that shifted them in
   auto symbol = [&](uint32_t t, float base, uint32_t x, uint32_t& sel) -> uint32_t {
     uint32_t sh;
-    const uint32_t ad = search(ncode, range, sh, s.lane_addr, s.key32);
+    const uint32_t ad = search(ncode, range, sh, s.lane_addr, s.key32, s.key28, s.key36);
     sel = shift_sel(sh);
     ncode = __builtin_amdgcn_perm(ncode, x, sel);
     out(t, __builtin_fmaf(byte1_to_float(ad), s.step, base));
@@ -550,7 +556,7 @@ __global__ __launch_bounds__(512) void k_decode_reg(DecodeArgs a) {
   // one symbol: search, interval update, renormalisation, reconstruction
   auto symbol = [&](uint32_t t, float base) {
     uint32_t sh;
-    const uint32_t ad = search(ncode, range, sh, s.lane_addr, s.key32);
+    const uint32_t ad = search(ncode, range, sh, s.lane_addr, s.key32, s.key28, s.key36);
     const uint32_t tl = left - sh;
     ncode = (ncode << sh) | __builtin_amdgcn_ubfe((uint32_t)(bb >> (tl & 63u)), 0u, sh);
     left = tl;
