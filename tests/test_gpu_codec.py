@@ -410,3 +410,50 @@ def test_open_words_and_carries_match_the_oracle():
     kg, vg, st = gu.gpu_decode(tab, [out[:nb]], k.shape)
     ko, vo, bad = gu.oracle_decode(ot, [ob], k.shape)
     assert st == 0 and not bad and gu.same_bits(kg, ko) and gu.same_bits(vg, vo)
+
+
+def test_symbols_outside_the_search_window():
+    """The decoder bisects the 16 symbols [24, 40) around the zero delta first
+    and lets a wave redo a symbol with the full search when some lane's symbol
+    lies outside.  Planted delta strings: one lane of a wave with only tail
+    symbols (the rest of the wave inside the window), the window's edges and the
+    alphabet's ends in turn (23, 24, 39, 40, 0, 63), and symbols on the inner
+    edges only.  Blobs and the decode through both kernels (two chunks of a
+    quality in one workgroup, and one chunk per workgroup) equal the oracle's."""
+    w = gu.workload(layers=1, tokens=2000, channels=128, chunk_tokens=1000, group_tokens=10,
+                    layer_group_end=(1,), layer_step=(0.5,), qualities=(0,), seed=23)
+    k, v = synth.gen_kv(w)
+    kd, vd = gu.to_dev(k), gu.to_dev(v)
+    tab = gu.gpu_tables(w, kd, vd)
+    ot = oracle.build_tables(oracle.params_for(w), k, v)
+    tv = oracle.tables_view(ot)
+    n = w.tokens - w.tokens // w.group_tokens
+    rng = np.random.default_rng(9)
+    tails = np.concatenate([np.arange(0, 24), np.arange(40, 64)])
+    edges = np.resize(np.array([23, 24, 39, 40, 0, 63, 32, 31]), n)
+    inner = np.resize(np.array([24, 39]), n)
+    plan = {(0, 5): rng.choice(tails, n), (0, 70): edges, (1, 3): inner, (1, 127): rng.choice(tails, n)}
+    k2, v2 = k.copy(), v.copy()
+    for (kv, c), syms in plan.items():
+        plant_symbols(k2 if kv == 0 else v2, tv, kv, 0, c, 0, syms, w.group_tokens)
+    for ch in range(w.n_chunks):
+        _, got = oracle.chunk_symbols(ot, k2, v2, ch, 0)
+        for (kv, c), syms in plan.items():
+            col = got[kv, 0, :, c]
+            assert np.array_equal(col[col != 255], syms[ch * 900:(ch + 1) * 900]), ("planting failed", kv, c)
+    kd2, vd2 = gu.to_dev(k2), gu.to_dev(v2)
+    dblobs, obs = [], []
+    for ch in range(w.n_chunks):
+        dblob, gb = gu.gpu_encode(tab, kd2, vd2, ch, 0)
+        ob = oracle.encode_chunk(ot, k2, v2, ch, 0)
+        assert gb == ob, ("blob differs", ch, gu.first_difference(gb, ob))
+        dblobs.append(dblob)
+        obs.append(ob)
+    ko, vo, bad = gu.oracle_decode(ot, obs, k.shape)
+    assert not bad
+    kg, vg, st = gu.gpu_decode(tab, dblobs, k.shape)  # both chunks in one workgroup
+    assert st == 0 and gu.same_bits(kg, ko) and gu.same_bits(vg, vo)
+    for ch in range(w.n_chunks):  # one chunk per workgroup
+        kg, vg, st = gu.gpu_decode(tab, [dblobs[ch]], k.shape)
+        rk, rv, _ = gu.oracle_decode(ot, [obs[ch]], k.shape)
+        assert st == 0 and gu.same_bits(kg, rk) and gu.same_bits(vg, rv), ch
