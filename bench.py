@@ -794,7 +794,8 @@ def _load_record(path):
 
 def record_valu(path, workload, counter_csvs, agent_csv):
     """Store the decoder's VALU issue for `workload`: SQ_INSTS_VALU and
-    GRBM_GUI_ACTIVE per decoder dispatch (averaged over its dispatches), the
+    GRBM_GUI_ACTIVE per decoder dispatch (averaged over its dispatches; with
+    SQ_INSTS_LDS and SQ_LDS_BANK_CONFLICT when the files hold them), the
     dispatch's duration from its timestamps, and the device's SIMD and XCD
     counts and peak engine clock from the agent file.  A wave64 VALU
     instruction takes 4 cycles of its SIMD, so
@@ -820,6 +821,8 @@ def record_valu(path, workload, counter_csvs, agent_csv):
         return sum(v) / len(v)
 
     insts, grbm = mean("SQ_INSTS_VALU"), mean("GRBM_GUI_ACTIVE")
+    lds = {c: mean(c) for c in ("SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT")
+           if any(k[1] == c for k in per)}
     launch_ns = sum(dur.values()) / len(dur)
     agent = None
     with open(agent_csv, newline="") as f:
@@ -843,6 +846,9 @@ def record_valu(path, workload, counter_csvs, agent_csv):
         "peak_clock_GHz": peak_ghz,
         "issue_frac_at_peak_clock": insts * 4 / (simds * peak_ghz * launch_ns),
     }
+    if lds:
+        rec["workloads"][workload]["valu"]["lds_insts_per_launch"] = lds.get("SQ_INSTS_LDS")
+        rec["workloads"][workload]["valu"]["lds_bank_conflict_cycles_per_launch"] = lds.get("SQ_LDS_BANK_CONFLICT")
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
@@ -862,6 +868,10 @@ def decode_valu(path, workload, wave_symbols):
         return None
     out = {k: round(v[k], 4) for k in ("busy_frac", "clock_GHz", "peak_clock_GHz", "issue_frac_at_peak_clock")}
     out["insts_per_symbol"] = round(v["valu_insts_per_launch"] / wave_symbols, 2) if wave_symbols else None
+    if v.get("lds_insts_per_launch") is not None and wave_symbols:
+        out["lds_insts_per_symbol"] = round(v["lds_insts_per_launch"] / wave_symbols, 2)
+    if v.get("lds_bank_conflict_cycles_per_launch") is not None:
+        out["lds_bank_conflict_cycles"] = v["lds_bank_conflict_cycles_per_launch"]
     return out
 
 
