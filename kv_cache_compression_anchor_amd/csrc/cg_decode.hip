@@ -129,11 +129,12 @@ __device__ __forceinline__ uint64_t carry_mask(uint32_t a, uint32_t b) {
 // s is the largest symbol with r cum[s] <= code.  Delta symbols crowd around
 // the zero delta (symbol 32), so the search first bisects the 16 symbols
 // [24, 40) only: the root cum[32] and the second level's cum[28] and cum[36]
-// are in registers, then two levels from LDS.  The result is the answer exactly when code - r cum[s] lies in
-// [0, r freq[s]), i.e. when ~(code - r cum[s]) + r freq[s] carries out of 32
-// bits; a lane whose symbol lies outside the window (or whose stream is
-// corrupt) fails that test, and then the wave redoes the symbol with the full
-// six-level bisection (valid lanes find the same symbol again).
+// are in registers, then two levels from LDS.  The result is the answer
+// exactly when code - r cum[s] lies in [0, r freq[s]), i.e. when
+// ~(code - r cum[s]) + r freq[s] carries out of 32 bits; a lane whose symbol
+// lies outside the window (or whose stream is corrupt) fails that test, and
+// then the wave redoes the symbol with the full six-level bisection (valid
+// lanes find the same symbol again).
 __device__ __forceinline__ uint32_t search(uint32_t& ncode, uint32_t& range, uint32_t& sh,
                                            uint32_t lane_addr, uint32_t key32, uint32_t key28,
                                            uint32_t key36) {
