@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--decode-reps", type=int, default=1,
                     help="timed decode launches per step (the selection is decoded this many times)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--repeat-decodes", type=int, default=10,
+                    help="after the timed steps, decodes of the last selection right after a decode "
+                         "of it (roofline.repeat_decode_ms); 0 skips them")
     ap.add_argument("--cpu-sample-seconds", type=float, default=10.0,
                     help="the oracle decodes the selection repeatedly for about this long")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -200,7 +203,7 @@ def main():
     blobs_last = [bufs[(c, q)][: sizes[(c, q)]] for c, q in enumerate(sel)]
     infos_last = [cg.cg_chunk_info_parse(b[:64].cpu()) for b in blobs_last]
     rep_ms = []
-    for i in range(11):
+    for i in range(args.repeat_decodes + 1 if args.repeat_decodes > 0 else 0):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         queue_ahead(torch, stream)
         e0.record(stream)
@@ -211,7 +214,7 @@ def main():
             rep_ms.append(e0.elapsed_time(e1))
     if int(status.item()) != 0:
         raise SystemExit("repeated decode reported a corrupt stream")
-    rep_avg_ms = sum(rep_ms) / len(rep_ms)
+    rep_avg_ms = sum(rep_ms) / len(rep_ms) if rep_ms else None
     copy_gbps = copy_bandwidth(torch, dev, stream)
     value = fp16_bytes / (dec_avg_ms * 1e-3) / 1e9
     achieved = (fp16_bytes + sel_blob_bytes) / (dec_avg_ms * 1e-3) / 1e9
@@ -282,9 +285,9 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "copy_GBps": round(copy_gbps, 1), "frac_of_copy": round(achieved / copy_gbps, 4),
                      "valu_issue": valu,
-                     "repeat_decode_ms": round(rep_avg_ms, 4),
+                     "repeat_decode_ms": round(rep_avg_ms, 4) if rep_avg_ms else None,
                      "repeat_frac": round((fp16_bytes + sel_blob_bytes) / (rep_avg_ms * 1e-3) / 1e9
-                                          / HBM_PEAK_GBPS, 4)},
+                                          / HBM_PEAK_GBPS, 4) if rep_avg_ms else None},
         "cpu_baseline": cpu,
         "encode_roofline": {"bound": "hbm", "kernel": f"k_encode + k_pack (all {len(sizes)} blobs)",
                             "achieved": round(enc_achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -362,6 +362,12 @@ int enqueue_decode(const cg_tables* h, int n, const void* const* blobs, const cg
     }
     a.n_groups = ngrp;
     a.waves = waves;
+    // a warming wave where it pays and costs no decoding wave: two chunks per
+    // workgroup (4 decoding waves, 26.9 KB of LDS, six workgroups per CU: 30 of
+    // a CU's 32 wave slots with it); with three or four chunks it would take
+    // slots the decoding waves fill, and one-chunk launches (the register-buffer
+    // kernel) decoded no faster with it
+    a.warm_wave = waves == 2 ? 1 : 0;
     HIP_TRY(launch_decode(a, st), "decode launch");
   }
   return CG_OK;

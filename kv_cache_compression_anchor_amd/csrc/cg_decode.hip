@@ -192,7 +192,47 @@ struct Lane {
   uint32_t tok0;
 };
 
-// Stages the tables and sets up the lane; false for a lane without a stream.
+// The warming wave of a workgroup: reads one word of every 64 bytes of the
+// block's streams of each chunk and kv (a contiguous byte range of the blob;
+// its first 64 KB), 16 loads in flight at a time.  A lane fetches its stream
+// 16 bytes at a time and needs the rest of a cache line only several groups
+// later, when the line has often left the L2; read ahead of the decoding waves
+// by a wave of its own (whose waits do not hold them up), the lines are served
+// by the memory-side cache instead of HBM.  Loads past a range point past the
+// blob's end (no memory access).
+__device__ __forceinline__ void warm_block(const DecodeArgs& a, int grp, int l, int cb, int lane) {
+  uint32_t x = 0;
+  for (int w = 0; w < 4; w++) {
+    const int ci = a.groups[grp].chunk[w];
+    if (ci < 0) continue;
+    const DecChunk ch = a.chunks[ci];
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)ch.blob, 0, (int)ch.blob_bytes, kBufRsrcWord3);
+    for (int kv = 0; kv < 2; kv++) {
+      const int row = kv * a.L + l;
+      const uint32_t len_base = ch.off_len + 2u * (uint32_t)row * (uint32_t)a.C;
+      uint32_t before = 0;
+      for (int j = lane; j < cb * kLanes; j += kLanes) before += ld16(rs, len_base + 2u * j);
+      const int c = cb * kLanes + lane;
+      uint32_t mine = c < a.C ? ld16(rs, len_base + 2u * c) : 0u;
+      for (int o = 32; o; o >>= 1) {
+        before += __shfl_xor(before, o);
+        mine += __shfl_xor(mine, o);
+      }
+      const uint32_t start = ld32(rs, 64u + 4u * row) + before;  // words into the payload
+      const uint32_t lo = (ch.off_pay + 4u * start) & ~63u;
+      const uint32_t hi = ch.off_pay + 4u * (start + mine);
+      const uint32_t n = __builtin_amdgcn_readfirstlane(hi > lo ? (hi - lo + 4095u) >> 12 : 0u);
+#pragma unroll
+      for (uint32_t k = 0; k < 16; k++)
+        x ^= ld32(rs, k < n ? lo + (k << 12) + 64u * (uint32_t)lane : 0xFFFFFFF0u);
+    }
+  }
+  if (x & a.sink_mask) atomicOr(a.status, 4u);
+}
+
+// Stages the tables and sets up the lane; false for a lane without a stream
+// (and for the warming wave, after its reads).
 template <bool PG>
 __device__ __forceinline__ bool setup(const DecodeArgs& a, int wave, int lane, Lane& s) {
   auto tab = lds_at<uint32_t>(0);
@@ -213,6 +253,10 @@ __device__ __forceinline__ bool setup(const DecodeArgs& a, int wave, int lane, L
     }
   }
   __syncthreads();
+  if (a.warm_wave && wave == 2 * a.waves) {
+    warm_block(a, grp, l, cb, lane);
+    return false;
+  }
   const int kv = wave & 1;
   const int ci = a.groups[grp].chunk[wave >> 1];
   if (ci < 0) return false;
@@ -653,7 +697,7 @@ namespace {
 template <bool PG>
 void launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   const unsigned blocks = (unsigned)(a.n_groups * a.L * a.nblk);
-  const dim3 grid(blocks), block(2 * kLanes * a.waves);
+  const dim3 grid(blocks), block(2 * kLanes * a.waves + (a.warm_wave ? kLanes : 0));
   if (a.waves == 1) {  // one chunk per workgroup: small rings, eight workgroups per CU
     const size_t lds = reg_ring_base() + (size_t)2 * reg_ring_bytes();
     if (a.G == 10)

@@ -149,6 +149,12 @@ struct DecodeArgs {
   uint16_t* k_out;  // [L][T][C], or when paged the pools [L][num_pages][page][C]
   uint16_t* v_out;
   uint32_t* status;
+  // 1: the workgroups have one more wave, which only reads the streams of its
+  // block ahead of the decoding waves (to warm the caches); 0: no such wave
+  int warm_wave;
+  // always zero: the warming wave ANDs the values it read with it, so that its
+  // loads are kept without their values deciding anything
+  uint32_t sink_mask;
   // paged output: context token t goes to row t mod page of page
   // block_table[t / page], page = 1 << page_shift
   int paged;
