@@ -300,7 +300,7 @@ int enqueue_decode(const cg_tables* h, int n, const void* const* blobs, const cg
                    void* k_out, void* v_out, uint32_t* status, hipStream_t st,
                    const PagedOut* pg = nullptr) {
   const DevTables& t = h->t;
-  // chunks grouped by quality, up to 4 per workgroup (one wave each)
+  // chunks grouped by quality, up to 4 per workgroup (one wave per chunk and kv)
   std::vector<int> byq[3];
   for (int i = 0; i < n; i++) byq[infos[i].quality].push_back(i);
   std::vector<std::vector<int>> groups;
