@@ -63,7 +63,9 @@ enum { CG_Q_H = 0, CG_Q_M = 1, CG_Q_L = 2 }; /* quality levels (CacheGen blog 2.
  * l < layer_group_end[g]; quality q multiplies the step by quality_mult[q]. */
 typedef struct {
   int32_t layers, tokens, channels; /* each of K and V is [layers][tokens][channels] */
-  int32_t chunk_tokens;             /* 1 .. 65536 (1536 in the pages' setting) */
+  int32_t chunk_tokens;             /* 1 .. 65536 (1536 in the pages' setting); one chunk of
+                                       one layer, min(chunk_tokens, tokens) x channels x 2
+                                       bytes, must be below 4 GiB */
   int32_t group_tokens;             /* 1 .. chunk_tokens (10 in the pages' setting) */
   int32_t n_layer_groups;           /* 1 .. 3 */
   int32_t layer_group_end[3];       /* exclusive ends, increasing, last == layers */
@@ -157,7 +159,10 @@ int cg_encode_batch(const cg_tables* tables, const void* k_dev, const void* v_de
                     const int32_t* chunks, const int32_t* qualities, void* const* outs_dev,
                     const size_t* caps, size_t* out_lens, void* stream);
 
-/* Parses and checks a blob header from host memory (len >= 64). Host only. */
+/* Parses and checks a blob header from host memory (len >= 64). Host only.
+ * CG_E_INVAL for a header that is not CGK1 v1, whose fields disagree with each
+ * other, whose blob would exceed 4 GiB, or whose chunk of one layer
+ * (chunk_tokens x channels x 2 bytes) is 4 GiB or more. */
 int cg_chunk_info_parse(const void* blob_host, size_t len, cg_chunk_info* out);
 
 /* Decodes n blobs (device addresses blobs_dev[i]) into K/V fp16

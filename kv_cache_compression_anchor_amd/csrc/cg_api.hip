@@ -75,6 +75,11 @@ int check_params(const cg_params* p) {
     return fail(CG_E_INVAL, "chunk_tokens must be in 1..65536");
   if (p->group_tokens < 1 || p->group_tokens > p->chunk_tokens)
     return fail(CG_E_INVAL, "group_tokens must be in 1..chunk_tokens");
+  // one chunk of one (kv, layer) row is addressed through 32-bit buffer ranges
+  // and row offsets (token row x 2 C bytes): it must stay below 4 GiB
+  if ((uint64_t)std::min(p->chunk_tokens, p->tokens) * (uint64_t)p->channels * 2u >= (1ull << 32))
+    return fail(CG_E_INVAL, "a chunk of one layer (chunk_tokens x channels x 2 bytes) must be "
+                            "smaller than 4 GiB");
   if (p->n_layer_groups < 1 || p->n_layer_groups > 3)
     return fail(CG_E_INVAL, "n_layer_groups must be 1..3");
   int prev = 0;
@@ -270,6 +275,9 @@ int parse_info(const uint8_t* b, size_t len, cg_chunk_info* o) {
       o->n_groups != (o->chunk_tokens + o->group_tokens - 1) / o->group_tokens ||
       o->payload_words > 0x3FFFFFFFu)
     return fail(CG_E_INVAL, "inconsistent blob header");
+  if ((uint64_t)o->chunk_tokens * (uint64_t)o->channels * 2u >= (1ull << 32))
+    return fail(CG_E_INVAL, "a chunk of one layer (chunk_tokens x channels x 2 bytes) must be "
+                            "smaller than 4 GiB");
   const BlobLayout bl = blob_layout(o->layers, o->channels, o->n_groups);
   o->blob_bytes = blob_bytes(bl, o->payload_words);
   if (o->blob_bytes > 0xFFFFFFFFull) return fail(CG_E_INVAL, "blob larger than 4 GiB");

@@ -193,7 +193,8 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
   const size_t pi = ((size_t)kv * a.L + l) * a.C + c;
   const float scale_a = a.scale_a[pi], inv_a = a.inv_a[pi], inv_step = B.inv_step[pi];
   // the chunk's rows of this (kv, layer): the lane's channel is the vector
-  // offset, the token row a scalar offset; rows past the chunk read as zero
+  // offset, the token row a scalar offset.  The scalar offset is outside the
+  // buffer's range check, so no load may name a row at or past tc.
   const uint32_t row_bytes = 2u * (uint32_t)a.C;
   const __amdgpu_buffer_rsrc_t xin = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((kv ? a.v : a.k) + ((size_t)l * a.T + B.t0) * a.C), 0,
@@ -231,12 +232,17 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
   };
 
   int g = 0;
-  if constexpr (GS > 0) {
-    const int nfull = B.tc / GS;
-    uint32_t xa[GS], xb[GS];
-    auto load = [&](uint32_t (&xv)[GS], int gg) {
+  const int nfull = GS > 0 ? B.tc / GS : 0;
+  if (GS > 0 && nfull > 0) {
+    constexpr int NG = GS > 0 ? GS : 1;
+    uint32_t xa[NG], xb[NG];
+    // A prefetch of a group past the last full one is never coded (the loop
+    // below ends first); it re-reads the last full group instead, so every
+    // row read lies inside the chunk.
+    auto load = [&](uint32_t (&xv)[NG], int gg) {
+      const int gl = min(gg, nfull - 1);
 #pragma unroll
-      for (int j = 0; j < GS; j++) xv[j] = ld_half(xin, lane_off, (uint32_t)(gg * GS + j) * row_bytes);
+      for (int j = 0; j < NG; j++) xv[j] = ld_half(xin, lane_off, (uint32_t)(gl * NG + j) * row_bytes);
     };
     load(xa, 0);
     load(xb, 1);
@@ -254,12 +260,12 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
       if (prio && (g >> 1) == p1) __builtin_amdgcn_s_setprio(2);
       if (prio && (g >> 1) == p2) __builtin_amdgcn_s_setprio(1);
       if (prio && (g >> 1) == p3) __builtin_amdgcn_s_setprio(0);
-      code_group(g, GS, [&](int j) { return xa[j]; });
+      code_group(g, NG, [&](int j) { return xa[j]; });
       load(xa, g + 2);
-      code_group(g + 1, GS, [&](int j) { return xb[j]; });
+      code_group(g + 1, NG, [&](int j) { return xb[j]; });
       load(xb, g + 3);
     }
-    if (g < nfull) code_group(g++, GS, [&](int j) { return xa[j]; });
+    if (g < nfull) code_group(g++, NG, [&](int j) { return xa[j]; });
   }
   for (; g < B.ng; g++) {
     const int ta = g * a.G;

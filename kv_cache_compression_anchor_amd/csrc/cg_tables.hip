@@ -195,7 +195,8 @@ __global__ __launch_bounds__(256) void k_histogram(HistArgs a) {
     const float is1 = NQ > 1 ? a.inv_step[1][pi] : 1.0f;
     const float is2 = NQ > 2 ? a.inv_step[2][pi] : 1.0f;
     // the chunk's rows of this layer: channel as the vector offset, token row as
-    // a scalar offset; rows past the chunk read as zero
+    // a scalar offset.  The scalar offset is outside the buffer's range check,
+    // so no load may name a row at or past tc.
     const uint32_t row_bytes = 2u * (uint32_t)a.C;
     const __amdgpu_buffer_rsrc_t xin = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.x + ((size_t)l * a.T + t0) * a.C), 0, (int)((uint32_t)tc * row_bytes),
@@ -221,25 +222,30 @@ __global__ __launch_bounds__(256) void k_histogram(HistArgs a) {
       }
     };
     int g = wave;
-    if constexpr (GS > 0) {
+    const int nfull = GS > 0 ? tc / GS : 0;
+    if (GS > 0 && nfull > 0) {
       // full groups of the compile-time size, loaded one of this wave's groups
-      // ahead (the loop issues only loads to memory, so the waits are exact)
-      const int nfull = tc / GS;
-      uint32_t xa[GS], xb[GS];
-      auto load = [&](uint32_t (&xv)[GS], int gg) {
+      // ahead (the loop issues only loads to memory, so the waits are exact).
+      // A prefetch of a group past the last full one is never counted (the
+      // loop ends first); it re-reads the last full group instead, so every
+      // row read lies inside the chunk.
+      constexpr int NG = GS > 0 ? GS : 1;
+      uint32_t xa[NG], xb[NG];
+      auto load = [&](uint32_t (&xv)[NG], int gg) {
+        const int gl = min(gg, nfull - 1);
 #pragma unroll
-        for (int j = 0; j < GS; j++) xv[j] = ld(gg * GS + j);
+        for (int j = 0; j < NG; j++) xv[j] = ld(gl * NG + j);
       };
       load(xa, g);
       load(xb, g + 4);
       for (; g + 4 < nfull; g += 8) {
-        group(GS, [&](int j) { return xa[j]; });
+        group(NG, [&](int j) { return xa[j]; });
         load(xa, g + 8);
-        group(GS, [&](int j) { return xb[j]; });
+        group(NG, [&](int j) { return xb[j]; });
         load(xb, g + 12);
       }
       if (g < nfull) {
-        group(GS, [&](int j) { return xa[j]; });
+        group(NG, [&](int j) { return xa[j]; });
         g += 4;
       }
     }

@@ -131,3 +131,37 @@ def test_tables_deserialize_validates_host_bytes(cg):
         mutate(bad)
         buf = ctypes.create_string_buffer(bytes(bad), len(bad))
         assert lib.cg_tables_deserialize(buf, len(bad), ctypes.byref(out)) == cg.CG_E_INVAL
+
+
+def test_chunks_of_4_gib_per_layer_are_rejected(cg):
+    """A chunk of one (kv, layer) row is addressed through 32-bit buffer ranges
+    and token-row offsets: params and blob headers whose chunk_tokens x channels
+    x 2 bytes reach 4 GiB fail with CG_E_INVAL before any launch.  (Device
+    pointers are NULL throughout, so a shape that passes stops at the NULL check
+    and nothing is launched on any machine.)"""
+    lib = cg.lib()
+    out = ctypes.c_void_p()
+
+    def build_msg(**kw):
+        p = cg.make_params(**kw)
+        rc = lib.cg_build_tables(ctypes.byref(p), None, None, None, ctypes.byref(out))
+        assert rc == cg.CG_E_INVAL
+        return cg.cg_last_error()
+
+    base = dict(layers=1, tokens=65536, channels=65536, chunk_tokens=65536, group_tokens=10,
+                layer_group_end=(1,), layer_step=(0.5,))
+    assert "4 GiB" in build_msg(**base)
+    assert "4 GiB" in build_msg(**dict(base, chunk_tokens=32768, tokens=40000))
+    # just below the limit the shape passes and the call stops at the NULL pointers
+    assert "NULL" in build_msg(**dict(base, chunk_tokens=32767))
+    # the context bounds the chunk too: a short context with a large chunk size passes
+    assert "NULL" in build_msg(**dict(base, tokens=100))
+    # a blob header naming such a chunk
+    hdr = np.zeros(16, np.uint32)
+    hdr[:12] = [0x314B4743, 1, 1, 65536, 65536, 0, 65536, 10, (65536 + 9) // 10, 0, 0, 15]
+    with pytest.raises(cg.CgError) as e:
+        cg.cg_chunk_info_parse(hdr.tobytes())
+    assert e.value.code == cg.CG_E_INVAL and "4 GiB" in str(e.value)
+    hdr[3] = 32767
+    info = cg.cg_chunk_info_parse(hdr.tobytes())
+    assert info.chunk_tokens == 65536 and info.channels == 32767
