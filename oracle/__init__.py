@@ -71,6 +71,7 @@ def lib():
         sigs = {
             "cgo_f16_to_f32_array": (None, [P, P, I64]),
             "cgo_f32_to_f16_array": (None, [P, P, I64]),
+            "cgo_dequant_delta_array": (None, [P, P, P, P, I64]),
             "cgo_rc_bound": (SZ, [I64]),
             "cgo_rc_encode": (I, [P, I64, P, I, P, SZ, C.POINTER(SZ)]),
             "cgo_rc_decode": (I, [P, SZ, I64, P, I, P, C.POINTER(SZ), C.POINTER(I)]),
@@ -127,6 +128,17 @@ def f32_to_f16(x: np.ndarray) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float32)
     out = np.empty(x.shape, np.uint16)
     lib().cgo_f32_to_f16_array(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def dequant_delta(sym, step, ahat) -> np.ndarray:
+    """Delta-token reconstruction: binary16 bits of the value nearest to the
+    exact ahat + (sym - 32) * step, ties to even (elementwise)."""
+    s, st, a = np.broadcast_arrays(np.asarray(sym, np.uint8), np.asarray(step, np.float32),
+                                   np.asarray(ahat, np.float32))
+    s, st, a = (np.ascontiguousarray(x) for x in (s, st, a))
+    out = np.empty(s.shape, np.uint16)
+    lib().cgo_dequant_delta_array(_ptr(s), _ptr(st), _ptr(a), _ptr(out), s.size)
     return out
 
 

@@ -302,10 +302,71 @@ static uint8_t quant_delta(float x, float ahat, float inv_step) {
   return (uint8_t)((int)r + 32);
 }
 
-/* reconstruction: y = (ahat - 32*step) + s*step, each fused, then binary16 */
+/* The error-free sum of two binary64 values (Knuth's TwoSum): s + *err equals
+ * a + b exactly, s being the binary64 sum rounded to nearest. */
+static double two_sum(double a, double b, double* err) {
+  double s = a + b;
+  double bp = s - a;
+  double ap = s - bp;
+  *err = (a - ap) + (b - bp);
+  return s;
+}
+
+/* Bits of a non-negative value that binary16 represents exactly (65536, one
+ * past the largest finite value, is infinity). */
+static uint16_t f16_bits_exact(double v) {
+  if (v >= 65536.0) return 0x7C00;
+  if (v < ldexp(1.0, -14)) return (uint16_t)(v * 16777216.0); /* subnormal: v / 2^-24 */
+  int e2;
+  double m = frexp(v, &e2);                                      /* v = m 2^e2, m in [0.5, 1) */
+  return (uint16_t)(((e2 - 1 + 15) << 10) | ((int)ldexp(m, 11) - 1024));
+}
+
+/* The binary16 value nearest to the real number S + e, ties to even, where S
+ * is binary64 and e the exact error of the binary64 sum that gave S (so e is
+ * at most half a binary64 ulp of S and S + e is the exact value).  Written
+ * from the format's definition: the magnitude |S + e| lies between two
+ * consecutive multiples n q and (n + 1) q of the binary16 quantum q of its
+ * binade (2^-24 below 2^-14); the nearer one is taken, and at the midpoint the
+ * sign of e decides, or, when e is zero, the even n. */
+static uint16_t f16_nearest(double S, double e) {
+  uint16_t sign = 0;
+  if (S < 0.0 || (S == 0.0 && e < 0.0)) {
+    sign = 0x8000;
+    S = -S;
+    e = -e;
+  }
+  if (S > 65520.0 || (S == 65520.0 && e >= 0.0)) return sign | 0x7C00; /* past 65504's half-way */
+  double q;
+  if (S < ldexp(1.0, -14)) {
+    q = ldexp(1.0, -24);
+  } else {
+    int e2;
+    frexp(S, &e2);                 /* S in [2^(e2-1), 2^e2) */
+    q = ldexp(1.0, e2 - 1 - 10);
+  }
+  double n = floor(S / q);         /* S / q is an exact scaling */
+  double rem = S - n * q;          /* exact: both are multiples of S's binary64 ulp */
+  double half = q / 2.0;
+  int up = rem > half || (rem == half && (e > 0.0 || (e == 0.0 && fmod(n, 2.0) == 1.0)));
+  return sign | f16_bits_exact((n + (up ? 1.0 : 0.0)) * q);
+}
+
+/* Reconstruction of a delta token (CacheGen blog, section 2.1: deltas are taken
+ * against the quantised anchor): the binary16 value nearest to the exact real
+ * number ahat + (s - 32) * step, ties to even.  (s - 32) * step is exact in
+ * binary64 (6 by 24 significant bits); the sum's rounding error is carried
+ * along exactly. */
 static uint16_t dequant_delta(uint8_t s, float step, float ahat) {
-  float base = fmaf(-32.0f, step, ahat);
-  return cgo_f32_to_f16(fmaf((float)s, step, base));
+  double p = (double)((int)s - 32) * (double)step;
+  double err;
+  double S = two_sum((double)ahat, p, &err);
+  return f16_nearest(S, err);
+}
+
+void cgo_dequant_delta_array(const uint8_t* s, const float* step, const float* ahat,
+                             uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; i++) out[i] = dequant_delta(s[i], step[i], ahat[i]);
 }
 
 /* ------------------------------------------------------------------------- */

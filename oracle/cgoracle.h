@@ -43,6 +43,10 @@ float cgo_f16_to_f32(uint16_t h);
 uint16_t cgo_f32_to_f16(float f);
 void cgo_f16_to_f32_array(const uint16_t* in, float* out, int64_t n);
 void cgo_f32_to_f16_array(const float* in, uint16_t* out, int64_t n);
+/* reconstruction of delta tokens: the binary16 nearest to the exact
+ * ahat + (s - 32) * step, ties to even */
+void cgo_dequant_delta_array(const uint8_t* s, const float* step, const float* ahat,
+                             uint16_t* out, int64_t n);
 
 /* generic range coder, P = 15, alphabet of nsym <= 256 symbols */
 size_t cgo_rc_bound(int64_t n);
