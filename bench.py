@@ -973,6 +973,22 @@ def cpu_model():
     return "unknown"
 
 
+def cpu_threads():
+    """Threads for the oracle: every core this process may run on (its CPU
+    affinity), capped by OMP_NUM_THREADS where the environment sets it (the CPU
+    share a job on this host is given); with the host's own counts, so the
+    baseline says what it ran on."""
+    host = os.cpu_count() or 1
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = host
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    threads = min(allowed, int(cap)) if cap.isdigit() and int(cap) > 0 else allowed
+    return max(1, threads), {"host_cores": host, "affinity_cores": allowed,
+                             "omp_num_threads": int(cap) if cap.isdigit() else None}
+
+
 def cpu_baseline(w, k, v, tab, bufs, sizes, sel, seconds):
     """The oracle decoding the selection (the same blobs the GPU decodes) on this
     host's cores, chunk after chunk, until about `seconds` have passed; GB/s of
@@ -981,7 +997,7 @@ def cpu_baseline(w, k, v, tab, bufs, sizes, sel, seconds):
 
     import kv_cache_compression_anchor_amd as cg
     import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads, host = cpu_threads()
     t = cg.cg_tables_serialize(tab)
     ko = np.zeros_like(k)
     vo = np.zeros_like(v)
@@ -1008,7 +1024,7 @@ def cpu_baseline(w, k, v, tab, bufs, sizes, sel, seconds):
             "sample": f"oracle decode of {n} chunk blobs of the selection "
                       f"({n // len(blobs)}+ passes, {2 * w.layers * tok * w.channels} elements, "
                       f"{dt:.1f} s)",
-            "value_1_thread": round(one, 4), "cpu_model": cpu_model()}
+            "value_1_thread": round(one, 4), "cpu_model": cpu_model(), **host}
 
 
 def cpu_baseline_encode(w, k, v, tab, seconds):
@@ -1017,7 +1033,7 @@ def cpu_baseline_encode(w, k, v, tab, seconds):
     per blob)."""
     import kv_cache_compression_anchor_amd as cg
     import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads, host = cpu_threads()
     t = cg.cg_tables_serialize(tab)
     n = 0
     elems = 0
@@ -1033,7 +1049,7 @@ def cpu_baseline_encode(w, k, v, tab, seconds):
             break
     return {"value": round(2 * elems / dt / 1e9, 4), "unit": "GB/s of fp16 in", "cores": threads,
             "kind": "oracle",
-            "sample": f"oracle encode of {n} chunk blobs ({elems} elements, {dt:.1f} s)"}
+            "sample": f"oracle encode of {n} chunk blobs ({elems} elements, {dt:.1f} s)", **host}
 
 
 if __name__ == "__main__":

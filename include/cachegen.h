@@ -67,7 +67,11 @@ typedef struct {
                                        one layer, min(chunk_tokens, tokens) x channels x 2
                                        bytes, must be below 4 GiB */
   int32_t group_tokens;             /* 1 .. chunk_tokens (10 in the pages' setting) */
-  int32_t n_layer_groups;           /* 1 .. 3 */
+  int32_t n_layer_groups;           /* 1 .. 3, or 0 for the default: three groups with ends
+                                       floor(10 L / 32), floor(20 L / 32), L (the pages'
+                                       layers 1-10 / 11-20 / 21-32 scaled to L >= 4 layers),
+                                       layer_step[0..2] their steps; layer_group_end is then
+                                       ignored and cg_tables_params reports the ends used */
   int32_t layer_group_end[3];       /* exclusive ends, increasing, last == layers */
   float layer_step[3];              /* delta step per layer group, channel-std units */
   float quality_mult[3];            /* step multiplier of H, M, L */

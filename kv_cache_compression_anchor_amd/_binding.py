@@ -134,14 +134,13 @@ def _dev_ptr(t, dtype=None, what="tensor"):
 def make_params(layers, tokens, channels, chunk_tokens=1536, group_tokens=10,
                 layer_group_end=None, layer_step=(0.5, 1.0, 1.5), quality_mult=(1.0, 1.5, 2.5),
                 quality_mask=1) -> cg_params:
-    if layer_group_end is None:
-        layer_group_end = (layers * 10 // 32, layers * 20 // 32, layers)
     p = cg_params()
     p.layers, p.tokens, p.channels = layers, tokens, channels
     p.chunk_tokens, p.group_tokens = chunk_tokens, group_tokens
-    p.n_layer_groups = len(layer_group_end)
+    ends = tuple(layer_group_end) if layer_group_end is not None else ()
+    p.n_layer_groups = len(ends)  # 0: the library's default split
     for i in range(3):
-        p.layer_group_end[i] = layer_group_end[i] if i < len(layer_group_end) else 0
+        p.layer_group_end[i] = ends[i] if i < len(ends) else 0
         p.layer_step[i] = layer_step[i] if i < len(layer_step) else 0.0
         p.quality_mult[i] = quality_mult[i]
     p.quality_mask = quality_mask

@@ -65,6 +65,23 @@ struct DeviceGuard {
   }
 };
 
+// n_layer_groups = 0 asks for the default split: the pages' three groups of a
+// 32-layer model (layers 1-10, 11-20, 21-32) scaled to L layers, ends
+// floor(10 L / 32), floor(20 L / 32), L.  The caller's params with that split
+// filled in, or CG_E_INVAL when L is too small for three non-empty groups.
+int resolve_params(const cg_params* in, cg_params* out) {
+  if (!in) return fail(CG_E_INVAL, "params is NULL");
+  *out = *in;
+  if (in->n_layer_groups != 0) return CG_OK;
+  if (in->layers < 4)
+    return fail(CG_E_INVAL, "the default layer groups (n_layer_groups = 0) need at least 4 layers");
+  out->n_layer_groups = 3;
+  out->layer_group_end[0] = (int32_t)((int64_t)in->layers * 10 / 32);
+  out->layer_group_end[1] = (int32_t)((int64_t)in->layers * 20 / 32);
+  out->layer_group_end[2] = in->layers;
+  return CG_OK;
+}
+
 int check_params(const cg_params* p) {
   if (!p) return fail(CG_E_INVAL, "params is NULL");
   if (p->layers < 1 || p->tokens < 1 || p->channels < 1)
@@ -420,9 +437,13 @@ int cg_build_tables(const cg_params* params, const void* k_dev, const void* v_de
   return cg_build_tables_grouped(params, CG_GROUP_LAYER_CHANNEL, k_dev, v_dev, stream, out);
 }
 
-int cg_build_tables_grouped(const cg_params* params, int32_t grouping, const void* k_dev,
+int cg_build_tables_grouped(const cg_params* params_in, int32_t grouping, const void* k_dev,
                             const void* v_dev, void* stream, cg_tables** out) {
-  int rc = check_params(params);
+  cg_params resolved;
+  int rc = resolve_params(params_in, &resolved);
+  if (rc) return rc;
+  const cg_params* params = &resolved;
+  rc = check_params(params);
   if (rc) return rc;
   if (grouping < CG_GROUP_LAYER_CHANNEL || grouping > CG_GROUP_GLOBAL)
     return fail(CG_E_INVAL, "unknown table grouping");

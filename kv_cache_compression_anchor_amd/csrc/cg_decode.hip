@@ -86,6 +86,21 @@ __device__ __forceinline__ float byte1_to_float(uint32_t x) {
   return f;
 }
 
+// Binary16 bits (in the low half) of the value nearest to the exact a * b + c,
+// ties to even: v_fma_mixlo_f16 with binary32 sources rounds the exact result
+// once, to binary16.
+__device__ __forceinline__ uint32_t fma_to_half(float a, float b, float c) {
+  uint32_t d;
+  asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[0,0,0]" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
+// A delta token: the binary16 nearest to ahat + (s - 32) step, s being bits
+// 8..13 of the symbol's LDS address (s - 32 is exact in binary32).
+__device__ __forceinline__ uint32_t delta_half(uint32_t ad, float step, float ahat) {
+  return fma_to_half(byte1_to_float(ad) - 32.0f, step, ahat);
+}
+
 // The workgroup's LDS holds the K and V tables of one (layer, 64-channel block)
 // side by side: row k = [cum[k] of the 64 K streams | cum[k] of the 64 V
 // streams], 256 bytes, so the byte address of entry k of a lane is
@@ -312,8 +327,9 @@ __device__ __forceinline__ bool setup(const DecodeArgs& a, int wave, int lane, L
   return true;
 }
 
-__device__ __forceinline__ void put_half(const Lane& s, float y, uint32_t t) {
-  __builtin_amdgcn_raw_buffer_store_b16(float_to_half_bits(y), s.ro, s.lane_off, t * s.row_bytes, kStoreNT);
+// stores the binary16 in the low half of h as token row t of the lane's channel
+__device__ __forceinline__ void put_half(const Lane& s, uint32_t h, uint32_t t) {
+  __builtin_amdgcn_raw_buffer_store_b16((uint16_t)h, s.ro, s.lane_off, t * s.row_bytes, kStoreNT);
 }
 
 // ---------------------------------------------------------------------------
@@ -344,11 +360,11 @@ struct Pager {
     if (!ok && lane < te - ta) bad = 1u;
     po = ok ? ((ent << a.page_shift) | (tok & ((1u << a.page_shift) - 1u))) * s.row_bytes : kNoRow;
   }
-  __device__ __forceinline__ void put(const Lane& s, float y, uint32_t t) const {
+  __device__ __forceinline__ void put(const Lane& s, uint32_t h, uint32_t t) const {
     const uint32_t ro = (uint32_t)__builtin_amdgcn_readlane((int)po, (int)t - ta);
     const __amdgpu_buffer_rsrc_t r =
         __builtin_amdgcn_make_buffer_rsrc(s.pool, 0, ro != kNoRow ? (int)s.pool_bytes : 0, kBufRsrcWord3);
-    __builtin_amdgcn_raw_buffer_store_b16(float_to_half_bits(y), r, s.lane_off, ro, kStoreNT);
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)h, r, s.lane_off, ro, kStoreNT);
   }
 };
 
@@ -390,9 +406,9 @@ __global__ __launch_bounds__(512) void k_decode_win(DecodeArgs a) {
   Lane s;
   if (!setup<PG>(a, wave, lane, s)) return;
   Pager pg;
-  auto out = [&](uint32_t t, float y) {
-    if constexpr (PG) pg.put(s, y, t);
-    else put_half(s, y, t);
+  auto out = [&](uint32_t t, uint32_t h) {
+    if constexpr (PG) pg.put(s, h, t);
+    else put_half(s, h, t);
   };
   constexpr int RB = kWinRB;
   constexpr uint32_t M = kWinM;
@@ -423,18 +439,18 @@ __global__ __launch_bounds__(512) void k_decode_win(DecodeArgs a) {
 
   // one symbol, its new bits x (the next stream bits, most significant first);
   // returns sh and the selector that shifted them in
-  auto symbol = [&](uint32_t t, float base, uint32_t x, uint32_t& sel) -> uint32_t {
+  auto symbol = [&](uint32_t t, float ahat, uint32_t x, uint32_t& sel) -> uint32_t {
     uint32_t sh;
     const uint32_t ad = search(ncode, range, sh, s.lane_addr, s.key32, s.key28, s.key36);
     sel = shift_sel(sh);
     ncode = __builtin_amdgcn_perm(ncode, x, sel);
-    out(t, __builtin_fmaf(byte1_to_float(ad), s.step, base));
+    out(t, delta_half(ad, s.step, ahat));
     return sh;
   };
 
   // N (1..3) symbols from one 64-bit window of the stream (they take at most
   // 48 bits)
-  auto run = [&](auto n_c, uint32_t t, float base) {
+  auto run = [&](auto n_c, uint32_t t, float ahat) {
     constexpr int N = decltype(n_c)::value;
     if ((int)nc < lim) {
       // the ring has run dry (more bits taken than fetched, which typical data
@@ -463,13 +479,13 @@ __global__ __launch_bounds__(512) void k_decode_win(DecodeArgs a) {
     const uint32_t hi = __builtin_amdgcn_alignbit(w0, w1, nc);
     const uint32_t lo = __builtin_amdgcn_alignbit(w1, w2, nc);
     uint32_t sel1, sel2, sel3;
-    uint32_t tot = symbol(t, base, hi, sel1);
+    uint32_t tot = symbol(t, ahat, hi, sel1);
     if constexpr (N >= 2) {
       const uint64_t win = (((uint64_t)hi << 32) | lo) << tot;
       const uint32_t h2 = (uint32_t)(win >> 32), l2 = (uint32_t)win;
-      const uint32_t sh2 = symbol(t + 1, base, h2, sel2);
+      const uint32_t sh2 = symbol(t + 1, ahat, h2, sel2);
       tot += sh2;
-      if constexpr (N >= 3) tot += symbol(t + 2, base, __builtin_amdgcn_perm(h2, l2, sel2), sel3);
+      if constexpr (N >= 3) tot += symbol(t + 2, ahat, __builtin_amdgcn_perm(h2, l2, sel2), sel3);
     }
     nc -= tot;
   };
@@ -500,20 +516,19 @@ __global__ __launch_bounds__(512) void k_decode_win(DecodeArgs a) {
     const int anc = anc_next;
     anc_next = ld8s(s.rs, s.anc_base + (uint32_t)(g + 1) * s.C);  // past the last group: unused
     const float ahat = anchor_value(anc, s.scale_a);
-    const float base = __builtin_fmaf(-32.0f, s.step, ahat);
-    out((uint32_t)ta, ahat);
+    out((uint32_t)ta, float_to_half_bits(ahat));
     int t = ta + 1;
 #pragma unroll
     for (; t + 2 < te; t += 3) {
       __builtin_amdgcn_sched_barrier(0);
-      run(I3{}, (uint32_t)t, base);
+      run(I3{}, (uint32_t)t, ahat);
     }
     if (t + 1 < te) {
       __builtin_amdgcn_sched_barrier(0);
-      run(I2{}, (uint32_t)t, base);
+      run(I2{}, (uint32_t)t, ahat);
     } else if (t < te) {
       __builtin_amdgcn_sched_barrier(0);
-      run(I1{}, (uint32_t)t, base);
+      run(I1{}, (uint32_t)t, ahat);
     }
   };
 
@@ -567,9 +582,9 @@ __global__ __launch_bounds__(512) void k_decode_reg(DecodeArgs a) {
   Lane s;
   if (!setup<PG>(a, wave, lane, s)) return;
   Pager pg;
-  auto out = [&](uint32_t t, float y) {
-    if constexpr (PG) pg.put(s, y, t);
-    else put_half(s, y, t);
+  auto out = [&](uint32_t t, uint32_t h) {
+    if constexpr (PG) pg.put(s, h, t);
+    else put_half(s, h, t);
   };
   constexpr int RB = kRegRB;
 
@@ -599,13 +614,13 @@ __global__ __launch_bounds__(512) void k_decode_reg(DecodeArgs a) {
   int anc_next = ld8s(s.rs, s.anc_base);
 
   // one symbol: search, interval update, renormalisation, reconstruction
-  auto symbol = [&](uint32_t t, float base) {
+  auto symbol = [&](uint32_t t, float ahat) {
     uint32_t sh;
     const uint32_t ad = search(ncode, range, sh, s.lane_addr, s.key32, s.key28, s.key36);
     const uint32_t tl = left - sh;
     ncode = (ncode << sh) | __builtin_amdgcn_ubfe((uint32_t)(bb >> (tl & 63u)), 0u, sh);
     left = tl;
-    out(t, __builtin_fmaf(byte1_to_float(ad), s.step, base));
+    out(t, delta_half(ad, s.step, ahat));
   };
 
   // A lane takes a word when fewer than 32 bits remain (two symbols need at
@@ -648,8 +663,7 @@ __global__ __launch_bounds__(512) void k_decode_reg(DecodeArgs a) {
     const int anc = anc_next;
     anc_next = ld8s(s.rs, s.anc_base + (uint32_t)(g + 1) * s.C);  // past the last group: unused
     const float ahat = anchor_value(anc, s.scale_a);
-    out((uint32_t)ta, ahat);
-    const float base = __builtin_fmaf(-32.0f, s.step, ahat);
+    out((uint32_t)ta, float_to_half_bits(ahat));
     int t = ta + 1;
 #pragma unroll
     for (; t + 1 < te; t += 2) {
@@ -657,13 +671,13 @@ __global__ __launch_bounds__(512) void k_decode_reg(DecodeArgs a) {
       // leaves those two stores in flight
       __builtin_amdgcn_sched_barrier(0);
       refill();
-      symbol((uint32_t)t, base);
-      symbol((uint32_t)(t + 1), base);
+      symbol((uint32_t)t, ahat);
+      symbol((uint32_t)(t + 1), ahat);
     }
     if (t < te) {
       __builtin_amdgcn_sched_barrier(0);
       refill();
-      symbol((uint32_t)t, base);
+      symbol((uint32_t)t, ahat);
     }
   };
 

@@ -165,3 +165,18 @@ def test_chunks_of_4_gib_per_layer_are_rejected(cg):
     hdr[3] = 32767
     info = cg.cg_chunk_info_parse(hdr.tobytes())
     assert info.chunk_tokens == 65536 and info.channels == 32767
+
+
+def test_default_layer_groups_are_resolved_by_the_library(cg):
+    """layer_group_end=None leaves the split to the library (n_layer_groups = 0):
+    the binding passes no computed ends, and the library rejects a depth too
+    small for three non-empty groups before any other check."""
+    lib = cg.lib()
+    out = ctypes.c_void_p()
+    p = cg.make_params(3, 64, 128, 64, 10, None, (0.5, 1.0, 1.5))
+    assert p.n_layer_groups == 0 and list(p.layer_group_end) == [0, 0, 0]
+    assert lib.cg_build_tables(ctypes.byref(p), None, None, None, ctypes.byref(out)) == cg.CG_E_INVAL
+    assert "at least 4 layers" in cg.cg_last_error()
+    p = cg.make_params(48, 64, 128, 64, 10, None, (0.5, 1.0, 1.5))
+    assert lib.cg_build_tables(ctypes.byref(p), None, None, None, ctypes.byref(out)) == cg.CG_E_INVAL
+    assert "NULL" in cg.cg_last_error()

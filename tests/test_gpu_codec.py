@@ -457,3 +457,20 @@ def test_symbols_outside_the_search_window():
         kg, vg, st = gu.gpu_decode(tab, [dblobs[ch]], k.shape)
         rk, rv, _ = gu.oracle_decode(ot, [obs[ch]], k.shape)
         assert st == 0 and gu.same_bits(kg, rk) and gu.same_bits(vg, rv), ch
+
+
+def test_default_layer_groups_match_the_explicit_split():
+    """n_layer_groups = 0 (the binding's layer_group_end=None): the library's
+    default split of 48 layers is 15 / 30 / 48, the tables equal the oracle's
+    with those ends written out, and cg_tables_params reports them."""
+    import kv_cache_compression_anchor_amd as cg
+    w = gu.workload(layers=48, tokens=200, channels=64, chunk_tokens=200,
+                    layer_group_end=(15, 30, 48), qualities=(0,))
+    k, v = synth.gen_kv(w)
+    kd, vd = gu.to_dev(k), gu.to_dev(v)
+    p = cg.make_params(w.layers, w.tokens, w.channels, w.chunk_tokens, w.group_tokens, None,
+                       w.layer_step, w.quality_mult, w.quality_mask)
+    tab = cg.cg_build_tables(p, kd, vd)
+    assert cg.cg_tables_serialize(tab) == oracle.build_tables(oracle.params_for(w), k, v)
+    got = cg.cg_tables_params(tab)
+    assert got.n_layer_groups == 3 and list(got.layer_group_end) == [15, 30, 48]
