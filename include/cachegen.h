@@ -163,6 +163,23 @@ int cg_encode_batch(const cg_tables* tables, const void* k_dev, const void* v_de
                     const int32_t* chunks, const int32_t* qualities, void* const* outs_dev,
                     const size_t* caps, size_t* out_lens, void* stream);
 
+/* For callers that cannot allocate device memory (harnesses that forbid
+ * hipMalloc, serving loops that must not allocate): cg_encode_batch with the
+ * same arguments, results and errors, that allocates nothing.  Its encode
+ * scratch is a 256 MiB array of static device memory, one per GPU, held from
+ * the library's load until the process ends; a blob is coded over as many
+ * (kv, layer) rows at a time as fit in it, one blob after another.  A chunk
+ * whose single (kv, layer) row needs more scratch than that (about
+ * channels x 64 x chunk_tokens x 15 / 32 words) fails with CG_E_CAPACITY
+ * before any launch.  Calls on one GPU share the array: the library lets one
+ * call at a time use it and holds it until the call's stream has finished, so
+ * calls that would overlap on one GPU take turns.  Waits for the stream after
+ * every blob. */
+int cg_encode_batch_noalloc(const cg_tables* tables, const void* k_dev, const void* v_dev,
+                            int32_t n, const int32_t* chunks, const int32_t* qualities,
+                            void* const* outs_dev, const size_t* caps, size_t* out_lens,
+                            void* stream);
+
 /* Parses and checks a blob header from host memory (len >= 64). Host only.
  * CG_E_INVAL for a header that is not CGK1 v1, whose fields disagree with each
  * other, whose blob would exceed 4 GiB, or whose chunk of one layer

@@ -5,7 +5,7 @@ from ._binding import (CG_GROUP_CHANNEL, CG_GROUP_GLOBAL, CG_GROUP_LAYER,  # noq
                        CG_E_NOMEM, CG_OK, CG_Q_H, CG_Q_L, CG_Q_M, EXPORTS, LIB_PATH, CgError,
                        Tables, cg_build_tables, cg_build_tables_grouped, cg_chunk_info, cg_chunk_info_parse, cg_decode,
                        cg_decode_async, cg_decode_paged_async, cg_decode_streamed, cg_encode,
-                       cg_encode_batch,
+                       cg_encode_batch, cg_encode_batch_noalloc,
                        cg_encode_bound,
                        cg_chunk_plan_in, cg_last_error, cg_num_chunks, cg_params,
                        cg_plan_chunk, cg_tables_deserialize,

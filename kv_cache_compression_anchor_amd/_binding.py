@@ -23,7 +23,7 @@ _NAMES = {0: "CG_OK", -1: "CG_E_INVAL", -2: "CG_E_NOMEM", -3: "CG_E_HIP", -4: "C
 
 EXPORTS = ["cg_build_tables", "cg_build_tables_grouped", "cg_tables_free", "cg_tables_serialize",
            "cg_tables_deserialize", "cg_tables_id", "cg_tables_params", "cg_num_chunks", "cg_encode_bound", "cg_encode",
-           "cg_encode_batch", "cg_chunk_info_parse", "cg_decode", "cg_decode_async", "cg_decode_paged_async",
+           "cg_encode_batch", "cg_encode_batch_noalloc", "cg_chunk_info_parse", "cg_decode", "cg_decode_async", "cg_decode_paged_async",
            "cg_decode_streamed",
            "cg_plan_chunk", "cg_last_error"]
 
@@ -80,6 +80,8 @@ def lib():
             "cg_encode": (I, [P, P, P, I32, I32, P, SZ, C.POINTER(SZ), P]),
             "cg_encode_batch": (I, [P, P, P, I32, C.POINTER(I32), C.POINTER(I32), C.POINTER(P),
                                     C.POINTER(SZ), C.POINTER(SZ), P]),
+            "cg_encode_batch_noalloc": (I, [P, P, P, I32, C.POINTER(I32), C.POINTER(I32),
+                                            C.POINTER(P), C.POINTER(SZ), C.POINTER(SZ), P]),
             "cg_chunk_info_parse": (I, [P, SZ, C.POINTER(cg_chunk_info)]),
             "cg_decode": (I, [P, I32, C.POINTER(P), C.POINTER(SZ), P, P, P]),
             "cg_decode_async": (I, [P, I32, C.POINTER(P), C.POINTER(cg_chunk_info), P, P, P, P]),
@@ -250,6 +252,16 @@ def cg_encode(t: Tables, k, v, chunk: int, quality: int, out, stream=None) -> in
 def cg_encode_batch(t: Tables, k, v, chunks, qualities, outs, stream=None):
     """Encodes blob i = (chunks[i], qualities[i]) into the uint8 device tensor outs[i];
     returns the blob sizes."""
+    return _encode_batch("cg_encode_batch", t, k, v, chunks, qualities, outs, stream)
+
+
+def cg_encode_batch_noalloc(t: Tables, k, v, chunks, qualities, outs, stream=None):
+    """cg_encode_batch through the entry point that allocates nothing (static
+    device scratch); returns the blob sizes."""
+    return _encode_batch("cg_encode_batch_noalloc", t, k, v, chunks, qualities, outs, stream)
+
+
+def _encode_batch(name, t: Tables, k, v, chunks, qualities, outs, stream):
     import torch
     n = len(chunks)
     if len(qualities) != n or len(outs) != n:
@@ -261,8 +273,8 @@ def cg_encode_batch(t: Tables, k, v, chunks, qualities, outs, stream=None):
     qarr = (C.c_int32 * max(1, n))(*qualities)
     caps = (C.c_size_t * max(1, n))(*[o.numel() for o in outs])
     lens = (C.c_size_t * max(1, n))()
-    _check(lib().cg_encode_batch(t.handle, kp, vp, n, carr, qarr, _ptr_array(ops), caps, lens,
-                                 _stream(stream)))
+    _check(getattr(lib(), name)(t.handle, kp, vp, n, carr, qarr, _ptr_array(ops), caps, lens,
+                                _stream(stream)))
     return [int(x) for x in lens[:n]]
 
 

@@ -398,6 +398,118 @@ int enqueue_decode(const cg_tables* h, int n, const void* const* blobs, const cg
   return CG_OK;
 }
 
+// Arguments of an encode batch, checked before any launch.
+int check_encode_args(const cg_tables* h, const void* k_dev, const void* v_dev, int32_t n,
+                      const int32_t* chunks, const int32_t* qualities, void* const* outs_dev,
+                      const size_t* caps, size_t* out_lens) {
+  if (!h || !k_dev || !v_dev || n < 0 || (n > 0 && (!chunks || !qualities || !outs_dev ||
+                                                     !caps || !out_lens)))
+    return fail(CG_E_INVAL, "NULL argument");
+  const DevTables& t = h->t;
+  for (int i = 0; i < n; i++) {
+    if (!outs_dev[i]) return fail(CG_E_INVAL, "NULL output");
+    if (chunks[i] < 0 || chunks[i] >= n_chunks_of(t)) return fail(CG_E_INVAL, "chunk out of range");
+    if (qualities[i] < 0 || qualities[i] > 2 || !((t.mask >> qualities[i]) & 1u))
+      return fail(CG_E_MISMATCH, "quality not in the tables");
+    const ChunkGeo g = chunk_geo(t, chunks[i]);
+    if (caps[i] < blob_layout(t.L, t.C, g.ng).off_pay + 16)
+      return fail(CG_E_CAPACITY, "output smaller than the blob's fixed part");
+  }
+  return CG_OK;
+}
+
+// Scratch words of one stream: its worst-case words plus the placeholder word
+// in front of them (every chunk of the tables fits the longest chunk's bound).
+size_t stream_scratch_words(const DevTables& t) {
+  return std::max<size_t>(stream_words_bound(t.CH - (t.CH + t.G - 1) / t.G), 1) + 1;
+}
+
+// The fields of one blob of an encode launch, but for its scratch buffers.
+void init_enc_blob(EncBlob& B, const DevTables& t, int chunk, int q, void* out, size_t cap) {
+  const ChunkGeo g = chunk_geo(t, chunk);
+  B.blob = static_cast<uint8_t*>(out);
+  B.cap = cap;
+  B.t0 = g.t0;
+  B.tc = g.tc;
+  B.ng = g.ng;
+  B.q = q;
+  B.lay = blob_layout(t.L, t.C, g.ng);
+  B.img = t.img[q];
+  B.inv_step = reinterpret_cast<const float*>(t.ser + t.lay.off_inv_step[q]);
+}
+
+// The launch-wide fields of an encode launch.
+void init_enc_args(EncodeArgs& a, const cg_tables* h, const void* k_dev, const void* v_dev,
+                   size_t swb) {
+  const DevTables& t = h->t;
+  memset(&a, 0, sizeof(a));
+  a.k = static_cast<const uint16_t*>(k_dev);
+  a.v = static_cast<const uint16_t*>(v_dev);
+  a.L = t.L;
+  a.T = t.T;
+  a.C = t.C;
+  a.G = t.G;
+  a.nblk = t.nblk;
+  a.swb = swb;
+  a.scale_a = reinterpret_cast<const float*>(t.ser + t.lay.off_scale_a);
+  a.inv_a = reinterpret_cast<const float*>(t.ser + t.lay.off_inv_a);
+  a.tables_id = h->id;
+  a.row0 = 0;
+  a.nrows = 2 * t.L;
+  a.waves = 1;
+}
+
+// out_lens[i] and the call's result from blob i's status words {payload words,
+// too large, non-finite}; rc keeps the first failure.
+void finish_blob(const DevTables& t, int chunk, const uint32_t* sw, size_t* out_len, int* rc) {
+  *out_len = 0;
+  if (sw[2]) {
+    if (*rc == CG_OK) *rc = fail(CG_E_INVAL, "K/V hold a non-finite value");
+  } else if (sw[1]) {
+    if (*rc == CG_OK) *rc = fail(CG_E_CAPACITY, "blob larger than the output buffer");
+  } else {
+    *out_len = blob_bytes(blob_layout(t.L, t.C, chunk_geo(t, chunk).ng), sw[0]);
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// The static encode scratch of cg_encode_batch_noalloc: device memory that
+// exists, one copy per GPU, from the code object's load until the process
+// ends, so that the call allocates nothing.  In host code the array's name is
+// a host-side stand-in, not a device address: host code reaches the array only
+// through the address hipGetSymbolAddress returns for the current device.
+constexpr size_t kStaticScratchBytes = (size_t)256 << 20;
+static __device__ __align__(256) uint32_t scratch[kStaticScratchBytes / 4];
+
+namespace {
+
+struct StaticScratch {
+  std::mutex mu;            // held by a call until its stream has finished
+  uint32_t* ptr = nullptr;  // device address of this device's array
+};
+
+StaticScratch* static_scratch(int dev) {
+  static StaticScratch s[kMaxDevices];
+  return dev >= 0 && dev < kMaxDevices ? &s[dev] : nullptr;
+}
+
+// The device address of the array on the current device (with s->mu held):
+// looked up once per device, on the first call there.
+int static_scratch_ptr(StaticScratch* s, uint32_t** out) {
+  if (!s->ptr) {
+    uint32_t* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    s->ptr = ptr;
+  }
+  *out = s->ptr;
+  return CG_OK;
+}
+
+size_t align64w(size_t words) { return (words + 63) & ~(size_t)63; }
+
 }  // namespace
 
 extern "C" {
@@ -663,26 +775,15 @@ size_t resident_waves(int dev) {
 int cg_encode_batch(const cg_tables* ch, const void* k_dev, const void* v_dev, int32_t n,
                     const int32_t* chunks, const int32_t* qualities, void* const* outs_dev,
                     const size_t* caps, size_t* out_lens, void* stream) {
-  if (!ch || !k_dev || !v_dev || n < 0 || (n > 0 && (!chunks || !qualities || !outs_dev ||
-                                                      !caps || !out_lens)))
-    return fail(CG_E_INVAL, "NULL argument");
+  int rc = check_encode_args(ch, k_dev, v_dev, n, chunks, qualities, outs_dev, caps, out_lens);
+  if (rc) return rc;
+  if (n == 0) return CG_OK;
   cg_tables* h = const_cast<cg_tables*>(ch);
   const DevTables& t = h->t;
-  for (int i = 0; i < n; i++) {
-    if (!outs_dev[i]) return fail(CG_E_INVAL, "NULL output");
-    if (chunks[i] < 0 || chunks[i] >= n_chunks_of(t)) return fail(CG_E_INVAL, "chunk out of range");
-    if (qualities[i] < 0 || qualities[i] > 2 || !((t.mask >> qualities[i]) & 1u))
-      return fail(CG_E_MISMATCH, "quality not in the tables");
-    const ChunkGeo g = chunk_geo(t, chunks[i]);
-    if (caps[i] < blob_layout(t.L, t.C, g.ng).off_pay + 16)
-      return fail(CG_E_CAPACITY, "output smaller than the blob's fixed part");
-  }
-  if (n == 0) return CG_OK;
   DeviceGuard dg(h->dev);
   if (!dg.ok) return fail(CG_E_HIP, "cannot select the tables' device");
   std::lock_guard<std::mutex> lk(h->mu);
-  // a stream's words plus the placeholder word in front of them
-  const size_t swb = std::max<size_t>(stream_words_bound(t.CH - (t.CH + t.G - 1) / t.G), 1) + 1;
+  const size_t swb = stream_scratch_words(t);
   const size_t slot_words = (size_t)2 * t.L * t.nblk * kLanes * swb;  // whole 64-stream blocks
   // Blobs per launch: at most what the scratch budget holds.  When one more
   // launch is enough to make every launch fit the device at once (a blob is
@@ -731,34 +832,13 @@ int cg_encode_batch(const cg_tables* ch, const void* k_dev, const void* v_dev, i
   const int per_launch = (n + launches - 1) / launches;
   for (int i0 = 0; i0 < n; i0 += per_launch) {
     EncodeArgs a;
-    memset(&a, 0, sizeof(a));
-    a.k = static_cast<const uint16_t*>(k_dev);
-    a.v = static_cast<const uint16_t*>(v_dev);
-    a.L = t.L;
-    a.T = t.T;
-    a.C = t.C;
-    a.G = t.G;
-    a.nblk = t.nblk;
+    init_enc_args(a, h, k_dev, v_dev, swb);
     a.nblobs = std::min(per_launch, n - i0);
     a.prio = (size_t)a.nblobs * wpb <= cap ? 1 : 0;
-    a.swb = swb;
-    a.scale_a = reinterpret_cast<const float*>(t.ser + t.lay.off_scale_a);
-    a.inv_a = reinterpret_cast<const float*>(t.ser + t.lay.off_inv_a);
-    a.tables_id = h->id;
-    a.waves = 1;
     for (int j = 0; j < a.nblobs; j++) {
       const int i = order[i0 + j];
-      const ChunkGeo g = chunk_geo(t, chunks[i]);
       EncBlob& B = a.b[j];
-      B.blob = static_cast<uint8_t*>(outs_dev[i]);
-      B.cap = caps[i];
-      B.t0 = g.t0;
-      B.tc = g.tc;
-      B.ng = g.ng;
-      B.q = qualities[i];
-      B.lay = blob_layout(t.L, t.C, g.ng);
-      B.img = t.img[qualities[i]];
-      B.inv_step = reinterpret_cast<const float*>(t.ser + t.lay.off_inv_step[qualities[i]]);
+      init_enc_blob(B, t, chunks[i], qualities[i], outs_dev[i], caps[i]);
       B.scratch = h->scratch + (size_t)j * slot_words;
       B.lens = h->lens + (size_t)j * t.lay.n;
       B.row_words = h->row_words + (size_t)j * 2 * t.L * (1 + t.nblk);
@@ -780,17 +860,71 @@ int cg_encode_batch(const cg_tables* ch, const void* k_dev, const void* v_dev, i
   HIP_TRY(hipMemcpyAsync(h->enc_host, h->enc_status, 16 * (size_t)n, hipMemcpyDeviceToHost, st),
           "encode status");
   HIP_TRY(hipStreamSynchronize(st), "encode");
-  int rc = CG_OK;
+  rc = CG_OK;
+  for (int i = 0; i < n; i++) finish_blob(t, chunks[i], h->enc_host + 4 * (size_t)i, &out_lens[i], &rc);
+  return rc;
+}
+
+int cg_encode_batch_noalloc(const cg_tables* ch, const void* k_dev, const void* v_dev, int32_t n,
+                            const int32_t* chunks, const int32_t* qualities,
+                            void* const* outs_dev, const size_t* caps, size_t* out_lens,
+                            void* stream) {
+  int rc = check_encode_args(ch, k_dev, v_dev, n, chunks, qualities, outs_dev, caps, out_lens);
+  if (rc) return rc;
+  if (n == 0) return CG_OK;
+  const DevTables& t = ch->t;
+  // The array holds 64 status words, then for a range of (kv, layer) rows their
+  // stream lengths, row and block totals and stream words; the range is as many
+  // rows as fit, a blob is coded range after range.
+  const size_t swb = stream_scratch_words(t);
+  const size_t per_row = (size_t)t.C + 1 + t.nblk + (size_t)t.nblk * kLanes * swb;
+  const size_t fixed = 64 + 3 * 63;  // status words and the ranges' alignment
+  const size_t rows_fit = (kStaticScratchBytes / 4 - fixed) / per_row;
+  if (rows_fit < 1)
+    return fail(CG_E_CAPACITY, "one (kv, layer) row of a chunk needs " + std::to_string(4 * per_row) +
+                                   " bytes of encode scratch; the static scratch holds " +
+                                   std::to_string(kStaticScratchBytes));
+  const int rows_max = (int)std::min<size_t>(rows_fit, (size_t)2 * t.L);
+  DeviceGuard dg(ch->dev);
+  if (!dg.ok) return fail(CG_E_HIP, "cannot select the tables' device");
+  StaticScratch* ss = static_scratch(ch->dev);
+  if (!ss) return fail(CG_E_INVAL, "device index beyond the supported range");
+  std::lock_guard<std::mutex> lk(ss->mu);
+  uint32_t* base = nullptr;
+  if ((rc = static_scratch_ptr(ss, &base))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t cap = resident_waves(ch->dev);
+  uint32_t* status = base;  // words 0..3 of blob i while it is coded
+  rc = CG_OK;
   for (int i = 0; i < n; i++) {
-    const uint32_t* sw = h->enc_host + 4 * (size_t)i;
-    out_lens[i] = 0;
-    if (sw[2]) {
-      if (rc == CG_OK) rc = fail(CG_E_INVAL, "K/V hold a non-finite value");
-    } else if (sw[1]) {
-      if (rc == CG_OK) rc = fail(CG_E_CAPACITY, "blob larger than the output buffer");
-    } else {
-      out_lens[i] = blob_bytes(blob_layout(t.L, t.C, chunk_geo(t, chunks[i]).ng), sw[0]);
+    HIP_TRY(launch_zero_words(status, 4, st), "clear status");
+    for (int r0 = 0; r0 < 2 * t.L; r0 += rows_max) {
+      EncodeArgs a;
+      init_enc_args(a, ch, k_dev, v_dev, swb);
+      a.row0 = r0;
+      a.nrows = std::min(rows_max, 2 * t.L - r0);
+      a.nblobs = 1;
+      a.n_groups = 1;
+      a.groups[0].blob[0] = 0;
+      for (int w = 1; w < 4; w++) a.groups[0].blob[w] = -1;
+      a.prio = (size_t)a.nrows * t.nblk <= cap ? 1 : 0;
+      EncBlob& B = a.b[0];
+      init_enc_blob(B, t, chunks[i], qualities[i], outs_dev[i], caps[i]);
+      size_t off = 64;
+      B.lens = base + off;
+      off = align64w(off + (size_t)a.nrows * t.C);
+      B.row_words = base + off;
+      off = align64w(off + (size_t)a.nrows);
+      B.block_words = base + off;
+      off = align64w(off + (size_t)a.nrows * t.nblk);
+      B.scratch = base + off;
+      B.status = status;
+      HIP_TRY(launch_encode(a, st), "encode launch");
     }
+    uint32_t sw[4];
+    HIP_TRY(hipMemcpyAsync(sw, status, sizeof(sw), hipMemcpyDeviceToHost, st), "encode status");
+    HIP_TRY(hipStreamSynchronize(st), "encode");
+    finish_blob(t, chunks[i], sw, &out_lens[i], &rc);
   }
   return rc;
 }

@@ -68,11 +68,14 @@ struct EncBlob {
   BlobLayout lay;
   const uint16_t* img;       // cum images of quality q
   const float* inv_step;     // of quality q
+  // per launch, for the launch's rows [row0, row0 + nrows) of the 2L (kv, layer) rows:
   uint32_t* scratch;         // per 64-stream block: [swb rows][64 lanes] words, row 0 placeholders
-  uint32_t* lens;            // [2][L][C] words
-  uint32_t* row_words;       // [2L]
-  uint32_t* block_words;     // [2L][nblk] words of each 64-stream block
-  uint32_t* status;          // [0] payload words, [1] too large for cap, [2] non-finite input
+  uint32_t* lens;            // [nrows][C] words
+  uint32_t* row_words;       // [nrows]
+  uint32_t* block_words;     // [nrows][nblk] words of each 64-stream block
+  // per blob, zero before its first launch: [0] payload words of the rows coded
+  // so far, [1] too large for cap (sticky), [2] non-finite input
+  uint32_t* status;
 };
 struct EncGroup {  // blobs of one quality coded by one workgroup (one wave each)
   int8_t blob[4];
@@ -83,6 +86,10 @@ struct EncodeArgs {
   int L, T, C, G, nblk, nblobs;
   int n_groups, waves;  // workgroups per (kv, layer, block) and their widest group
   int prio;             // 1: the launch's waves are all resident at once; level their progress
+  // the (kv, layer) rows this launch codes and packs, row = kv * L + l: a blob
+  // is coded by launches over consecutive row ranges, in order; the one that
+  // ends at 2L also writes the header and the padding
+  int row0, nrows;
   size_t swb;
   const float* scale_a;
   const float* inv_a;
@@ -91,5 +98,8 @@ struct EncodeArgs {
   EncBlob b[kEncMaxBlobs];
 };
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t st);
+// zeroes n words at p on st (a kernel, so that the clearing also works where
+// a caller captures the stream into a graph)
+hipError_t launch_zero_words(uint32_t* p, uint32_t n, hipStream_t st);
 
 }  // namespace cg

@@ -171,12 +171,15 @@ template <int GS>
 __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) {
   __shared__ uint16_t tab[kImgRows * kLanes];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int per_grp = 2 * a.L * a.nblk;
+  const int per_grp = a.nrows * a.nblk;
   const int grp = blockIdx.x / per_grp, unit = blockIdx.x % per_grp;
+  const int rrel = unit / a.nblk;  // row within the launch's range
+  const int row = a.row0 + rrel;   // kv * L + l
+  const int cb = unit % a.nblk;
   const EncGroup eg = a.groups[grp];
   {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.b[eg.blob[0]].img +
-                                                            (size_t)unit * kImgRows * kLanes);
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(
+        a.b[eg.blob[0]].img + ((size_t)row * a.nblk + cb) * kImgRows * kLanes);
     uint32_t* dst = reinterpret_cast<uint32_t*>(tab);
     for (int j = threadIdx.x; j < kImgRows * kLanes / 2; j += blockDim.x) dst[j] = src[j];
   }
@@ -185,9 +188,8 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
   const int bi = __builtin_amdgcn_readfirstlane(eg.blob[wave]);
   if (bi < 0) return;
   const EncBlob& B = a.b[bi];
-  const int kv = unit / (a.L * a.nblk);
-  const int l = (unit / a.nblk) % a.L;
-  const int cb = unit % a.nblk;
+  const int kv = row / a.L;
+  const int l = row % a.L;
   const int c = cb * kLanes + lane;
   if (c >= a.C) return;
   const size_t pi = ((size_t)kv * a.L + l) * a.C + c;
@@ -204,7 +206,7 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
   // the wave's block of 64 streams in scratch, [swb rows][64 lanes], row 0
   // holding the placeholders
   Sink o;
-  const size_t block = ((size_t)kv * a.L + l) * a.nblk + cb;
+  const size_t block = (size_t)rrel * a.nblk + cb;
   o.rs = __builtin_amdgcn_make_buffer_rsrc(B.scratch + block * kLanes * a.swb, 0,
                                            (int)(kRowBytes * (uint32_t)a.swb), kBufRsrcWord3);
   o.woff = 4u * (uint32_t)lane;
@@ -275,15 +277,16 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
   if (B.tc > B.ng) rc_finish(e, o);  // a stream without symbols stays empty
   if (nonfinite) atomicOr(&B.status[2], 1u);
   const uint32_t nwords = o.woff > woff0 ? (o.woff - woff0) / kRowBytes : 0u;
-  B.lens[pi] = nwords;
+  B.lens[(size_t)rrel * a.C + c] = nwords;
   reinterpret_cast<uint16_t*>(B.blob + B.lay.off_len)[pi] = (uint16_t)nwords;
 }
 
-// words of every 64-stream block and of every (kv, layer) row of every blob
+// words of every 64-stream block and of every (kv, layer) row of the launch's
+// range, for every blob
 __global__ __launch_bounds__(256) void k_row_totals(EncodeArgs a) {
   __shared__ uint32_t part[4];
   const EncBlob& B = a.b[blockIdx.y];
-  const int row = blockIdx.x, lane = threadIdx.x & 63;
+  const int row = blockIdx.x, lane = threadIdx.x & 63;  // row within the range
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t* r = B.lens + (size_t)row * a.C;
   uint32_t total = 0;
@@ -299,20 +302,23 @@ __global__ __launch_bounds__(256) void k_row_totals(EncodeArgs a) {
   if (threadIdx.x == 0) B.row_words[row] = part[0] + part[1] + part[2] + part[3];
 }
 
-// per blob: row offsets, payload size, header; flags a blob larger than cap
+// per blob: offsets of the range's rows, continuing from the words of the rows
+// coded before; flags a blob whose words so far do not fit cap (the range's
+// packing is then skipped, and so is every later one); the launch that ends
+// the rows writes the header
 __global__ void k_row_scan(EncodeArgs a) {
   if (threadIdx.x != 0) return;
   const EncBlob& B = a.b[blockIdx.x];
-  const int rows = 2 * a.L;
   uint32_t* row_off = reinterpret_cast<uint32_t*>(B.blob + B.lay.off_rows);
-  uint64_t w = 0;
-  for (int r = 0; r < rows; r++) {
-    row_off[r] = (uint32_t)w;
+  uint64_t w = B.status[0];
+  for (int r = 0; r < a.nrows; r++) {
+    row_off[a.row0 + r] = (uint32_t)w;
     w += B.row_words[r];
   }
   const size_t total = blob_bytes(B.lay, w);
   B.status[0] = (uint32_t)w;
-  B.status[1] = (total > B.cap || w > 0x3FFFFFFFull) ? 1u : 0u;
+  if (total > B.cap || w > 0x3FFFFFFFull) B.status[1] = 1u;
+  if (a.row0 + a.nrows != 2 * a.L) return;
   uint32_t* h = reinterpret_cast<uint32_t*>(B.blob);
   h[0] = kBlobMagic;
   h[1] = 1;
@@ -356,16 +362,17 @@ __global__ __launch_bounds__(256) void k_pack(EncodeArgs a) {
   __shared__ uint32_t tile[kLanes * kPackPitch];
   __shared__ uint32_t soff[kLanes], slen[kLanes];
   __shared__ uint32_t maxlen;
-  const int row = blockIdx.x / a.nblk, cb = blockIdx.x % a.nblk;
+  const int rrel = blockIdx.x / a.nblk, cb = blockIdx.x % a.nblk;
+  const int row = a.row0 + rrel;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (wave == 0) {
-    const uint32_t* bw = B.block_words + (size_t)row * a.nblk;
+    const uint32_t* bw = B.block_words + (size_t)rrel * a.nblk;
     uint32_t before = 0;
     for (int j = lane; j < cb; j += kLanes) before += bw[j];
     for (int o = 32; o; o >>= 1) before += __shfl_xor(before, o);
     const int c = cb * kLanes + lane;
-    const uint32_t len = c < a.C ? B.lens[(size_t)row * a.C + c] : 0u;
+    const uint32_t len = c < a.C ? B.lens[(size_t)rrel * a.C + c] : 0u;
     uint32_t incl = len, mx = len;
     for (int o = 1; o < 64; o <<= 1) {
       const uint32_t y = __shfl_up(incl, o);
@@ -378,7 +385,7 @@ __global__ __launch_bounds__(256) void k_pack(EncodeArgs a) {
     if (lane == 0) maxlen = mx;
   }
   __syncthreads();
-  const uint32_t* src = B.scratch + ((size_t)row * a.nblk + cb) * kLanes * a.swb + kLanes;  // row 1
+  const uint32_t* src = B.scratch + ((size_t)rrel * a.nblk + cb) * kLanes * a.swb + kLanes;  // row 1
   uint32_t* pay = reinterpret_cast<uint32_t*>(B.blob + B.lay.off_pay);
   const uint32_t mx = maxlen;
   const int nt = (int)((mx + kLanes - 1) / kLanes), ns = min(kLanes, a.C - cb * kLanes);
@@ -401,15 +408,27 @@ __global__ __launch_bounds__(256) void k_pack(EncodeArgs a) {
 
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t st) {
   const unsigned nb = (unsigned)a.nblobs;
-  const unsigned blocks = (unsigned)(a.n_groups * 2 * a.L * a.nblk);
+  const unsigned blocks = (unsigned)(a.n_groups * a.nrows * a.nblk);
   if (a.G == 10)
     k_encode<10><<<blocks, kLanes * a.waves, 0, st>>>(a);
   else
     k_encode<0><<<blocks, kLanes * a.waves, 0, st>>>(a);
-  k_row_totals<<<dim3(2 * a.L, nb), 256, 0, st>>>(a);
+  k_row_totals<<<dim3(a.nrows, nb), 256, 0, st>>>(a);
   k_row_scan<<<nb, 64, 0, st>>>(a);
-  k_pad<<<nb, 256, 0, st>>>(a);
-  k_pack<<<dim3(2 * a.L * a.nblk, nb), 256, 0, st>>>(a);
+  if (a.row0 + a.nrows == 2 * a.L) k_pad<<<nb, 256, 0, st>>>(a);
+  k_pack<<<dim3(a.nrows * a.nblk, nb), 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+namespace {
+__global__ __launch_bounds__(256) void k_zero_words(uint32_t* p, uint32_t n) {
+  const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+}  // namespace
+
+hipError_t launch_zero_words(uint32_t* p, uint32_t n, hipStream_t st) {
+  if (n) k_zero_words<<<(n + 255u) / 256u, 256, 0, st>>>(p, n);
   return hipGetLastError();
 }
 
