@@ -271,7 +271,7 @@ int parse_info(const uint8_t* b, size_t len, cg_chunk_info* o) {
   if (len < (size_t)kBlobHdr) return fail(CG_E_INVAL, "blob shorter than its header");
   uint32_t u[16];
   memcpy(u, b, 64);
-  if (u[0] != kBlobMagic || u[1] != 1) return fail(CG_E_INVAL, "not a CGK1 v1 blob");
+  if (u[0] != kBlobMagic || u[1] != kBlobVersion) return fail(CG_E_INVAL, "not a CGK1 v2 blob");
   if (u[11] != (uint32_t)kProbBits) return fail(CG_E_INVAL, "unsupported probability precision");
   o->layers = (int32_t)u[2];
   o->channels = (int32_t)u[3];

@@ -187,10 +187,26 @@ __device__ __forceinline__ uint32_t shift_sel(uint32_t sh) {
   return (uint32_t)((0x0706050403020100ull << sh) >> 32);
 }
 
+// Where a lane's stream lies in the payload layout.  A 64-stream block holds
+// m whole 16-byte units of every one of its ns streams first, unit by unit,
+// then each stream's remaining words: word w of the lane's stream is at byte
+// a0 + (w / 4) us + 4 (w % 4) while w / 4 < m (us = 16 ns bytes between the
+// units of one stream), else at t0 + 4 w (t0 = where its tail starts, less
+// 16 m).  m and us are the same for the whole wave.
+struct Words {
+  uint32_t a0, t0, us, m;
+  // byte offset of unit u (words 4u .. 4u + 3)
+  __device__ __forceinline__ uint32_t unit(uint32_t u) const {
+    const uint32_t inter = a0 + mul24(u, us), tail = t0 + (u << 4);
+    return u < m ? inter : tail;
+  }
+  __device__ __forceinline__ uint32_t word(uint32_t w) const { return unit(w >> 2) + 4u * (w & 3u); }
+};
+
 // Per-lane state both kernels set up the same way.
 struct Lane {
   __amdgpu_buffer_rsrc_t rs, ro;
-  uint32_t sbase;      // byte offset of the stream's word 0 in the blob
+  Words wd;            // the lane's stream words in the blob
   uint32_t bad;        // stream extends past the payload
   float scale_a, step;
   uint32_t lane_addr;  // LDS address of the lane's cum[0]
@@ -281,22 +297,35 @@ __device__ __forceinline__ bool setup(const DecodeArgs& a, int wave, int lane, L
   const int c = cb * kLanes + lane;
   const bool active = c < a.C;
 
-  // start of this lane's stream: row offset + lengths of the streams before it
-  // (the whole wave takes part in the prefix sums)
+  // the block's place in the payload (row offset + the words of the row's
+  // earlier blocks), its units m and the lane's tail offset (the whole wave
+  // takes part in the reductions and the scan)
   const uint32_t len_base = s.ch.off_len + 2u * (uint32_t)row * (uint32_t)a.C;
   uint32_t before = 0;
   for (int j = lane; j < cb * kLanes; j += kLanes) before += ld16(s.rs, len_base + 2u * j);
-  for (int o = 32; o; o >>= 1) before += __shfl_xor(before, o);
   const uint32_t my_len = active ? ld16(s.rs, len_base + 2u * c) : 0u;
-  uint32_t incl = my_len;
+  uint32_t total = my_len, mu = active ? my_len >> 2 : 0xFFFFFFFFu;
+  for (int o = 32; o; o >>= 1) {
+    before += __shfl_xor(before, o);
+    total += __shfl_xor(total, o);
+    mu = min(mu, __shfl_xor(mu, o));
+  }
+  const uint32_t m = __builtin_amdgcn_readfirstlane(mu);
+  const uint32_t ns = (uint32_t)min(kLanes, a.C - cb * kLanes);
+  const uint32_t tl = active ? my_len - 4u * m : 0u;  // the lane's tail words
+  uint32_t incl = tl;
   for (int o = 1; o < 64; o <<= 1) {
     const uint32_t y = __shfl_up(incl, o);
     if (lane >= o) incl += y;
   }
   if (!active) return false;  // no cross-lane work after this
-  const uint32_t start = ld32(s.rs, 64u + 4u * row) + before + incl - my_len;
-  s.bad = ((uint64_t)start + my_len > s.ch.W) ? 1u : 0u;
-  s.sbase = s.ch.off_pay + 4u * start;
+  const uint32_t blk = ld32(s.rs, 64u + 4u * row) + before;  // words into the payload
+  s.bad = ((uint64_t)blk + total > s.ch.W) ? 1u : 0u;
+  const uint32_t blk_byte = s.ch.off_pay + 4u * blk;
+  s.wd.m = m;
+  s.wd.us = 16u * ns;
+  s.wd.a0 = blk_byte + 16u * (uint32_t)lane;
+  s.wd.t0 = blk_byte + 4u * (4u * m * ns + incl - tl) - 16u * m;
 
   const size_t pi = (size_t)row * a.C + c;
   s.scale_a = a.scale_a[pi];
@@ -413,26 +442,26 @@ __global__ __launch_bounds__(512) void k_decode_win(DecodeArgs a) {
   constexpr int RB = kWinRB;
   constexpr uint32_t M = kWinM;
 
-  // decoder state: ncode = ~code, range, and nc = -(stream bits shifted into
-  // the code after its first word)
-  uint32_t ncode = ~ld32(s.rs, s.sbase);
+  // decoder state: ncode = ~code, range, and nc = -(32 + stream bits shifted
+  // into the code after its first word): ring word k is stream word k, so the
+  // next bits start 32 + those bits into the ring
+  const Block<RB> b0 = Block<RB>::load(s.rs, s.wd.unit(0));
+  const Block<RB> b1 = Block<RB>::load(s.rs, s.wd.unit(1));
+  uint32_t ncode = ~b0.v.x;
   uint32_t range = 0xFFFFFFFFu;
-  uint32_t nc = 0;
+  uint32_t nc = (uint32_t)-32;
   const uint32_t ring = kTabBytes + (uint32_t)wave * win_ring_bytes() + 4u * (uint32_t)lane;
   // Ring words 0 .. n - 1 have been written, n = (64 - lim) / 32: nc < lim
-  // means a window's words have not all landed.  fetch_off = the blob offset of
-  // ring word n, where the next block starts; land = where it lands (the high
-  // and low halves alternate, so land toggles as flip - land).
+  // means a window's words have not all landed.  fetched = the words fetched,
+  // landed or in flight (the next block holds unit fetched / 4); land = where
+  // the next block lands (the high and low halves alternate, so land toggles
+  // as flip - land).
   int lim = 64 - 32 * (int)(2u * RB);
-  uint32_t fetch_off = s.sbase + 4u + 8u * RB;
+  uint32_t fetched = 2u * RB;
   const uint32_t flip = 2u * ring + kWinHigh + kWinLow;
   uint32_t land = ring + kWinHigh;
-  {
-    const Block<RB> b0 = Block<RB>::load(s.rs, s.sbase + 4u);
-    const Block<RB> b1 = Block<RB>::load(s.rs, s.sbase + 4u + 4u * RB);
-    win_put(ring, ring + kWinHigh, true, b0);
-    win_put(ring, ring + kWinLow, false, b1);
-  }
+  win_put(ring, ring + kWinHigh, true, b0);
+  win_put(ring, ring + kWinLow, false, b1);
   Block<RB> pend = {};  // block in flight
   bool inflight = false;
   int anc_next = ld8s(s.rs, s.anc_base);
@@ -463,7 +492,7 @@ __global__ __launch_bounds__(512) void k_decode_win(DecodeArgs a) {
       for (uint32_t d = 0; d < 3; d++) {
         const uint32_t k = j + d;
         if (k >= landed) {
-          const uint32_t w = ~ld32(s.rs, s.sbase + 4u + 4u * k);
+          const uint32_t w = ~ld32(s.rs, s.wd.word(k));
           const uint32_t sl = k & M;
           *lds_at<uint32_t>(ring + (2u + M - sl) * kSlot) = w;
           if (sl < 2u) *lds_at<uint32_t>(ring + (1u - sl) * kSlot) = w;
@@ -491,17 +520,17 @@ __global__ __launch_bounds__(512) void k_decode_win(DecodeArgs a) {
   };
 
   // once per group: write the block fetched one group earlier into the ring,
-  // then fetch the next one if the words it lands over are taken (lanes
+  // then fetch the next unit if the words it lands over are taken (lanes
   // without room point their load past the blob end: no memory access)
   auto ring_step = [&]() {
     if (inflight) {
       win_put(ring, land, land == ring + kWinHigh, pend);
       land = flip - land;
       lim -= 32 * RB;
-      fetch_off += 4u * RB;
     }
-    inflight = (int)nc <= lim + 32 * RB - 64;
-    pend = Block<RB>::load(s.rs, inflight ? fetch_off : 0xFFFFFFF0u);
+    inflight = (int)nc <= 64 - 32 * (int)fetched + 32 * RB - 64;
+    pend = Block<RB>::load(s.rs, inflight ? s.wd.unit(fetched >> 2) : 0xFFFFFFF0u);
+    fetched += inflight ? (uint32_t)RB : 0u;
   };
 
   using I1 = std::integral_constant<int, 1>;
@@ -591,24 +620,25 @@ __global__ __launch_bounds__(512) void k_decode_reg(DecodeArgs a) {
   // decoder state: ncode = ~code; range; bb = the next bits of the stream,
   // complemented, in its low `left` bits (most significant first, 32..64 of
   // them before every pair of symbols).  Words 0..2 start the state; words 3..
-  // reach bb through the wave's LDS ring: word 3 + i sits in slot i mod 2 RB of
-  // the lane's column, fetched RB words at a time one group ahead of use.
-  uint32_t ncode = ~ld32(s.rs, s.sbase);
-  uint64_t bb = ((uint64_t)~ld32(s.rs, s.sbase + 4u) << 32) | ~ld32(s.rs, s.sbase + 8u);
+  // reach bb through the wave's LDS ring: word k sits in slot k mod 2 RB of the
+  // lane's column, fetched RB words (half a unit) at a time one group ahead of
+  // use.  Word 3 and words 4, 5 are written below.
+  static_assert(kRegRB == 2, "the ring holds half units");
+  const u32x4 u0 = __builtin_amdgcn_raw_buffer_load_b128(s.rs, s.wd.unit(0), 0, 0);
+  const Block<RB> b1 = Block<RB>::load(s.rs, s.wd.word(4));
+  uint32_t ncode = ~u0.x;
+  uint64_t bb = ((uint64_t)~u0.y << 32) | ~u0.z;
   uint32_t left = 64;
   uint32_t range = 0xFFFFFFFFu;
   constexpr uint32_t kSlotMask = (2u * RB - 1u) << 8;
   const uint32_t ring = reg_ring_base() + (uint32_t)wave * reg_ring_bytes() + 4u * (uint32_t)lane;
-  // ring words taken and written, counted in units of 256 (one slot's size)
-  uint32_t taken = 0;
-  uint32_t landed = (2u * RB) << 8;                  // words 3 .. 2 RB + 2, written below
-  uint32_t fetch_off = s.sbase + 12u + 8u * RB;      // the next block
-  {
-    const Block<RB> b0 = Block<RB>::load(s.rs, s.sbase + 12u);
-    const Block<RB> b1 = Block<RB>::load(s.rs, s.sbase + 12u + 4u * RB);
-    reg_put(ring, 0u, b0);
-    reg_put(ring, (uint32_t)RB << 8, b1);
-  }
+  // words taken from the ring and written to it, counted in units of 256 (one
+  // slot's size): the next word to take is word 3, words 3 .. 5 are written
+  uint32_t taken = 3u << 8;
+  uint32_t landed = 6u << 8;
+  uint32_t fetch_w = 6;  // the next block's first word
+  *lds_at<uint32_t>(ring + (3u << 8)) = u0.w;
+  reg_put(ring, 0u, b1);
   Block<RB> pend = {};  // block in flight
   bool inflight = false;
   int anc_next = ld8s(s.rs, s.anc_base);
@@ -631,7 +661,7 @@ __global__ __launch_bounds__(512) void k_decode_reg(DecodeArgs a) {
     const bool take = left < 32;
     const uint32_t slot = (taken & kSlotMask) | ring;
     if (take && taken >= landed)
-      *lds_at<uint32_t>(slot) = ld32(s.rs, s.sbase + 12u + (taken >> 6));
+      *lds_at<uint32_t>(slot) = ld32(s.rs, s.wd.word(taken >> 8));
     const uint32_t w = lds32(slot);
     if (take) {
       bb = (bb << 32) | ~w;
@@ -648,8 +678,8 @@ __global__ __launch_bounds__(512) void k_decode_reg(DecodeArgs a) {
       landed += (uint32_t)RB << 8;
     }
     inflight = landed + ((uint32_t)RB << 8) <= taken + ((2u * RB) << 8);
-    pend = Block<RB>::load(s.rs, inflight ? fetch_off : 0xFFFFFFF0u);
-    if (inflight) fetch_off += 4u * RB;
+    pend = Block<RB>::load(s.rs, inflight ? s.wd.word(fetch_w) : 0xFFFFFFF0u);
+    if (inflight) fetch_w += RB;
   };
 
   // one group: the anchor row, then its deltas in pairs (a lone last one when

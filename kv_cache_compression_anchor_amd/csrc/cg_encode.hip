@@ -321,7 +321,7 @@ __global__ void k_row_scan(EncodeArgs a) {
   if (a.row0 + a.nrows != 2 * a.L) return;
   uint32_t* h = reinterpret_cast<uint32_t*>(B.blob);
   h[0] = kBlobMagic;
-  h[1] = 1;
+  h[1] = kBlobVersion;
   h[2] = (uint32_t)a.L;
   h[3] = (uint32_t)a.C;
   h[4] = (uint32_t)a.T;
@@ -349,59 +349,66 @@ __global__ __launch_bounds__(256) void k_pad(EncodeArgs a) {
   for (size_t j = tail0 + threadIdx.x; j < tail1; j += 256) B.blob[j] = 0;
 }
 
-// Pack one 64-stream block: its payload offset is the row's offset plus the
-// words of the row's earlier blocks, each stream's the block's offset plus the
-// lengths of the streams before it (a wave scan).  The block's words are
-// [row][lane] in scratch; 64-row tiles go through LDS (rows padded to 65 words,
-// so reading a column hits 64 distinct banks) and leave as each stream's
-// consecutive words, 64 at a time.
+// Pack one 64-stream block into the payload layout: its payload offset is the
+// row's offset plus the words of the row's earlier blocks; m = the fewest
+// whole 16-byte units any of its streams has; units 0 .. m-1 of its ns streams
+// first, unit by unit (unit u of stream j at word 4 (u ns + j)), then every
+// stream's remaining words, stream after stream.  The block's words are
+// [row][lane] in scratch (row 0 the placeholders): a unit of all streams is
+// four scratch rows, transposed through LDS into one contiguous run of 4 ns
+// words; the tails are read a row at a time (the lanes are the streams).
 constexpr int kPackPitch = kLanes + 1;
 __global__ __launch_bounds__(256) void k_pack(EncodeArgs a) {
   const EncBlob& B = a.b[blockIdx.y];
   if (B.status[1]) return;
-  __shared__ uint32_t tile[kLanes * kPackPitch];
-  __shared__ uint32_t soff[kLanes], slen[kLanes];
-  __shared__ uint32_t maxlen;
+  __shared__ uint32_t tile[4 * kPackPitch];
+  __shared__ uint32_t toff[kLanes], slen[kLanes];
+  __shared__ uint32_t s_base, s_units, s_maxlen;
   const int rrel = blockIdx.x / a.nblk, cb = blockIdx.x % a.nblk;
   const int row = a.row0 + rrel;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ns = min(kLanes, a.C - cb * kLanes);
   if (wave == 0) {
     const uint32_t* bw = B.block_words + (size_t)rrel * a.nblk;
     uint32_t before = 0;
     for (int j = lane; j < cb; j += kLanes) before += bw[j];
     for (int o = 32; o; o >>= 1) before += __shfl_xor(before, o);
     const int c = cb * kLanes + lane;
-    const uint32_t len = c < a.C ? B.lens[(size_t)rrel * a.C + c] : 0u;
-    uint32_t incl = len, mx = len;
+    const uint32_t len = lane < ns ? B.lens[(size_t)rrel * a.C + c] : 0u;
+    uint32_t mu = lane < ns ? len / 4u : 0xFFFFFFFFu, mx = len;
+    for (int o = 32; o; o >>= 1) {
+      mu = min(mu, __shfl_xor(mu, o));
+      mx = max(mx, __shfl_xor(mx, o));
+    }
+    const uint32_t tl = lane < ns ? len - 4u * mu : 0u;  // this stream's tail words
+    uint32_t incl = tl;
     for (int o = 1; o < 64; o <<= 1) {
       const uint32_t y = __shfl_up(incl, o);
       if (lane >= o) incl += y;
     }
-    for (int o = 32; o; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
-    const uint32_t base = reinterpret_cast<const uint32_t*>(B.blob + B.lay.off_rows)[row] + before;
-    soff[lane] = base + incl - len;
+    toff[lane] = 4u * mu * (uint32_t)ns + incl - tl;
     slen[lane] = len;
-    if (lane == 0) maxlen = mx;
+    if (lane == 0) {
+      s_base = reinterpret_cast<const uint32_t*>(B.blob + B.lay.off_rows)[row] + before;
+      s_units = mu;
+      s_maxlen = mx;
+    }
   }
   __syncthreads();
   const uint32_t* src = B.scratch + ((size_t)rrel * a.nblk + cb) * kLanes * a.swb + kLanes;  // row 1
-  uint32_t* pay = reinterpret_cast<uint32_t*>(B.blob + B.lay.off_pay);
-  const uint32_t mx = maxlen;
-  const int nt = (int)((mx + kLanes - 1) / kLanes), ns = min(kLanes, a.C - cb * kLanes);
-  for (int kt = 0; kt < nt; kt++) {
-    // rows kt*64 .. kt*64 + 63 of the block that hold words (the longest
-    // stream's; rows past it lie outside the block): wave w loads every fourth
-    for (int k = wave; k < kLanes && (uint32_t)(kt * kLanes + k) < mx; k += 4)
-      tile[k * kPackPitch + lane] = src[((size_t)kt * kLanes + k) * kLanes + lane];
+  uint32_t* pay = reinterpret_cast<uint32_t*>(B.blob + B.lay.off_pay) + s_base;
+  const uint32_t m = s_units, mx = s_maxlen;
+  // interleaved units: scratch rows 4u .. 4u + 3 (wave w takes row 4u + w)
+  for (uint32_t u = 0; u < m; u++) {
+    if (lane < ns) tile[wave * kPackPitch + lane] = src[(size_t)(4u * u + wave) * kLanes + lane];
     __syncthreads();
-    // stream j's words kt*64 + lane
-    for (int j = wave; j < ns; j += 4) {
-      const uint32_t kk = (uint32_t)(kt * kLanes + lane);
-      if (kk < slen[j]) pay[soff[j] + kk] = tile[lane * kPackPitch + j];
-    }
+    if (tid < 4 * ns) pay[4u * u * (uint32_t)ns + tid] = tile[(tid & 3) * kPackPitch + (tid >> 2)];
     __syncthreads();
   }
+  // tails: stream j's words 4m .. len_j - 1, one scratch row at a time
+  for (uint32_t k = 4u * m + (uint32_t)wave; k < mx; k += 4u)
+    if (lane < ns && k < slen[lane]) pay[toff[lane] + (k - 4u * m)] = src[(size_t)k * kLanes + lane];
 }
 
 }  // namespace

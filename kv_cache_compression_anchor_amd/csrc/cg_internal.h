@@ -23,6 +23,8 @@ constexpr int kTabHdr = 80;
 constexpr int kBlobHdr = 64;
 constexpr uint32_t kTabMagic = 0x31544743u;   // "CGT1"
 constexpr uint32_t kBlobMagic = 0x314B4743u;  // "CGK1"
+constexpr uint32_t kBlobVersion = 2;           // payload blocks interleaved unit by unit
+constexpr uint32_t kUnitWords = 4;             // a 16-byte unit of a stream
 constexpr int kMaxTokens = 1 << 21;
 constexpr int kMaxChunk = 65536;
 constexpr int kIdLeaf = 1024;          // tables id: FNV-1a-64 tree over 1 KiB leaves,

@@ -498,10 +498,31 @@ def blob_view(b: bytes) -> BlobView:
     return BlobView(h, rows, anchors, lengths, payload, off, bytes(b[off + 4 * W:]))
 
 
+BLOCK_STREAMS = 64  # streams per payload block
+UNIT_WORDS = 4      # words per interleaved unit
+
+
+def stream_word_offsets(lengths_of_row: np.ndarray, c: int) -> np.ndarray:
+    """Payload word offsets, from the row's start, of the words of stream c of a
+    (kv, layer) row whose stream lengths (words) are ``lengths_of_row``: blocks
+    of 64 streams one after another; inside a block, units 0 .. m-1 (m the fewest
+    whole 4-word units any stream of the block has) interleaved unit by unit,
+    then each stream's remaining words, stream after stream."""
+    lens = lengths_of_row.astype(np.int64)
+    b0 = c - c % BLOCK_STREAMS
+    blk = lens[b0: b0 + BLOCK_STREAMS]
+    ns, j = len(blk), c - b0
+    m = int((blk // UNIT_WORDS).min())
+    base = int(lens[:b0].sum())
+    w = np.arange(int(lens[c]), dtype=np.int64)
+    inter = base + UNIT_WORDS * ((w // UNIT_WORDS) * ns + j) + w % UNIT_WORDS
+    tail0 = base + UNIT_WORDS * m * ns + int((blk[:j] - UNIT_WORDS * m).sum())
+    return np.where(w < UNIT_WORDS * m, inter, tail0 + w - UNIT_WORDS * m)
+
+
 def stream_bytes(bv: BlobView, kv: int, l: int, c: int, extra_words: int = 4) -> bytes:
-    """Bytes of stream (kv, l, c) followed by ``extra_words`` words of what follows it."""
-    L, Cc = bv.header["layers"], bv.header["channels"]
-    start = int(bv.row_offset[kv, l]) + int(bv.lengths[kv, l, :c].astype(np.int64).sum())
-    n = int(bv.lengths[kv, l, c])
-    words = bv.payload[start: start + n + extra_words]
+    """Bytes of stream (kv, l, c) followed by ``extra_words`` zero words (whatever
+    follows a stream does not change what it decodes to)."""
+    at = int(bv.row_offset[kv, l]) + stream_word_offsets(bv.lengths[kv, l], c)
+    words = np.concatenate([bv.payload[at], np.zeros(extra_words, np.uint32)])
     return words.astype(">u4").tobytes()

@@ -31,6 +31,9 @@
 #define BLOB_HDR 64
 #define TAB_MAGIC 0x31544743u   /* "CGT1" */
 #define BLOB_MAGIC 0x314B4743u  /* "CGK1" */
+#define BLOB_VERSION 2          /* payload blocks laid out as below (stream_layout) */
+#define BLOCK_STREAMS 64        /* streams per payload block */
+#define UNIT_WORDS 4            /* a 16-byte unit of a stream */
 #define MAX_TOKENS (1 << 21)
 #define MAX_CHUNK 65536
 
@@ -714,6 +717,58 @@ static size_t bytes_to_words(const uint8_t* b, size_t nb, uint32_t* w) {
   return nw;
 }
 
+/* Payload layout (reading R13).  The streams of a (kv, layer) row lie in
+ * blocks of BLOCK_STREAMS consecutive channels (the last block may hold fewer),
+ * blocks one after another.  Inside a block of ns streams of len[0..ns) words,
+ * m = the fewest whole 16-byte units (UNIT_WORDS words) any of its streams has;
+ * units 0 .. m-1 of the ns streams come first, unit by unit (unit u of stream
+ * j is the four words at 4 (u ns + j)), then every stream's remaining words,
+ * 4m .. len[j]-1, stream after stream.  Nothing is padded: the block holds
+ * exactly the sum of its streams' words. */
+static int block_units(const uint16_t* len, int ns) {
+  int m = 0;
+  for (int j = 0; j < ns; j++) {
+    int u = len[j] / UNIT_WORDS;
+    if (j == 0 || u < m) m = u;
+  }
+  return m;
+}
+
+/* tail[j] = offset in the block of stream j's first word past its first m units */
+static void block_tails(const uint16_t* len, int ns, int m, size_t* tail) {
+  size_t off = (size_t)UNIT_WORDS * m * ns;
+  for (int j = 0; j < ns; j++) {
+    tail[j] = off;
+    off += len[j] - (size_t)UNIT_WORDS * m;
+  }
+}
+
+/* offset in the block of word w of stream j */
+static size_t block_word(int ns, int m, const size_t* tail, int j, size_t w) {
+  if (w < (size_t)UNIT_WORDS * m)
+    return UNIT_WORDS * ((w / UNIT_WORDS) * ns + j) + w % UNIT_WORDS;
+  return tail[j] + (w - (size_t)UNIT_WORDS * m);
+}
+
+/* the row's streams (each one's words consecutive in `src`, lengths `len`,
+ * C channels) into the payload layout at `dst` */
+static void lay_out_row(const uint32_t* src, const uint16_t* len, int C, uint32_t* dst) {
+  size_t base = 0, s = 0;
+  size_t tail[BLOCK_STREAMS];
+  for (int c0 = 0; c0 < C; c0 += BLOCK_STREAMS) {
+    int ns = C - c0 < BLOCK_STREAMS ? C - c0 : BLOCK_STREAMS;
+    int m = block_units(len + c0, ns);
+    block_tails(len + c0, ns, m, tail);
+    size_t words = 0;
+    for (int j = 0; j < ns; j++) {
+      for (size_t w = 0; w < len[c0 + j]; w++) dst[base + block_word(ns, m, tail, j, w)] = src[s + w];
+      s += len[c0 + j];
+      words += len[c0 + j];
+    }
+    base += words;
+  }
+}
+
 int cgo_encode_chunk(const uint8_t* tables, size_t tlen, const uint16_t* k,
                      const uint16_t* v, int chunk, int q, int nthreads, uint8_t* out,
                      size_t cap, size_t* len) {
@@ -787,7 +842,7 @@ int cgo_encode_chunk(const uint8_t* tables, size_t tlen, const uint16_t* k,
   if (rc == OK) {
     memset(out, 0, total);
     wr32(out, BLOB_MAGIC);
-    wr32(out + 4, 1);
+    wr32(out + 4, BLOB_VERSION);
     wri32(out + 8, L);
     wri32(out + 12, C);
     wri32(out + 16, T);
@@ -800,11 +855,14 @@ int cgo_encode_chunk(const uint8_t* tables, size_t tlen, const uint16_t* k,
     wr32(out + 44, PBITS);
     wr64(out + 48, tv.id);
     size_t woff = 0;
+    uint32_t* laid = (uint32_t*)malloc(sizeof(uint32_t) * (swb * C + 1));
     for (int r = 0; r < 2 * L; r++) {
       wr32(out + BLOB_HDR + 4 * r, (uint32_t)woff);
-      memcpy(out + off_pay + 4 * woff, rows[r], 4 * (size_t)rowlen[r]);
+      lay_out_row(rows[r], slen + (size_t)r * C, C, laid);
+      memcpy(out + off_pay + 4 * woff, laid, 4 * (size_t)rowlen[r]);
       woff += rowlen[r];
     }
+    free(laid);
     memcpy(out + off_anchor, anchors, 2 * (size_t)L * ng * C);
     memcpy(out + off_len, slen, 2 * 2 * lc);
     *len = total;
@@ -854,7 +912,7 @@ typedef struct {
 } blobview;
 
 static int parse_blob(const tabview* tv, const uint8_t* b, size_t blen, blobview* bv) {
-  if (blen < BLOB_HDR || rd32(b) != BLOB_MAGIC || rd32(b + 4) != 1) return E_INVAL;
+  if (blen < BLOB_HDR || rd32(b) != BLOB_MAGIC || rd32(b + 4) != BLOB_VERSION) return E_INVAL;
   bv->L = rdi32(b + 8); bv->C = rdi32(b + 12); bv->T = rdi32(b + 16);
   bv->t0 = rdi32(b + 20); bv->tc = rdi32(b + 24); bv->G = rdi32(b + 28);
   bv->ng = rdi32(b + 32); bv->q = rdi32(b + 36); bv->W = rd32(b + 40);
@@ -882,22 +940,24 @@ static int parse_blob(const tabview* tv, const uint8_t* b, size_t blen, blobview
   return OK;
 }
 
-/* the byte string of at most maxw payload words starting at word w (each
- * word holds four stream bytes, most significant first) */
-static uint8_t* payload_bytes(const blobview* bv, size_t w, size_t maxw, size_t* nb) {
+/* The byte string of stream j of the block at payload word `base` (each word
+ * holds four stream bytes, most significant first), read through the payload
+ * layout; words outside the payload read as zero.  Whatever follows a stream
+ * does not change what it decodes to (its flush names a block inside the
+ * final interval), so the decoder reads on into zeros. */
+static uint8_t* stream_bytes(const blobview* bv, size_t base, int ns, int m, const size_t* tail,
+                             int j, size_t len, size_t* nb) {
   size_t words = bv->payload_bytes_avail / 4;
-  if (w > words) w = words;
-  size_t nw = words - w < maxw ? words - w : maxw;
-  size_t n = nw * 4;
-  uint8_t* out = (uint8_t*)malloc(n + 1);
-  for (size_t i = 0; i < nw; i++) {
-    uint32_t v = rd32(bv->payload + 4 * (w + i));
-    out[4 * i] = (uint8_t)(v >> 24);
-    out[4 * i + 1] = (uint8_t)(v >> 16);
-    out[4 * i + 2] = (uint8_t)(v >> 8);
-    out[4 * i + 3] = (uint8_t)v;
+  uint8_t* out = (uint8_t*)malloc(4 * len + 1);
+  for (size_t w = 0; w < len; w++) {
+    size_t at = base + block_word(ns, m, tail, j, w);
+    uint32_t v = at < words ? rd32(bv->payload + 4 * at) : 0;
+    out[4 * w] = (uint8_t)(v >> 24);
+    out[4 * w + 1] = (uint8_t)(v >> 16);
+    out[4 * w + 2] = (uint8_t)(v >> 8);
+    out[4 * w + 3] = (uint8_t)v;
   }
-  *nb = n;
+  *nb = 4 * len;
   return out;
 }
 
@@ -922,14 +982,24 @@ static int decode_blob_impl(const uint8_t* tables, size_t tlen, const uint8_t* b
     int kv = row / L, l = row % L;
     uint8_t* sym = (uint8_t*)malloc(nsyms + 1);
     size_t w = rd32(bv.rows + 4 * row);
+    uint16_t blen16[BLOCK_STREAMS];
+    size_t tail[BLOCK_STREAMS];
+    size_t bbase = w;
+    int ns = 0, m = 0;
     for (int c = 0; c < C; c++) {
       size_t i = kv * lc + (size_t)l * C + c;
-      size_t slw = (uint16_t)(bv.lens[2 * i] | (bv.lens[2 * i + 1] << 8));
+      if (c % BLOCK_STREAMS == 0) { /* a new block: its streams' lengths and layout */
+        bbase = w;
+        ns = C - c < BLOCK_STREAMS ? C - c : BLOCK_STREAMS;
+        for (int j = 0; j < ns; j++)
+          blen16[j] = (uint16_t)(bv.lens[2 * (i + j)] | (bv.lens[2 * (i + j) + 1] << 8));
+        m = block_units(blen16, ns);
+        block_tails(blen16, ns, m, tail);
+      }
+      size_t slw = blen16[c % BLOCK_STREAMS];
       if (w + slw > bv.W) bad = 1;
       size_t nb = 0;
-      /* a valid stream is read at most three bytes past its end; the window
-       * covers its words plus the four that follow (zeros past the padding) */
-      uint8_t* bytes = payload_bytes(&bv, w, slw + 4, &nb);
+      uint8_t* bytes = stream_bytes(&bv, bbase, ns, m, tail, c % BLOCK_STREAMS, slw, &nb);
       int cor = 0;
       uint16_t f[NSYM];
       tv_freq(tv.freq[q], i, f);

@@ -90,7 +90,7 @@ def test_chunk_info_parse_rejects_bad_headers(cg):
     k, v = synth.gen_kv(w)
     t = oracle.build_tables(oracle.params_for(w), k, v)
     b = bytearray(oracle.encode_chunk(t, k, v, 0, 0))
-    for off, val in ((0, 0x58), (4, 2), (44, 14), (32, 99), (36, 3), (8, 0)):
+    for off, val in ((0, 0x58), (4, 1), (4, 3), (44, 14), (32, 99), (36, 3), (8, 0)):
         bad = bytearray(b)
         bad[off] = val
         with pytest.raises(cg.CgError) as e:
@@ -158,7 +158,7 @@ def test_chunks_of_4_gib_per_layer_are_rejected(cg):
     assert "NULL" in build_msg(**dict(base, tokens=100))
     # a blob header naming such a chunk
     hdr = np.zeros(16, np.uint32)
-    hdr[:12] = [0x314B4743, 1, 1, 65536, 65536, 0, 65536, 10, (65536 + 9) // 10, 0, 0, 15]
+    hdr[:12] = [0x314B4743, 2, 1, 65536, 65536, 0, 65536, 10, (65536 + 9) // 10, 0, 0, 15]
     with pytest.raises(cg.CgError) as e:
         cg.cg_chunk_info_parse(hdr.tobytes())
     assert e.value.code == cg.CG_E_INVAL and "4 GiB" in str(e.value)

@@ -183,7 +183,7 @@ def test_blob_layout(oracle_lib, coded):
         bv = oracle_lib.blob_view(b)
         h = bv.header
         t0, tc, ng = oracle_lib.chunk_geometry(t, ch)
-        assert h["magic"] == b"CGK1" and h["version"] == 1 and h["prob_bits"] == 15
+        assert h["magic"] == b"CGK1" and h["version"] == 2 and h["prob_bits"] == 15
         assert (h["token_offset"], h["chunk_tokens"], h["n_groups"]) == (t0, tc, ng)
         assert h["quality"] == q and h["tables_id"] == tid
         lens = bv.lengths.astype(np.int64)
@@ -193,6 +193,35 @@ def test_blob_layout(oracle_lib, coded):
         assert len(b) % 16 == 0 and len(bv.tail) >= 16 and not any(bv.tail)
         assert bv.payload_offset % 16 == 0
         assert len(b) <= oracle_lib.encode_bound(t, ch)
+
+
+def test_payload_block_layout(oracle_lib, coded):
+    """The payload layout of a block of streams, on a hand-made block (lengths
+    5, 9, 4, 8 words: one whole unit each, m = 1): unit 0 of every stream,
+    stream after stream, then the rest of each stream in stream order; and on
+    every row of the coded blobs: the streams' words cover the row's payload
+    words exactly once (nothing padded, nothing shared), in blocks of 64
+    streams in channel order."""
+    lens = np.array([5, 9, 4, 8], np.uint16)
+    got = [list(oracle_lib.stream_word_offsets(lens, c)) for c in range(4)]
+    assert got == [[0, 1, 2, 3, 16], [4, 5, 6, 7, 17, 18, 19, 20, 21],
+                   [8, 9, 10, 11], [12, 13, 14, 15, 22, 23, 24, 25]]
+    lens2 = np.array([3, 12, 7], np.uint16)  # a stream shorter than a unit: m = 0
+    assert [list(oracle_lib.stream_word_offsets(lens2, c)) for c in range(3)] == [
+        [0, 1, 2], list(range(3, 15)), list(range(15, 22))]
+    w, k, v, t, blobs = coded
+    for (ch, q), b in list(blobs.items())[:3]:
+        bv = oracle_lib.blob_view(b)
+        for kv in range(2):
+            for l in range(w.layers):
+                at = np.concatenate([oracle_lib.stream_word_offsets(bv.lengths[kv, l], c)
+                                     for c in range(w.channels)])
+                assert np.array_equal(np.sort(at), np.arange(int(bv.lengths[kv, l].sum())))
+                for c0 in range(0, w.channels, 64):  # a block's words are its own
+                    base = int(bv.lengths[kv, l, :c0].astype(np.int64).sum())
+                    blk = np.concatenate([oracle_lib.stream_word_offsets(bv.lengths[kv, l], c)
+                                          for c in range(c0, min(c0 + 64, w.channels))])
+                    assert blk.min() == base and blk.max() == base + len(blk) - 1
 
 
 def test_single_stream_api_matches_blobs(oracle_lib, coded):
