@@ -1,6 +1,7 @@
-"""Builds libcachegen.so (HIP for gfx950) in-tree with hipcc.
+"""Builds libcachegen.so (HIP for gfx950) in-tree with hipcc; the host-only
+checks (cg_host.cpp, no HIP) with the host C++ compiler.
 
-Flags: no FP contraction (the quantiser and the reconstruction use exactly the
+HIP flags: no FP contraction (the quantiser and the reconstruction use exactly the
 binary32 operations they name), binary32 denormals kept, and no packed-fp32
 instruction selection.
 """
@@ -15,7 +16,11 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcachegen.so")
 SOURCES = ["cg_tables.hip", "cg_encode.hip", "cg_decode.hip", "cg_api.hip"]
+HOST_SOURCES = ["cg_host.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CXX = os.environ.get("CXX", "g++")
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra",
+              "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -38,6 +43,13 @@ def build(verbose: bool = False, extra=()) -> str:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
         objs.append(obj)
+    for src in HOST_SOURCES:
+        obj = os.path.join(objdir, src.replace(".cpp", ".o"))
+        cmd = [CXX, *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        objs.append(obj)
     failed = []
     for src, p in procs:
         out, _ = p.communicate()
@@ -49,7 +61,7 @@ def build(verbose: bool = False, extra=()) -> str:
         elif verbose and text.strip():
             print(text)
     if failed:
-        raise RuntimeError(f"hipcc failed for {failed}")
+        raise RuntimeError(f"compiler failed for {failed}")
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:

@@ -1003,7 +1003,10 @@ static int decode_blob_impl(const uint8_t* tables, size_t tlen, const uint8_t* b
       int cor = 0;
       uint16_t f[NSYM];
       tv_freq(tv.freq[q], i, f);
-      cgo_rc_decode(bytes, nb, nsyms, f, NSYM, sym, NULL, &cor);
+      if (cgo_rc_decode(bytes, nb, nsyms, f, NSYM, sym, NULL, &cor) != OK) {
+        cor = 1; /* an unusable frequency table: the stream is corrupt */
+        memset(sym, 32, nsyms);
+      }
       free(bytes);
       if (cor) bad = 1;
       w += slw;
@@ -1096,7 +1099,10 @@ int cgo_stream_decode(const uint8_t* tables, size_t tlen, int kv, int l, int c, 
   uint16_t f[NSYM];
   tv_freq(tv.freq[q], i, f);
   *corrupt = 0;
-  cgo_rc_decode(bytes, nbytes, tc - ng, f, NSYM, sym, NULL, corrupt);
+  if (cgo_rc_decode(bytes, nbytes, tc - ng, f, NSYM, sym, NULL, corrupt) != OK) {
+    *corrupt = 1; /* an unusable frequency table */
+    memset(sym, 32, tc);
+  }
   float scale_a = tv_f(tv.scale_a, i), step = tv_f(tv.step[q], i);
   int ns = 0, g = 0;
   for (int g0 = 0; g0 < tc; g0 += G, g++) {
