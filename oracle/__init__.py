@@ -29,6 +29,7 @@ CFLAGS = ["-O2", "-std=gnu11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=of
           "-fno-fast-math", "-Wall", "-Wextra"]
 
 NSYM = 64
+ASYM = 256  # anchor symbols: value a in -127..127 is symbol a + 128
 PROB_BITS = 15
 ERRORS = {0: "ok", -1: "invalid argument", -2: "out of memory", -4: "corrupt",
           -5: "capacity", -6: "mismatch"}
@@ -55,7 +56,7 @@ class cgo_params(C.Structure):
                 ("chunk_tokens", C.c_int32), ("group_tokens", C.c_int32),
                 ("n_layer_groups", C.c_int32), ("layer_group_end", C.c_int32 * 3),
                 ("layer_step", C.c_float * 3), ("quality_mult", C.c_float * 3),
-                ("quality_mask", C.c_uint32)]
+                ("quality_mask", C.c_uint32), ("anchor_coding", C.c_int32)]
 
 
 _lib = None
@@ -204,7 +205,8 @@ def channel_stats(x: np.ndarray):
 
 
 def make_params(layers, tokens, channels, chunk_tokens, group_tokens, layer_group_end,
-                layer_step, quality_mult=(1.0, 1.5, 2.5), quality_mask=1) -> cgo_params:
+                layer_step, quality_mult=(1.0, 1.5, 2.5), quality_mask=1,
+                anchor_coding=0) -> cgo_params:
     p = cgo_params()
     p.layers, p.tokens, p.channels = layers, tokens, channels
     p.chunk_tokens, p.group_tokens = chunk_tokens, group_tokens
@@ -214,13 +216,16 @@ def make_params(layers, tokens, channels, chunk_tokens, group_tokens, layer_grou
         p.layer_step[i] = layer_step[i] if i < len(layer_step) else 0.0
         p.quality_mult[i] = quality_mult[i]
     p.quality_mask = quality_mask
+    p.anchor_coding = anchor_coding
     return p
 
 
-def params_for(w) -> cgo_params:
-    """Parameters of a ``synth.Workload``."""
+def params_for(w, anchor_coding: int = 0) -> cgo_params:
+    """Parameters of a ``synth.Workload``; anchor_coding = 1 range-codes the
+    anchors with one 256-symbol table per (kv, layer)."""
     return make_params(w.layers, w.tokens, w.channels, w.chunk_tokens, w.group_tokens,
-                       w.layer_group_end, w.layer_step, w.quality_mult, w.quality_mask)
+                       w.layer_group_end, w.layer_step, w.quality_mult, w.quality_mask,
+                       anchor_coding)
 
 
 def build_tables(p: cgo_params, k: np.ndarray, v: np.ndarray, threads: Optional[int] = None,
@@ -436,6 +441,7 @@ class TablesView:
     step: dict               # q -> f32 [2,L,C]
     inv_step: dict
     freq: dict               # q -> u16 [2,L,C,64]
+    afreq: Optional[np.ndarray] = None  # u16 [2,L,256] anchor tables (tables version 2)
 
 
 def tables_view(t: bytes) -> TablesView:
@@ -459,8 +465,9 @@ def tables_view(t: bytes) -> TablesView:
             step[q] = take(np.float32, n, (2, L, Cc))
             inv_step[q] = take(np.float32, n, (2, L, Cc))
             freq[q] = take(np.uint16, n * NSYM, (2, L, Cc, NSYM))
+    afreq = take(np.uint16, 2 * L * ASYM, (2, L, ASYM)) if h["version"] == 2 else None
     assert off == len(t)
-    return TablesView(h, scale_a, inv_a, step, inv_step, freq)
+    return TablesView(h, scale_a, inv_a, step, inv_step, freq, afreq)
 
 
 def parse_blob_header(b: bytes) -> dict:
@@ -474,28 +481,39 @@ def parse_blob_header(b: bytes) -> dict:
 @dataclass
 class BlobView:
     header: dict
-    row_offset: np.ndarray   # u32 [2,L]
-    anchors: np.ndarray      # i8 [2,L,ng,C]
+    row_offset: np.ndarray   # u32 [2,L]: the delta streams' rows
+    anchors: Optional[np.ndarray]  # i8 [2,L,ng,C] (raw anchors, version 2), else None
     lengths: np.ndarray      # u16 [2,L,C]  (words)
     payload: np.ndarray      # u32 [W]
     payload_offset: int
     tail: bytes              # bytes after the payload words
+    anchor_row_offset: Optional[np.ndarray] = None  # u32 [2,L] (coded anchors, version 3)
+    anchor_lengths: Optional[np.ndarray] = None     # u16 [2,L,C]
 
 
 def blob_view(b: bytes) -> BlobView:
+    """Version 2 (raw anchors): header, u32 rows[2L], i8 anchors[2,L,ng,C], u16
+    lengths[2L,C], pad to 16, payload.  Version 3 (coded anchors): header, u32
+    rows[4L], u16 lengths[4L,C], pad to 16, payload; rows 2L.. are the anchor
+    streams' rows."""
     h = parse_blob_header(b)
     L, Cc, ng, W = h["layers"], h["channels"], h["n_groups"], h["payload_words"]
+    coded = h["version"] == 3
+    R = 4 * L if coded else 2 * L
     buf = np.frombuffer(b, np.uint8)
     off = 64
-    rows = buf[off: off + 8 * L].view(np.uint32).reshape(2, L)
-    off += 8 * L
-    anchors = buf[off: off + 2 * L * ng * Cc].view(np.int8).reshape(2, L, ng, Cc)
-    off += 2 * L * ng * Cc
-    lengths = buf[off: off + 4 * L * Cc].view(np.uint16).reshape(2, L, Cc)
-    off += 4 * L * Cc
+    rows = buf[off: off + 4 * R].view(np.uint32).reshape(R // L, L)
+    off += 4 * R
+    anchors = None
+    if not coded:
+        anchors = buf[off: off + 2 * L * ng * Cc].view(np.int8).reshape(2, L, ng, Cc)
+        off += 2 * L * ng * Cc
+    lengths = buf[off: off + 2 * R * Cc].view(np.uint16).reshape(R // L, L, Cc)
+    off += 2 * R * Cc
     off = (off + 15) // 16 * 16
     payload = buf[off: off + 4 * W].view(np.uint32)
-    return BlobView(h, rows, anchors, lengths, payload, off, bytes(b[off + 4 * W:]))
+    return BlobView(h, rows[:2], anchors, lengths[:2], payload, off, bytes(b[off + 4 * W:]),
+                    rows[2:] if coded else None, lengths[2:] if coded else None)
 
 
 BLOCK_STREAMS = 64  # streams per payload block
@@ -520,9 +538,13 @@ def stream_word_offsets(lengths_of_row: np.ndarray, c: int) -> np.ndarray:
     return np.where(w < UNIT_WORDS * m, inter, tail0 + w - UNIT_WORDS * m)
 
 
-def stream_bytes(bv: BlobView, kv: int, l: int, c: int, extra_words: int = 4) -> bytes:
-    """Bytes of stream (kv, l, c) followed by ``extra_words`` zero words (whatever
-    follows a stream does not change what it decodes to)."""
-    at = int(bv.row_offset[kv, l]) + stream_word_offsets(bv.lengths[kv, l], c)
+def stream_bytes(bv: BlobView, kv: int, l: int, c: int, extra_words: int = 4,
+                 anchors: bool = False) -> bytes:
+    """Bytes of delta stream (kv, l, c), or with ``anchors`` of its anchor
+    stream, followed by ``extra_words`` zero words (whatever follows a stream does
+    not change what it decodes to)."""
+    rows, lens = ((bv.anchor_row_offset, bv.anchor_lengths) if anchors
+                  else (bv.row_offset, bv.lengths))
+    at = int(rows[kv, l]) + stream_word_offsets(lens[kv, l], c)
     words = np.concatenate([bv.payload[at], np.zeros(extra_words, np.uint32)])
     return words.astype(">u4").tobytes()

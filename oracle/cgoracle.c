@@ -32,6 +32,10 @@
 #define TAB_MAGIC 0x31544743u   /* "CGT1" */
 #define BLOB_MAGIC 0x314B4743u  /* "CGK1" */
 #define BLOB_VERSION 2          /* payload blocks laid out as below (stream_layout) */
+#define BLOB_VERSION_CODED 3    /* the same with range-coded anchors (reading R14) */
+#define TAB_VERSION 1           /* tables without anchor tables */
+#define TAB_VERSION_CODED 2     /* tables with one anchor table per (kv, layer) */
+#define ASYM 256                /* anchor symbols: value a in -127..127 is a + 128 */
 #define BLOCK_STREAMS 64        /* streams per payload block */
 #define UNIT_WORDS 4            /* a 16-byte unit of a stream */
 #define MAX_TOKENS (1 << 21)
@@ -445,6 +449,10 @@ static int check_params(const cgo_params* p) {
   }
   if (prev != p->layers) return E_INVAL;
   if ((p->quality_mask & ~7u) || !p->quality_mask) return E_INVAL;
+  if (p->anchor_coding != 0 && p->anchor_coding != 1) return E_INVAL;
+  /* an anchor table counts channels x groups per layer: at most C x T < 2^32 */
+  if (p->anchor_coding && (uint64_t)p->channels * (uint64_t)p->tokens >= (1ull << 32))
+    return E_INVAL;
   for (int q = 0; q < 3; q++)
     if ((p->quality_mask >> q) & 1)
       if (!(p->quality_mult[q] > 0.0f) || !isfinite(p->quality_mult[q])) return E_INVAL;
@@ -453,7 +461,8 @@ static int check_params(const cgo_params* p) {
 
 size_t cgo_tables_size(const cgo_params* p) {
   size_t n = (size_t)2 * p->layers * p->channels;
-  return TAB_HDR + 8 * n + (size_t)nq_of(p->quality_mask) * (8 * n + 2 * NSYM * n);
+  return TAB_HDR + 8 * n + (size_t)nq_of(p->quality_mask) * (8 * n + 2 * NSYM * n) +
+         (p->anchor_coding ? (size_t)2 * p->layers * ASYM * 2 : 0);
 }
 
 static int layer_group(const cgo_params* p, int l) {
@@ -471,12 +480,16 @@ typedef struct {
   const uint8_t* step[3];    /* f32 [2][L][C] per quality (NULL if absent) */
   const uint8_t* inv_step[3];
   const uint8_t* freq[3];    /* u16 [2][L][C][64] */
+  const uint8_t* afreq;      /* u16 [2][L][256] anchor tables (NULL: raw anchors) */
   uint64_t id;
 } tabview;
 
 static int parse_tables(const uint8_t* t, size_t len, tabview* tv) {
-  if (len < TAB_HDR || rd32(t) != TAB_MAGIC || rd32(t + 4) != 1) return E_INVAL;
+  if (len < TAB_HDR || rd32(t) != TAB_MAGIC) return E_INVAL;
+  uint32_t version = rd32(t + 4);
+  if (version != TAB_VERSION && version != TAB_VERSION_CODED) return E_INVAL;
   cgo_params* p = &tv->p;
+  p->anchor_coding = version == TAB_VERSION_CODED;
   p->layers = rdi32(t + 8);
   p->channels = rdi32(t + 12);
   p->tokens = rdi32(t + 16);
@@ -503,6 +516,7 @@ static int parse_tables(const uint8_t* t, size_t len, tabview* tv) {
     tv->inv_step[k] = q; q += 4 * tv->n;
     tv->freq[k] = q; q += 2 * NSYM * tv->n;
   }
+  tv->afreq = p->anchor_coding ? q : NULL;
   tv->id = cgo_tables_id(t, len);
   return OK;
 }
@@ -546,6 +560,28 @@ static void count_symbols(const cgo_params* p, const uint16_t* x, const float* s
   }
 }
 
+/* anchor-symbol counts of one [L][T][C] tensor, per layer over every chunk,
+ * group and channel (reading R14: one anchor table per (kv, layer), counted
+ * over the tensor the tables are built from; anchors do not depend on the
+ * quality) */
+static void count_anchors(const cgo_params* p, const uint16_t* x, const float* inv_a,
+                          uint32_t* counts) {
+  const int L = p->layers, T = p->tokens, C = p->channels;
+  const int CH = p->chunk_tokens, G = p->group_tokens;
+  memset(counts, 0, sizeof(uint32_t) * ASYM * (size_t)L);
+  for (int l = 0; l < L; l++)
+    for (int t0 = 0; t0 < T; t0 += CH) {
+      int tc = (T - t0 < CH) ? T - t0 : CH;
+      for (int g0 = 0; g0 < tc; g0 += G) {
+        const uint16_t* row = x + ((size_t)l * T + t0 + g0) * C;
+        for (int c = 0; c < C; c++) {
+          int a = quant_anchor(cgo_f16_to_f32(row[c]), inv_a[(size_t)l * C + c]);
+          counts[(size_t)l * ASYM + a + 128]++;
+        }
+      }
+    }
+}
+
 int cgo_build_tables(const cgo_params* p, const uint16_t* k, const uint16_t* v,
                      int nthreads, uint8_t* out, size_t cap, size_t* len,
                      uint32_t* counts_out) {
@@ -581,7 +617,7 @@ int cgo_build_tables(const cgo_params* p, const uint16_t* k, const uint16_t* v,
   }
   memset(out, 0, size);
   wr32(out, TAB_MAGIC);
-  wr32(out + 4, 1);
+  wr32(out + 4, p->anchor_coding ? TAB_VERSION_CODED : TAB_VERSION);
   wri32(out + 8, p->layers);
   wri32(out + 12, p->channels);
   wri32(out + 16, p->tokens);
@@ -638,6 +674,23 @@ int cgo_build_tables(const cgo_params* p, const uint16_t* k, const uint16_t* v,
     }
     w += 2 * NSYM * n;
   }
+  if (p->anchor_coding) {
+    uint32_t* ac = (uint32_t*)malloc(sizeof(uint32_t) * ASYM * L);
+    if (!ac) {
+      rc = E_NOMEM;
+      goto done;
+    }
+    for (int kv = 0; kv < 2; kv++) {
+      count_anchors(p, kv ? v : k, inv_a + kv * lc, ac);
+      for (int l = 0; l < L; l++) {
+        uint16_t f[ASYM];
+        cgo_normalize(ac + (size_t)l * ASYM, ASYM, f);
+        memcpy(w, f, 2 * ASYM);
+        w += 2 * ASYM;
+      }
+    }
+    free(ac);
+  }
   *len = size;
 done:
   free(sigma); free(amax); free(scale_a); free(inv_a); free(step); free(inv_step);
@@ -650,6 +703,27 @@ done:
 /* ------------------------------------------------------------------------- */
 
 static size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+/* Blob container offsets (readings R13, R14).  Raw anchors (version 2):
+ * header, u32 row_offset[2L], i8 anchors[2][L][ng][C], u16 lengths[2L][C],
+ * pad to 16, payload.  Coded anchors (version 3): header, u32 row_offset[4L],
+ * u16 lengths[4L][C], pad to 16, payload; rows 0 .. 2L-1 hold the delta
+ * streams of (kv, layer) = (r / L, r % L), rows 2L .. 4L-1 the anchor streams
+ * of (kv, layer) = ((r - 2L) / L, (r - 2L) % L). */
+typedef struct {
+  int rows;  /* payload rows */
+  size_t off_anchor, off_len, off_pay;
+} blobgeo;
+
+static blobgeo blob_geometry(int L, int C, int ng, int coded) {
+  blobgeo g;
+  g.rows = coded ? 4 * L : 2 * L;
+  size_t after_rows = BLOB_HDR + 4 * (size_t)g.rows;
+  g.off_anchor = coded ? 0 : after_rows;
+  g.off_len = coded ? after_rows : after_rows + 2 * (size_t)L * ng * C;
+  g.off_pay = align16(g.off_len + 2 * (size_t)g.rows * C);
+  return g;
+}
 
 int cgo_chunk_geometry(const uint8_t* tables, size_t tlen, int chunk, int32_t* t0,
                        int32_t* tc, int32_t* n_groups) {
@@ -675,8 +749,10 @@ size_t cgo_encode_bound(const uint8_t* tables, size_t tlen, int chunk) {
   if (parse_tables(tables, tlen, &tv) != OK) return 0;
   if (cgo_chunk_geometry(tables, tlen, chunk, &t0, &tc, &ng) != OK) return 0;
   size_t L = tv.p.layers, C = tv.p.channels;
-  size_t body = BLOB_HDR + 8 * L + 2 * L * ng * C + 4 * L * C;
-  return align16(align16(body) + 4 * 2 * L * C * stream_words_bound(tc, ng) + 16);
+  const blobgeo geo = blob_geometry((int)L, (int)C, ng, tv.afreq != NULL);
+  size_t words = 2 * L * C * stream_words_bound(tc, ng);
+  if (tv.afreq) words += 2 * L * C * ((cgo_rc_bound(ng) + 3) / 4);
+  return align16(geo.off_pay + 4 * words + 16);
 }
 
 /* a binary16 value whose exponent field is all ones is infinite or NaN */
@@ -779,16 +855,17 @@ int cgo_encode_chunk(const uint8_t* tables, size_t tlen, const uint16_t* k,
   if (cgo_chunk_geometry(tables, tlen, chunk, &t0, &tc, &ng) != OK) return E_INVAL;
   if (nthreads <= 0) nthreads = 1;
   const int L = tv.p.layers, C = tv.p.channels, T = tv.p.tokens, G = tv.p.group_tokens;
+  const int coded = tv.afreq != NULL;
   const size_t lc = (size_t)L * C;
   const int nsyms = tc - ng;
   const size_t swb = stream_words_bound(tc, ng);
-  const size_t off_anchor = BLOB_HDR + 8 * (size_t)L;
-  const size_t off_len = off_anchor + 2 * (size_t)L * ng * C;
-  const size_t off_pay = align16(off_len + 4 * lc);
-  /* per row: words of every stream, then concatenated in (kv, l, c) order */
-  uint32_t** rows = (uint32_t**)calloc(2 * L, sizeof(uint32_t*));
-  uint32_t* rowlen = (uint32_t*)calloc(2 * L, sizeof(uint32_t));
-  uint16_t* slen = (uint16_t*)calloc(2 * lc, sizeof(uint16_t));
+  const size_t aswb = (cgo_rc_bound(ng) + 3) / 4;
+  const blobgeo geo = blob_geometry(L, C, ng, coded);
+  const int R = geo.rows;
+  /* per row: words of every stream, then concatenated in row order */
+  uint32_t** rows = (uint32_t**)calloc(R, sizeof(uint32_t*));
+  uint32_t* rowlen = (uint32_t*)calloc(R, sizeof(uint32_t));
+  uint16_t* slen = (uint16_t*)calloc((size_t)R * C, sizeof(uint16_t));
   int8_t* anchors = (int8_t*)calloc(2 * (size_t)L * ng * C, 1);
   if (!rows || !rowlen || !slen || !anchors) {
     free(rows); free(rowlen); free(slen); free(anchors);
@@ -800,16 +877,18 @@ int cgo_encode_chunk(const uint8_t* tables, size_t tlen, const uint16_t* k,
     int kv = row / L, l = row % L;
     const uint16_t* x = (kv ? v : k) + ((size_t)l * T + t0) * C;
     uint32_t* buf = (uint32_t*)malloc(sizeof(uint32_t) * (swb * C + 1));
+    uint32_t* abuf = coded ? (uint32_t*)malloc(sizeof(uint32_t) * (aswb * C + 1)) : NULL;
     uint8_t* sym = (uint8_t*)malloc(nsyms + 1);
-    uint8_t* bytes = (uint8_t*)malloc(cgo_rc_bound(nsyms) + 1);
+    uint8_t* bytes = (uint8_t*)malloc(cgo_rc_bound(nsyms > ng ? nsyms : ng) + 1);
     int8_t* anc = (int8_t*)malloc(ng);
-    if (!buf || !sym || !bytes || !anc) {
+    uint8_t* asym = (uint8_t*)malloc(ng);
+    if (!buf || (coded && !abuf) || !sym || !bytes || !anc || !asym) {
 #pragma omp critical
       rc = E_NOMEM;
-      free(buf); free(sym); free(bytes); free(anc);
+      free(buf); free(abuf); free(sym); free(bytes); free(anc); free(asym);
       continue;
     }
-    size_t used = 0;
+    size_t used = 0, aused = 0;
     for (int c = 0; c < C; c++) {
       size_t i = kv * lc + (size_t)l * C + c;
       if (any_nonfinite(x + c, C, tc)) {
@@ -828,21 +907,40 @@ int cgo_encode_chunk(const uint8_t* tables, size_t tlen, const uint16_t* k,
         rc = e;
       }
       size_t nw = bytes_to_words(bytes, nb, buf + used);
-      slen[i] = (uint16_t)nw;
+      slen[(size_t)row * C + c] = (uint16_t)nw;
       used += nw;
+      if (coded) {
+        /* the anchor stream: symbol a + 128 of every group, with the (kv, layer)
+         * anchor table (reading R14) */
+        uint16_t af[ASYM];
+        memcpy(af, tv.afreq + 2 * ASYM * ((size_t)kv * L + l), sizeof(af));
+        for (int g = 0; g < ng; g++) asym[g] = (uint8_t)(anc[g] + 128);
+        e = cgo_rc_encode(asym, ng, af, ASYM, bytes, cgo_rc_bound(ng) + 1, &nb);
+        if (e != OK) {
+#pragma omp critical
+          rc = e;
+        }
+        nw = bytes_to_words(bytes, nb, abuf + aused);
+        slen[(size_t)(2 * L + row) * C + c] = (uint16_t)nw;
+        aused += nw;
+      }
     }
     rows[row] = buf;
     rowlen[row] = (uint32_t)used;
-    free(sym); free(bytes); free(anc);
+    if (coded) {
+      rows[2 * L + row] = abuf;
+      rowlen[2 * L + row] = (uint32_t)aused;
+    }
+    free(sym); free(bytes); free(anc); free(asym);
   }
   size_t W = 0;
-  for (int r = 0; r < 2 * L; r++) W += rowlen[r];
-  size_t total = align16(off_pay + 4 * W + 16);
+  for (int r = 0; r < R; r++) W += rowlen[r];
+  size_t total = align16(geo.off_pay + 4 * W + 16);
   if (rc == OK && total > cap) rc = E_CAPACITY;
   if (rc == OK) {
     memset(out, 0, total);
     wr32(out, BLOB_MAGIC);
-    wr32(out + 4, BLOB_VERSION);
+    wr32(out + 4, coded ? BLOB_VERSION_CODED : BLOB_VERSION);
     wri32(out + 8, L);
     wri32(out + 12, C);
     wri32(out + 16, T);
@@ -854,20 +952,22 @@ int cgo_encode_chunk(const uint8_t* tables, size_t tlen, const uint16_t* k,
     wr32(out + 40, (uint32_t)W);
     wr32(out + 44, PBITS);
     wr64(out + 48, tv.id);
-    size_t woff = 0;
-    uint32_t* laid = (uint32_t*)malloc(sizeof(uint32_t) * (swb * C + 1));
-    for (int r = 0; r < 2 * L; r++) {
+    size_t woff = 0, most = 0;
+    for (int r = 0; r < R; r++)
+      if (rowlen[r] > most) most = rowlen[r];
+    uint32_t* laid = (uint32_t*)malloc(sizeof(uint32_t) * (most + 1));
+    for (int r = 0; r < R; r++) {
       wr32(out + BLOB_HDR + 4 * r, (uint32_t)woff);
       lay_out_row(rows[r], slen + (size_t)r * C, C, laid);
-      memcpy(out + off_pay + 4 * woff, laid, 4 * (size_t)rowlen[r]);
+      memcpy(out + geo.off_pay + 4 * woff, laid, 4 * (size_t)rowlen[r]);
       woff += rowlen[r];
     }
     free(laid);
-    memcpy(out + off_anchor, anchors, 2 * (size_t)L * ng * C);
-    memcpy(out + off_len, slen, 2 * 2 * lc);
+    if (!coded) memcpy(out + geo.off_anchor, anchors, 2 * (size_t)L * ng * C);
+    memcpy(out + geo.off_len, slen, 2 * (size_t)R * C);
     *len = total;
   }
-  for (int r = 0; r < 2 * L; r++) free(rows[r]);
+  for (int r = 0; r < R; r++) free(rows[r]);
   free(rows); free(rowlen); free(slen); free(anchors);
   return rc;
 }
@@ -904,15 +1004,19 @@ typedef struct {
   int32_t L, C, T, t0, tc, G, ng, q;
   uint32_t W;
   uint64_t id;
-  const uint8_t* rows;     /* u32 [2][L] */
-  const int8_t* anchors;   /* i8 [2][L][ng][C] */
-  const uint8_t* lens;     /* u16 [2][L][C] */
+  int coded;               /* anchors range-coded (version 3) */
+  const uint8_t* rows;     /* u32 [rows]: [2][L] delta rows, then [2][L] anchor rows if coded */
+  const int8_t* anchors;   /* i8 [2][L][ng][C], raw anchors only */
+  const uint8_t* lens;     /* u16 [rows][C] */
   const uint8_t* payload;  /* W big-endian-within-word u32 words */
   size_t payload_bytes_avail; /* payload plus trailing padding */
 } blobview;
 
 static int parse_blob(const tabview* tv, const uint8_t* b, size_t blen, blobview* bv) {
-  if (blen < BLOB_HDR || rd32(b) != BLOB_MAGIC || rd32(b + 4) != BLOB_VERSION) return E_INVAL;
+  if (blen < BLOB_HDR || rd32(b) != BLOB_MAGIC) return E_INVAL;
+  uint32_t version = rd32(b + 4);
+  if (version != BLOB_VERSION && version != BLOB_VERSION_CODED) return E_INVAL;
+  bv->coded = version == BLOB_VERSION_CODED;
   bv->L = rdi32(b + 8); bv->C = rdi32(b + 12); bv->T = rdi32(b + 16);
   bv->t0 = rdi32(b + 20); bv->tc = rdi32(b + 24); bv->G = rdi32(b + 28);
   bv->ng = rdi32(b + 32); bv->q = rdi32(b + 36); bv->W = rd32(b + 40);
@@ -922,21 +1026,19 @@ static int parse_blob(const tabview* tv, const uint8_t* b, size_t blen, blobview
       bv->G != tv->p.group_tokens)
     return E_MISMATCH;
   if (bv->id != tv->id) return E_MISMATCH;
+  if (bv->coded != (tv->afreq != NULL)) return E_MISMATCH;
   if (bv->q < 0 || bv->q > 2 || !tv->freq[bv->q]) return E_MISMATCH;
   int CH = tv->p.chunk_tokens;
   if (bv->t0 < 0 || bv->t0 % CH || bv->t0 >= bv->T) return E_INVAL;
   int tc = (bv->T - bv->t0 < CH) ? bv->T - bv->t0 : CH;
   if (bv->tc != tc || bv->ng != (tc + bv->G - 1) / bv->G) return E_INVAL;
-  size_t L = bv->L, C = bv->C;
-  size_t off_anchor = BLOB_HDR + 8 * L;
-  size_t off_len = off_anchor + 2 * L * bv->ng * C;
-  size_t off_pay = align16(off_len + 4 * L * C);
-  if (align16(off_pay + 4 * (size_t)bv->W + 16) > blen) return E_INVAL;
+  const blobgeo geo = blob_geometry(bv->L, bv->C, bv->ng, bv->coded);
+  if (align16(geo.off_pay + 4 * (size_t)bv->W + 16) > blen) return E_INVAL;
   bv->rows = b + BLOB_HDR;
-  bv->anchors = (const int8_t*)(b + off_anchor);
-  bv->lens = b + off_len;
-  bv->payload = b + off_pay;
-  bv->payload_bytes_avail = blen - off_pay;
+  bv->anchors = bv->coded ? NULL : (const int8_t*)(b + geo.off_anchor);
+  bv->lens = b + geo.off_len;
+  bv->payload = b + geo.off_pay;
+  bv->payload_bytes_avail = blen - geo.off_pay;
   return OK;
 }
 
@@ -961,8 +1063,56 @@ static uint8_t* stream_bytes(const blobview* bv, size_t base, int ns, int m, con
   return out;
 }
 
-/* decode a blob's rows; each stream starts at its row offset plus the lengths of
- * the streams before it; the decoder reads on into whatever bytes follow */
+/* The streams of payload row r, channel after channel: each stream starts at
+ * the row offset plus the lengths of the streams before it, laid out by
+ * blocks as in lay_out_row. */
+typedef struct {
+  const blobview* bv;
+  int r, R, C, ns, m;
+  size_t w, bbase;
+  uint16_t blen16[BLOCK_STREAMS];
+  size_t tail[BLOCK_STREAMS];
+} rowwalk;
+
+static void rowwalk_start(rowwalk* it, const blobview* bv, int r, int R, int C) {
+  it->bv = bv;
+  it->r = r;
+  it->R = R;
+  it->C = C;
+  it->w = rd32(bv->rows + 4 * (size_t)r);
+  it->bbase = it->w;
+  it->ns = it->m = 0;
+}
+
+/* bytes of stream c of the row (called for c = 0, 1, ... in order); sets
+ * *over when the stream runs past the payload */
+static uint8_t* rowwalk_next(rowwalk* it, int c, size_t* nb, int* over) {
+  const blobview* bv = it->bv;
+  if (c % BLOCK_STREAMS == 0) { /* a new block: its streams' lengths and layout */
+    size_t i = (size_t)it->r * it->C + c;
+    it->bbase = it->w;
+    it->ns = it->C - c < BLOCK_STREAMS ? it->C - c : BLOCK_STREAMS;
+    for (int j = 0; j < it->ns; j++)
+      it->blen16[j] = (uint16_t)(bv->lens[2 * (i + j)] | (bv->lens[2 * (i + j) + 1] << 8));
+    it->m = block_units(it->blen16, it->ns);
+    block_tails(it->blen16, it->ns, it->m, it->tail);
+  }
+  size_t slw = it->blen16[c % BLOCK_STREAMS];
+  if (it->w + slw > bv->W) *over = 1;
+  uint8_t* bytes = stream_bytes(bv, it->bbase, it->ns, it->m, it->tail, c % BLOCK_STREAMS, slw, nb);
+  it->w += slw;
+  return bytes;
+}
+
+/* whether the row's streams end where the next row starts */
+static int rowwalk_ends_right(const rowwalk* it) {
+  size_t next = (it->r + 1 < it->R) ? rd32(it->bv->rows + 4 * (size_t)(it->r + 1)) : it->bv->W;
+  return it->w == next;
+}
+
+/* decode a blob's rows: for coded anchors the (kv, layer) row's anchor streams
+ * first, then its delta streams; the decoder reads on into whatever bytes
+ * follow a stream */
 static int decode_blob_impl(const uint8_t* tables, size_t tlen, const uint8_t* blob,
                             size_t blen, uint16_t* k_out, uint16_t* v_out, uint8_t* syms,
                             int nthreads, int* corrupt) {
@@ -974,33 +1124,42 @@ static int decode_blob_impl(const uint8_t* tables, size_t tlen, const uint8_t* b
   if (rc != OK) return rc;
   if (nthreads <= 0) nthreads = 1;
   const int L = bv.L, C = bv.C, T = bv.T, G = bv.G, tc = bv.tc, ng = bv.ng, q = bv.q;
+  const int R = bv.coded ? 4 * L : 2 * L;
   const size_t lc = (size_t)L * C;
   const int nsyms = tc - ng;
   int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : bad)
   for (int row = 0; row < 2 * L; row++) {
     int kv = row / L, l = row % L;
-    uint8_t* sym = (uint8_t*)malloc(nsyms + 1);
-    size_t w = rd32(bv.rows + 4 * row);
-    uint16_t blen16[BLOCK_STREAMS];
-    size_t tail[BLOCK_STREAMS];
-    size_t bbase = w;
-    int ns = 0, m = 0;
+    uint8_t* sym = (uint8_t*)malloc((nsyms > ng ? nsyms : ng) + 1);
+    /* the row's anchors [ng][C] */
+    int8_t* anc = (int8_t*)malloc((size_t)ng * C + 1);
+    rowwalk it;
+    size_t nb = 0;
+    if (bv.coded) {
+      uint16_t af[ASYM];
+      memcpy(af, tv.afreq + 2 * ASYM * ((size_t)kv * L + l), sizeof(af));
+      rowwalk_start(&it, &bv, 2 * L + row, R, C);
+      for (int c = 0; c < C; c++) {
+        int cor = 0;
+        uint8_t* bytes = rowwalk_next(&it, c, &nb, &cor);
+        if (cgo_rc_decode(bytes, nb, ng, af, ASYM, sym, NULL, &cor) != OK) {
+          cor = 1; /* an unusable anchor table */
+          memset(sym, 128, ng);
+        }
+        free(bytes);
+        if (cor) bad = 1;
+        for (int g = 0; g < ng; g++) anc[(size_t)g * C + c] = (int8_t)(sym[g] - 128);
+      }
+      if (!rowwalk_ends_right(&it)) bad = 1; /* lengths disagree with the row offsets */
+    } else {
+      memcpy(anc, bv.anchors + ((size_t)kv * L + l) * ng * C, (size_t)ng * C);
+    }
+    rowwalk_start(&it, &bv, row, R, C);
     for (int c = 0; c < C; c++) {
       size_t i = kv * lc + (size_t)l * C + c;
-      if (c % BLOCK_STREAMS == 0) { /* a new block: its streams' lengths and layout */
-        bbase = w;
-        ns = C - c < BLOCK_STREAMS ? C - c : BLOCK_STREAMS;
-        for (int j = 0; j < ns; j++)
-          blen16[j] = (uint16_t)(bv.lens[2 * (i + j)] | (bv.lens[2 * (i + j) + 1] << 8));
-        m = block_units(blen16, ns);
-        block_tails(blen16, ns, m, tail);
-      }
-      size_t slw = blen16[c % BLOCK_STREAMS];
-      if (w + slw > bv.W) bad = 1;
-      size_t nb = 0;
-      uint8_t* bytes = stream_bytes(&bv, bbase, ns, m, tail, c % BLOCK_STREAMS, slw, &nb);
       int cor = 0;
+      uint8_t* bytes = rowwalk_next(&it, c, &nb, &cor);
       uint16_t f[NSYM];
       tv_freq(tv.freq[q], i, f);
       if (cgo_rc_decode(bytes, nb, nsyms, f, NSYM, sym, NULL, &cor) != OK) {
@@ -1009,12 +1168,11 @@ static int decode_blob_impl(const uint8_t* tables, size_t tlen, const uint8_t* b
       }
       free(bytes);
       if (cor) bad = 1;
-      w += slw;
       float scale_a = tv_f(tv.scale_a, i), step = tv_f(tv.step[q], i);
       int ns = 0, g = 0;
       for (int g0 = 0; g0 < tc; g0 += G, g++) {
         int ge = (g0 + G < tc) ? g0 + G : tc;
-        int8_t a = bv.anchors[(((size_t)kv * L + l) * ng + g) * C + c];
+        int8_t a = anc[(size_t)g * C + c];
         float ahat = anchor_value(a, scale_a);
         size_t o = ((size_t)l * T + bv.t0 + g0) * C + c;
         if (k_out) (kv ? v_out : k_out)[o] = cgo_f32_to_f16(ahat);
@@ -1027,9 +1185,9 @@ static int decode_blob_impl(const uint8_t* tables, size_t tlen, const uint8_t* b
         }
       }
     }
-    size_t next = (row + 1 < 2 * L) ? rd32(bv.rows + 4 * (row + 1)) : bv.W;
-    if (w != next) bad = 1; /* lengths disagree with the row offsets */
+    if (!rowwalk_ends_right(&it)) bad = 1; /* lengths disagree with the row offsets */
     free(sym);
+    free(anc);
   }
   *corrupt = bad;
   return OK;

@@ -36,6 +36,9 @@ typedef struct {
   float layer_step[3];
   float quality_mult[3];
   uint32_t quality_mask;
+  /* 1: anchors range-coded with one 256-symbol table per (kv, layer) (tables
+   * version 2, blob version 3); 0: anchors stored as raw bytes */
+  int32_t anchor_coding;
 } cgo_params;
 
 /* IEEE 754 binary16 conversions */
