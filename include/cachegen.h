@@ -76,6 +76,11 @@ typedef struct {
   float layer_step[3];              /* delta step per layer group, channel-std units */
   float quality_mult[3];            /* step multiplier of H, M, L */
   uint32_t quality_mask;            /* bit q set: build tables for quality q */
+  int32_t anchor_coding;            /* 0: anchors stored as raw bytes (tables version 1,
+                                       blobs version 2); 1: anchors range-coded with one
+                                       256-symbol table per (kv, layer) counted like the
+                                       delta tables (tables version 2, blobs version 3;
+                                       channels x tokens must stay below 2^32) */
 } cg_params;
 
 /* Header fields of one chunk blob, read from host memory by cg_chunk_info_parse. */
@@ -85,7 +90,7 @@ typedef struct {
   int32_t chunk_tokens;  /* tokens in this chunk (the last chunk may be short) */
   int32_t group_tokens, n_groups, quality;
   uint32_t payload_words;
-  uint32_t reserved;
+  uint32_t version;      /* blob format: 2 raw anchors, 3 range-coded anchors */
   uint64_t tables_id;    /* identity of the tables the blob was coded with */
   uint64_t blob_bytes;   /* total size of the blob */
 } cg_chunk_info;

@@ -39,7 +39,7 @@ class cg_params(C.Structure):
                 ("chunk_tokens", C.c_int32), ("group_tokens", C.c_int32),
                 ("n_layer_groups", C.c_int32), ("layer_group_end", C.c_int32 * 3),
                 ("layer_step", C.c_float * 3), ("quality_mult", C.c_float * 3),
-                ("quality_mask", C.c_uint32)]
+                ("quality_mask", C.c_uint32), ("anchor_coding", C.c_int32)]
 
 
 class cg_chunk_plan_in(C.Structure):
@@ -51,7 +51,7 @@ class cg_chunk_info(C.Structure):
     _fields_ = [("layers", C.c_int32), ("channels", C.c_int32), ("total_tokens", C.c_int32),
                 ("token_offset", C.c_int32), ("chunk_tokens", C.c_int32),
                 ("group_tokens", C.c_int32), ("n_groups", C.c_int32), ("quality", C.c_int32),
-                ("payload_words", C.c_uint32), ("reserved", C.c_uint32),
+                ("payload_words", C.c_uint32), ("version", C.c_uint32),
                 ("tables_id", C.c_uint64), ("blob_bytes", C.c_uint64)]
 
 
@@ -135,7 +135,7 @@ def _dev_ptr(t, dtype=None, what="tensor"):
 
 def make_params(layers, tokens, channels, chunk_tokens=1536, group_tokens=10,
                 layer_group_end=None, layer_step=(0.5, 1.0, 1.5), quality_mult=(1.0, 1.5, 2.5),
-                quality_mask=1) -> cg_params:
+                quality_mask=1, anchor_coding=0) -> cg_params:
     p = cg_params()
     p.layers, p.tokens, p.channels = layers, tokens, channels
     p.chunk_tokens, p.group_tokens = chunk_tokens, group_tokens
@@ -146,6 +146,7 @@ def make_params(layers, tokens, channels, chunk_tokens=1536, group_tokens=10,
         p.layer_step[i] = layer_step[i] if i < len(layer_step) else 0.0
         p.quality_mult[i] = quality_mult[i]
     p.quality_mask = quality_mask
+    p.anchor_coding = anchor_coding
     return p
 
 

@@ -66,7 +66,7 @@ void init_dev_tables(DevTables& t, const cg_params& p) {
   t.G = p.group_tokens;
   t.nblk = (p.channels + kLanes - 1) / kLanes;
   t.mask = p.quality_mask;
-  t.lay = tab_layout(p.layers, p.channels, p.quality_mask);
+  t.lay = tab_layout(p.layers, p.channels, p.quality_mask, p.anchor_coding != 0);
 }
 
 size_t img_bytes(const DevTables& t) { return (size_t)2 * t.L * t.nblk * kImgRows * kLanes * 2; }
@@ -75,7 +75,7 @@ void write_header(uint8_t* h, const cg_params& p) {
   memset(h, 0, kTabHdr);
   uint32_t u[20] = {0};
   u[0] = kTabMagic;
-  u[1] = 1;
+  u[1] = p.anchor_coding ? kTabVersionCoded : kTabVersion;
   u[2] = (uint32_t)p.layers;
   u[3] = (uint32_t)p.channels;
   u[4] = (uint32_t)p.tokens;
@@ -204,11 +204,20 @@ ChunkGeo chunk_geo(const DevTables& t, int chunk) {
 
 int n_chunks_of(const DevTables& t) { return (t.T + t.CH - 1) / t.CH; }
 
+bool coded_anchors(const DevTables& t) { return t.lay.off_afreq != 0; }
+
+// the layout of a blob of `ng` groups coded with these tables
+BlobLayout blob_layout_of(const DevTables& t, int ng) {
+  return blob_layout(t.L, t.C, ng, coded_anchors(t));
+}
+
 int check_info_against(const cg_tables* h, const cg_chunk_info& in) {
   const DevTables& t = h->t;
   if (in.layers != t.L || in.channels != t.C || in.total_tokens != t.T || in.group_tokens != t.G)
     return fail(CG_E_MISMATCH, "blob shape differs from the tables");
   if (in.tables_id != h->id) return fail(CG_E_MISMATCH, "blob was coded with other tables");
+  if ((in.version == kBlobVersionCoded) != coded_anchors(t))
+    return fail(CG_E_MISMATCH, "blob format differs from the tables' anchor coding");
   if (!((t.mask >> in.quality) & 1u)) return fail(CG_E_MISMATCH, "quality not in the tables");
   if (in.token_offset % t.CH) return fail(CG_E_INVAL, "token_offset is not a chunk start");
   const ChunkGeo g = chunk_geo(t, in.token_offset / t.CH);
@@ -222,11 +231,12 @@ struct PagedOut {
   uint32_t n_blocks, num_pages, shift;
 };
 
-// Enqueues the decode of n blobs whose headers are already checked, into
-// [L][T][C] tensors or, with pg, into paged pools.
-int enqueue_decode(const cg_tables* h, int n, const void* const* blobs, const cg_chunk_info* infos,
-                   void* k_out, void* v_out, uint32_t* status, hipStream_t st,
-                   const PagedOut* pg = nullptr) {
+// The decode launches of n blobs whose headers are already checked, into
+// [L][T][C] tensors or, with pg, into paged pools; anc[i] = blob i's anchors
+// (i8 [2][L][ng][C]).
+int enqueue_decode_chunks(const cg_tables* h, int n, const void* const* blobs,
+                          const cg_chunk_info* infos, const int8_t* const* anc, void* k_out,
+                          void* v_out, uint32_t* status, hipStream_t st, const PagedOut* pg) {
   const DevTables& t = h->t;
   // chunks grouped by quality, up to 4 per workgroup (one wave per chunk and kv)
   std::vector<int> byq[3];
@@ -270,7 +280,7 @@ int enqueue_decode(const cg_tables* h, int n, const void* const* blobs, const cg
       for (size_t w = 0; w < groups[gi].size(); w++) {
         const int i = groups[gi][w];
         const cg_chunk_info& in = infos[i];
-        const BlobLayout bl = blob_layout(t.L, t.C, in.n_groups);
+        const BlobLayout bl = blob_layout_of(t, in.n_groups);
         DecChunk& dc = a.chunks[nc];
         dc.blob = static_cast<const uint8_t*>(blobs[i]);
         dc.blob_bytes = (uint32_t)in.blob_bytes;
@@ -278,7 +288,8 @@ int enqueue_decode(const cg_tables* h, int n, const void* const* blobs, const cg
         dc.tc = in.chunk_tokens;
         dc.ng = in.n_groups;
         dc.q = in.quality;
-        dc.off_anchor = (uint32_t)bl.off_anchor;
+        dc.anc = anc[i];
+        dc.anc_bytes = (uint32_t)((size_t)2 * t.L * in.n_groups * t.C);
         dc.off_len = (uint32_t)bl.off_len;
         dc.off_pay = (uint32_t)bl.off_pay;
         dc.W = in.payload_words;
@@ -301,6 +312,60 @@ int enqueue_decode(const cg_tables* h, int n, const void* const* blobs, const cg
   return CG_OK;
 }
 
+// Enqueues the decode of n checked blobs.  Raw anchors are read from the
+// blobs; coded anchors are first decoded into a stream-ordered allocation of
+// 2 L ng C bytes per blob (hipMallocAsync on st, freed on st after the decode).
+int enqueue_decode(const cg_tables* h, int n, const void* const* blobs, const cg_chunk_info* infos,
+                   void* k_out, void* v_out, uint32_t* status, hipStream_t st,
+                   const PagedOut* pg = nullptr) {
+  const DevTables& t = h->t;
+  std::vector<const int8_t*> anc(n);
+  if (!coded_anchors(t)) {
+    for (int i = 0; i < n; i++)
+      anc[i] = reinterpret_cast<const int8_t*>(blobs[i]) + blob_layout_of(t, infos[i].n_groups).off_anchor;
+    return enqueue_decode_chunks(h, n, blobs, infos, anc.data(), k_out, v_out, status, st, pg);
+  }
+  std::vector<size_t> off(n);
+  size_t bytes = 0;
+  for (int i = 0; i < n; i++) {
+    off[i] = bytes;
+    bytes += align256((size_t)2 * t.L * infos[i].n_groups * t.C);
+  }
+  int8_t* ws = nullptr;
+  HIP_TRY(hipMallocAsync((void**)&ws, bytes, st), "hipMallocAsync(anchors)");
+  int rc = CG_OK;
+  for (int i0 = 0; i0 < n && rc == CG_OK; i0 += kDecMaxChunks) {
+    AnchorDecodeArgs a;
+    memset(&a, 0, sizeof(a));
+    a.L = t.L;
+    a.C = t.C;
+    a.nblk = t.nblk;
+    a.nchunks = std::min(kDecMaxChunks, n - i0);
+    a.afreq = reinterpret_cast<const uint16_t*>(t.ser + t.lay.off_afreq);
+    a.status = status;
+    for (int j = 0; j < a.nchunks; j++) {
+      const cg_chunk_info& in = infos[i0 + j];
+      const BlobLayout bl = blob_layout_of(t, in.n_groups);
+      AncChunk& c = a.chunks[j];
+      c.blob = static_cast<const uint8_t*>(blobs[i0 + j]);
+      c.blob_bytes = (uint32_t)in.blob_bytes;
+      c.ng = in.n_groups;
+      c.off_len = (uint32_t)bl.off_len;
+      c.off_pay = (uint32_t)bl.off_pay;
+      c.W = in.payload_words;
+      c.out = ws + off[i0 + j];
+    }
+    const hipError_t e = launch_anchor_decode(a, st);
+    if (e != hipSuccess) rc = hip_fail(e, "anchor decode launch");
+  }
+  for (int i = 0; i < n; i++) anc[i] = ws + off[i];
+  if (rc == CG_OK)
+    rc = enqueue_decode_chunks(h, n, blobs, infos, anc.data(), k_out, v_out, status, st, pg);
+  const hipError_t e = hipFreeAsync(ws, st);
+  if (rc == CG_OK && e != hipSuccess) rc = hip_fail(e, "hipFreeAsync(anchors)");
+  return rc;
+}
+
 // Arguments of an encode batch, checked before any launch.
 int check_encode_args(const cg_tables* h, const void* k_dev, const void* v_dev, int32_t n,
                       const int32_t* chunks, const int32_t* qualities, void* const* outs_dev,
@@ -315,7 +380,7 @@ int check_encode_args(const cg_tables* h, const void* k_dev, const void* v_dev, 
     if (qualities[i] < 0 || qualities[i] > 2 || !((t.mask >> qualities[i]) & 1u))
       return fail(CG_E_MISMATCH, "quality not in the tables");
     const ChunkGeo g = chunk_geo(t, chunks[i]);
-    if (caps[i] < blob_layout(t.L, t.C, g.ng).off_pay + 16)
+    if (caps[i] < blob_layout_of(t, g.ng).off_pay + 16)
       return fail(CG_E_CAPACITY, "output smaller than the blob's fixed part");
   }
   return CG_OK;
@@ -327,6 +392,11 @@ size_t stream_scratch_words(const DevTables& t) {
   return std::max<size_t>(stream_words_bound(t.CH - (t.CH + t.G - 1) / t.G), 1) + 1;
 }
 
+// the same for an anchor stream (one symbol per group), 0 without coded anchors
+size_t anchor_scratch_words(const DevTables& t) {
+  return coded_anchors(t) ? std::max<size_t>(stream_words_bound((t.CH + t.G - 1) / t.G), 1) + 1 : 0;
+}
+
 // The fields of one blob of an encode launch, but for its scratch buffers.
 void init_enc_blob(EncBlob& B, const DevTables& t, int chunk, int q, void* out, size_t cap) {
   const ChunkGeo g = chunk_geo(t, chunk);
@@ -336,7 +406,7 @@ void init_enc_blob(EncBlob& B, const DevTables& t, int chunk, int q, void* out, 
   B.tc = g.tc;
   B.ng = g.ng;
   B.q = q;
-  B.lay = blob_layout(t.L, t.C, g.ng);
+  B.lay = blob_layout_of(t, g.ng);
   B.img = t.img[q];
   B.inv_step = reinterpret_cast<const float*>(t.ser + t.lay.off_inv_step[q]);
 }
@@ -359,6 +429,8 @@ void init_enc_args(EncodeArgs& a, const cg_tables* h, const void* k_dev, const v
   a.tables_id = h->id;
   a.row0 = 0;
   a.nrows = 2 * t.L;
+  a.rows_total = coded_anchors(t) ? 4 * t.L : 2 * t.L;
+  a.afreq = coded_anchors(t) ? reinterpret_cast<const uint16_t*>(t.ser + t.lay.off_afreq) : nullptr;
   a.waves = 1;
 }
 
@@ -371,7 +443,7 @@ void finish_blob(const DevTables& t, int chunk, const uint32_t* sw, size_t* out_
   } else if (sw[1]) {
     if (*rc == CG_OK) *rc = fail(CG_E_CAPACITY, "blob larger than the output buffer");
   } else {
-    *out_len = blob_bytes(blob_layout(t.L, t.C, chunk_geo(t, chunk).ng), sw[0]);
+    *out_len = blob_bytes(blob_layout_of(t, chunk_geo(t, chunk).ng), sw[0]);
   }
 }
 
@@ -450,9 +522,10 @@ int cg_build_tables_grouped(const cg_params* params_in, int32_t grouping, const 
   }
   const size_t n = t.lay.n;
   const size_t counts_words = (size_t)n * t.lay.nq * kNSym;
+  const size_t acounts_words = t.lay.off_afreq ? (size_t)2 * t.L * kASym : 0;
   // workspace: [s1 | sa | sc] u64, amax u32, 8 flag words (2 and 3 hold the
-  // tables id), counts; then the id digests, then pooled counts
-  const size_t tmp_bytes = 3 * 8 * n + 4 * n + 32 + 4 * counts_words;
+  // tables id), counts, anchor counts; then the id digests, then pooled counts
+  const size_t tmp_bytes = 3 * 8 * n + 4 * n + 32 + 4 * (counts_words + acounts_words);
   const size_t dig_off = align256(tmp_bytes);
   const size_t pool_off = align256(dig_off + id_digest_bytes(t));
   const size_t pool_bytes = grouping ? 4 * pooled_words(t, grouping) : 0;
@@ -475,6 +548,7 @@ int cg_build_tables_grouped(const cg_params* params_in, int32_t grouping, const 
   sb.flags = sb.amax + n;
   uint64_t* id_dev = reinterpret_cast<uint64_t*>(sb.flags + 2);
   uint32_t* counts = sb.flags + 8;
+  uint32_t* acounts = counts + counts_words;
   uint64_t* dig = reinterpret_cast<uint64_t*>(tmp + dig_off);
   uint32_t* pooled = reinterpret_cast<uint32_t*>(tmp + pool_off);
   uint8_t hdr[kTabHdr];
@@ -486,10 +560,11 @@ int cg_build_tables_grouped(const cg_params* params_in, int32_t grouping, const 
   if (e == hipSuccess) e = launch_stats(k, 0, t.L, t.T, t.C, sb, st);
   if (e == hipSuccess) e = launch_stats(v, 1, t.L, t.T, t.C, sb, st);
   if (e == hipSuccess) e = launch_finalize(*params, sb, t, st);
-  if (e == hipSuccess) e = launch_histogram(k, 0, t, counts, st);
-  if (e == hipSuccess) e = launch_histogram(v, 1, t, counts, st);
+  if (e == hipSuccess) e = launch_histogram(k, 0, t, counts, acounts, st);
+  if (e == hipSuccess) e = launch_histogram(v, 1, t, counts, acounts, st);
   if (e == hipSuccess && grouping) e = launch_pool(t, counts, grouping, pooled, sb.flags + 4, st);
   if (e == hipSuccess) e = launch_normalize(t, counts, st);
+  if (e == hipSuccess) e = launch_normalize_anchors(t, acounts, st);
   if (e == hipSuccess) e = launch_images(t, st);
   // the id of whatever was built; discarded below when the build failed
   if (e == hipSuccess) e = launch_tables_id(t, dig, id_dev, st);
@@ -580,8 +655,10 @@ int cg_encode_bound(const cg_tables* h, int32_t chunk, size_t* max_bytes) {
   if (!h || !max_bytes) return fail(CG_E_INVAL, "NULL argument");
   if (chunk < 0 || chunk >= n_chunks_of(h->t)) return fail(CG_E_INVAL, "chunk out of range");
   const ChunkGeo g = chunk_geo(h->t, chunk);
-  const BlobLayout bl = blob_layout(h->t.L, h->t.C, g.ng);
-  *max_bytes = blob_bytes(bl, h->t.lay.n * stream_words_bound(g.tc - g.ng));
+  const BlobLayout bl = blob_layout_of(h->t, g.ng);
+  size_t words = h->t.lay.n * stream_words_bound(g.tc - g.ng);
+  if (coded_anchors(h->t)) words += h->t.lay.n * stream_words_bound(g.ng);
+  *max_bytes = blob_bytes(bl, words);
   return CG_OK;
 }
 
@@ -610,8 +687,10 @@ int cg_encode_batch(const cg_tables* ch, const void* k_dev, const void* v_dev, i
   DeviceGuard dg(h->dev);
   if (!dg.ok) return fail(CG_E_HIP, "cannot select the tables' device");
   std::lock_guard<std::mutex> lk(h->mu);
-  const size_t swb = stream_scratch_words(t);
-  const size_t slot_words = (size_t)2 * t.L * t.nblk * kLanes * swb;  // whole 64-stream blocks
+  const size_t swb = stream_scratch_words(t), aswb = anchor_scratch_words(t);
+  // whole 64-stream blocks of 2L rows: the delta rows, then (coded anchors) the
+  // anchor rows in the same buffers
+  const size_t slot_words = (size_t)2 * t.L * t.nblk * kLanes * std::max(swb, aswb);
   // Blobs per launch: at most what the scratch budget holds.  When one more
   // launch is enough to make every launch fit the device at once (a blob is
   // 2 L nblk waves), take that, so that no second round of a few waves per
@@ -683,6 +762,12 @@ int cg_encode_batch(const cg_tables* ch, const void* k_dev, const void* v_dev, i
       a.waves = std::max(a.waves, w + 1);
     }
     HIP_TRY(launch_encode(a, st), "encode launch");
+    if (coded_anchors(t)) {
+      // the anchor rows of the same blobs, through the same scratch
+      a.row0 = 2 * t.L;
+      a.swb = aswb;
+      HIP_TRY(launch_encode(a, st), "anchor encode launch");
+    }
   }
   HIP_TRY(hipMemcpyAsync(h->enc_host, h->enc_status, 16 * (size_t)n, hipMemcpyDeviceToHost, st),
           "encode status");
@@ -703,8 +788,8 @@ int cg_encode_batch_noalloc(const cg_tables* ch, const void* k_dev, const void* 
   // The array holds 64 status words, then for a range of (kv, layer) rows their
   // stream lengths, row and block totals and stream words; the range is as many
   // rows as fit, a blob is coded range after range.
-  const size_t swb = stream_scratch_words(t);
-  const size_t per_row = (size_t)t.C + 1 + t.nblk + (size_t)t.nblk * kLanes * swb;
+  const size_t swb = stream_scratch_words(t), aswb = anchor_scratch_words(t);
+  const size_t per_row = (size_t)t.C + 1 + t.nblk + (size_t)t.nblk * kLanes * std::max(swb, aswb);
   const size_t fixed = 64 + 3 * 63;  // status words and the ranges' alignment
   const size_t rows_fit = (kStaticScratchBytes / 4 - fixed) / per_row;
   if (rows_fit < 1)
@@ -725,11 +810,16 @@ int cg_encode_batch_noalloc(const cg_tables* ch, const void* k_dev, const void* 
   rc = CG_OK;
   for (int i = 0; i < n; i++) {
     HIP_TRY(launch_zero_words(status, 4, st), "clear status");
-    for (int r0 = 0; r0 < 2 * t.L; r0 += rows_max) {
+    // delta rows 0 .. 2L-1, then (coded anchors) anchor rows 2L .. 4L-1; no
+    // range straddles 2L
+    const int rows_total = coded_anchors(t) ? 4 * t.L : 2 * t.L;
+    for (int r0 = 0; r0 < rows_total;) {
+      const int part_end = r0 < 2 * t.L ? 2 * t.L : rows_total;
       EncodeArgs a;
-      init_enc_args(a, ch, k_dev, v_dev, swb);
+      init_enc_args(a, ch, k_dev, v_dev, r0 < 2 * t.L ? swb : aswb);
       a.row0 = r0;
-      a.nrows = std::min(rows_max, 2 * t.L - r0);
+      a.nrows = std::min(rows_max, part_end - r0);
+      r0 += a.nrows;
       a.nblobs = 1;
       a.n_groups = 1;
       a.groups[0].blob[0] = 0;

@@ -44,9 +44,12 @@ struct StatsBuf {
 hipError_t launch_stats(const uint16_t* x, int kv, int L, int T, int C, const StatsBuf& sb,
                         hipStream_t st);
 hipError_t launch_finalize(const cg_params& p, const StatsBuf& sb, DevTables& t, hipStream_t st);
+// acounts: [2][L][256] anchor-symbol counts, counted only when the tables code anchors
 hipError_t launch_histogram(const uint16_t* x, int kv, const DevTables& t, uint32_t* counts,
-                            hipStream_t st);
+                            uint32_t* acounts, hipStream_t st);
 hipError_t launch_normalize(const DevTables& t, const uint32_t* counts, hipStream_t st);
+// the anchor tables (no-op without coded anchors)
+hipError_t launch_normalize_anchors(const DevTables& t, const uint32_t* acounts, hipStream_t st);
 // pooled counts for a coarser table grouping (1 per layer, 2 per channel, 3 per
 // (kv, quality)); pooled needs pooled_words() words; sets *overflow if a
 // pooled count does not fit 32 bits
@@ -68,7 +71,7 @@ struct EncBlob {
   BlobLayout lay;
   const uint16_t* img;       // cum images of quality q
   const float* inv_step;     // of quality q
-  // per launch, for the launch's rows [row0, row0 + nrows) of the 2L (kv, layer) rows:
+  // per launch, for the launch's rows [row0, row0 + nrows) of the blob's payload rows:
   uint32_t* scratch;         // per 64-stream block: [swb rows][64 lanes] words, row 0 placeholders
   uint32_t* lens;            // [nrows][C] words
   uint32_t* row_words;       // [nrows]
@@ -86,11 +89,15 @@ struct EncodeArgs {
   int L, T, C, G, nblk, nblobs;
   int n_groups, waves;  // workgroups per (kv, layer, block) and their widest group
   int prio;             // 1: the launch's waves are all resident at once; level their progress
-  // the (kv, layer) rows this launch codes and packs, row = kv * L + l: a blob
-  // is coded by launches over consecutive row ranges, in order; the one that
-  // ends at 2L also writes the header and the padding
-  int row0, nrows;
-  size_t swb;
+  // the payload rows this launch codes and packs: rows 0 .. 2L-1 are the delta
+  // streams of (kv, layer) = (r / L, r % L) (k_encode), rows 2L .. 4L-1 the
+  // anchor streams of coded-anchor blobs (k_anchor_encode).  A blob is coded by
+  // launches over consecutive row ranges that do not straddle 2L, in order; the
+  // one that ends at rows_total (2L, or 4L with coded anchors) also writes the
+  // header and the padding
+  int row0, nrows, rows_total;
+  size_t swb;                // scratch rows per stream of this launch's rows
+  const uint16_t* afreq;     // [2][L][256] anchor tables (coded anchors), else null
   const float* scale_a;
   const float* inv_a;
   uint64_t tables_id;

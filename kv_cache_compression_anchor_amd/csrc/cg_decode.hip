@@ -206,6 +206,7 @@ struct Words {
 // Per-lane state both kernels set up the same way.
 struct Lane {
   __amdgpu_buffer_rsrc_t rs, ro;
+  __amdgpu_buffer_rsrc_t ra;  // the chunk's anchors
   Words wd;            // the lane's stream words in the blob
   uint32_t bad;        // stream extends past the payload
   float scale_a, step;
@@ -351,7 +352,8 @@ __device__ __forceinline__ bool setup(const DecodeArgs& a, int wave, int lane, L
   }
   s.row_bytes = 2u * (uint32_t)a.C;
   s.lane_off = 2u * (uint32_t)c;
-  s.anc_base = s.ch.off_anchor + (uint32_t)row * (uint32_t)s.ch.ng * (uint32_t)a.C + c;
+  s.ra = __builtin_amdgcn_make_buffer_rsrc((void*)s.ch.anc, 0, (int)s.ch.anc_bytes, kBufRsrcWord3);
+  s.anc_base = (uint32_t)row * (uint32_t)s.ch.ng * (uint32_t)a.C + c;
   s.C = a.C;
   return true;
 }
@@ -464,7 +466,7 @@ __global__ __launch_bounds__(512) void k_decode_win(DecodeArgs a) {
   win_put(ring, ring + kWinLow, false, b1);
   Block<RB> pend = {};  // block in flight
   bool inflight = false;
-  int anc_next = ld8s(s.rs, s.anc_base);
+  int anc_next = ld8s(s.ra, s.anc_base);
 
   // one symbol, its new bits x (the next stream bits, most significant first);
   // returns sh and the selector that shifted them in
@@ -543,7 +545,7 @@ __global__ __launch_bounds__(512) void k_decode_win(DecodeArgs a) {
       pg.fetch(a, s, lane, ta + (GS > 0 ? GS : a.G));
     }
     const int anc = anc_next;
-    anc_next = ld8s(s.rs, s.anc_base + (uint32_t)(g + 1) * s.C);  // past the last group: unused
+    anc_next = ld8s(s.ra, s.anc_base + (uint32_t)(g + 1) * s.C);  // past the last group: unused
     const float ahat = anchor_value(anc, s.scale_a);
     out((uint32_t)ta, float_to_half_bits(ahat));
     int t = ta + 1;
@@ -641,7 +643,7 @@ __global__ __launch_bounds__(512) void k_decode_reg(DecodeArgs a) {
   reg_put(ring, 0u, b1);
   Block<RB> pend = {};  // block in flight
   bool inflight = false;
-  int anc_next = ld8s(s.rs, s.anc_base);
+  int anc_next = ld8s(s.ra, s.anc_base);
 
   // one symbol: search, interval update, renormalisation, reconstruction
   auto symbol = [&](uint32_t t, float ahat) {
@@ -691,7 +693,7 @@ __global__ __launch_bounds__(512) void k_decode_reg(DecodeArgs a) {
       pg.fetch(a, s, lane, ta + (GS > 0 ? GS : a.G));
     }
     const int anc = anc_next;
-    anc_next = ld8s(s.rs, s.anc_base + (uint32_t)(g + 1) * s.C);  // past the last group: unused
+    anc_next = ld8s(s.ra, s.anc_base + (uint32_t)(g + 1) * s.C);  // past the last group: unused
     const float ahat = anchor_value(anc, s.scale_a);
     out((uint32_t)ta, float_to_half_bits(ahat));
     int t = ta + 1;
@@ -735,6 +737,111 @@ __global__ __launch_bounds__(512) void k_decode_reg(DecodeArgs a) {
   if (PG && pg.bad) atomicOr(a.status, 2u);
 }
 
+// ---------------------------------------------------------------------------
+// Anchor streams of coded-anchor blobs.  One lane per stream (kv, layer,
+// channel) of a chunk, one wave per (64-channel block, (kv, layer), chunk); the
+// wave stages the (kv, layer) anchor table's cumulative counts in LDS.  A lane
+// reads its stream through the payload layout (as the delta decoders do),
+// decodes its n_groups symbols (the largest s with r cum[s] <= code, by an
+// eight-level bisection of the 257 cumulative counts; bytes shifted in while
+// range < 2^24) and writes anchor s - 128 of every group to the chunk's
+// anchor array, 64 bytes per wave and group.
+__global__ __launch_bounds__(64) void k_anchor_decode(AnchorDecodeArgs a) {
+  __shared__ uint32_t cum[kASym + 1];
+  const int lane = threadIdx.x;
+  const int cb = blockIdx.x, arow = blockIdx.y;  // arow = kv * L + l
+  const AncChunk ch = a.chunks[blockIdx.z];
+  {
+    const uint16_t* f = a.afreq + (size_t)arow * kASym + 4 * lane;
+    const uint32_t f0 = f[0], f1 = f[1], f2 = f[2], f3 = f[3];
+    uint32_t incl = f0 + f1 + f2 + f3;
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    const uint32_t base = incl - (f0 + f1 + f2 + f3);
+    cum[4 * lane] = base;
+    cum[4 * lane + 1] = base + f0;
+    cum[4 * lane + 2] = base + f0 + f1;
+    cum[4 * lane + 3] = base + f0 + f1 + f2;
+    if (lane == 63) cum[kASym] = incl;
+  }
+  __syncthreads();
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)ch.blob, 0, (int)ch.blob_bytes, kBufRsrcWord3);
+  const int prow = 2 * a.L + arow;  // the payload row of these streams
+  const int c = cb * kLanes + lane;
+  const bool active = c < a.C;
+  // the stream's words in the payload layout, as in the delta decoders' setup
+  const uint32_t len_base = ch.off_len + 2u * (uint32_t)prow * (uint32_t)a.C;
+  uint32_t before = 0;
+  for (int j = lane; j < cb * kLanes; j += kLanes) before += ld16(rs, len_base + 2u * j);
+  const uint32_t my_len = active ? ld16(rs, len_base + 2u * c) : 0u;
+  uint32_t total = my_len, mu = active ? my_len >> 2 : 0xFFFFFFFFu;
+  for (int o = 32; o; o >>= 1) {
+    before += __shfl_xor(before, o);
+    total += __shfl_xor(total, o);
+    mu = min(mu, __shfl_xor(mu, o));
+  }
+  const uint32_t m = __builtin_amdgcn_readfirstlane(mu);
+  const uint32_t ns = (uint32_t)min(kLanes, a.C - cb * kLanes);
+  const uint32_t tl = active ? my_len - 4u * m : 0u;
+  uint32_t incl = tl;
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (!active) return;
+  const uint32_t blk = ld32(rs, 64u + 4u * (uint32_t)prow) + before;
+  uint32_t bad = ((uint64_t)blk + total > ch.W) ? 1u : 0u;
+  const uint32_t blk_byte = ch.off_pay + 4u * blk;
+  Words wd;
+  wd.m = m;
+  wd.us = 16u * ns;
+  wd.a0 = blk_byte + 16u * (uint32_t)lane;
+  wd.t0 = blk_byte + 4u * (4u * m * ns + incl - tl) - 16u * m;
+
+  // stream bytes (a word holds four, the first in its top byte): the next
+  // ones in the top `avail` bits of bb, the word after them prefetched in pf
+  uint64_t bb = ((uint64_t)ld32(rs, wd.word(0)) << 32) | ld32(rs, wd.word(1));
+  uint32_t avail = 64, nextw = 2;
+  uint32_t pf = ld32(rs, wd.word(nextw));
+  auto take_byte = [&]() -> uint32_t {
+    const uint32_t b = (uint32_t)(bb >> 56);
+    bb <<= 8;
+    avail -= 8;
+    if (avail <= 32) {
+      bb |= (uint64_t)pf << (32 - avail);
+      avail += 32;
+      pf = ld32(rs, wd.word(++nextw));
+    }
+    return b;
+  };
+  uint32_t code = 0;
+  for (int i = 0; i < 4; i++) code = (code << 8) | take_byte();
+  uint32_t range = 0xFFFFFFFFu;
+  int8_t* out = ch.out + (size_t)arow * ch.ng * a.C + c;
+  for (int g = 0; g < ch.ng; g++) {
+    const uint32_t r = range >> kProbBits;
+    if ((uint64_t)r * kProbTotal <= code) bad = 1u;  // code outside every symbol
+    uint32_t sym = 0;
+#pragma unroll
+    for (uint32_t stp = 128; stp; stp >>= 1)
+      if (r * cum[sym + stp] <= code) sym += stp;
+    const uint32_t c0 = cum[sym];
+    code -= r * c0;
+    range = r * (cum[sym + 1] - c0);
+    while (range < kTop) {
+      code = (code << 8) | take_byte();
+      range <<= 8;
+    }
+    out[(size_t)g * a.C] = (int8_t)((int)sym - 128);
+  }
+  // a valid stream keeps code < range throughout
+  bad |= code >= range ? 1u : 0u;
+  if (bad) atomicOr(a.status, 1u);
+}
+
 }  // namespace
 
 namespace {
@@ -757,6 +864,12 @@ void launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   }
 }
 }  // namespace
+
+hipError_t launch_anchor_decode(const AnchorDecodeArgs& a, hipStream_t st) {
+  if (a.nchunks > 0)
+    k_anchor_decode<<<dim3((unsigned)a.nblk, (unsigned)(2 * a.L), (unsigned)a.nchunks), 64, 0, st>>>(a);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   if (a.paged)

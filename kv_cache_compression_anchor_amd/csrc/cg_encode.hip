@@ -211,6 +211,9 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
                                            (int)(kRowBytes * (uint32_t)a.swb), kBufRsrcWord3);
   o.woff = 4u * (uint32_t)lane;
   const uint32_t woff0 = o.woff + kRowBytes;  // the stream's first word
+  // raw anchors into the blob; coded anchors are coded from the input by
+  // k_anchor_encode instead (a wave-uniform choice)
+  const bool raw_anchors = B.lay.off_anchor != 0;
   int8_t* anchors = reinterpret_cast<int8_t*>(B.blob + B.lay.off_anchor) +
                     ((size_t)kv * a.L + l) * B.ng * a.C + c;
   RcEnc e = {0, 0u, 0u, 0xFFFFFFFFu, 0u, 0u};
@@ -221,7 +224,7 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
     const uint32_t ha = half_of(0);
     nonfinite |= (ha & 0x7C00u) == 0x7C00u;
     const int av = quant_anchor(half_bits_to_float(ha), inv_a);
-    anchors[(size_t)g * a.C] = (int8_t)av;
+    if (raw_anchors) anchors[(size_t)g * a.C] = (int8_t)av;
     const float ahat = anchor_value(av, scale_a);
     for (int j = 1; j < n; j++) {
       const uint32_t hx = half_of(j);
@@ -281,7 +284,80 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
   reinterpret_cast<uint16_t*>(B.blob + B.lay.off_len)[pi] = (uint16_t)nwords;
 }
 
-// words of every 64-stream block and of every (kv, layer) row of the launch's
+// Anchor streams of coded-anchor blobs (payload rows 2L .. 4L-1): one lane
+// per (kv, layer, channel), a workgroup per (group of up to 4 blobs, row,
+// 64-channel block) with one wave per blob, as in k_encode.  The anchor of
+// group g is chunk token g G, quantised as in the delta encoder's closed loop;
+// its symbol a + 128 is range-coded with the (kv, layer) anchor table (CacheGen
+// blog, section 2.1: the quantised anchor, then arithmetic coding), into the
+// same per-block scratch layout as the delta streams, so the same kernels pack
+// them.  Non-finite input is flagged by k_encode, which reads every token.
+__global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_anchor_encode(EncodeArgs a) {
+  __shared__ uint32_t cum[kASym + 1];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int per_grp = a.nrows * a.nblk;
+  const int grp = blockIdx.x / per_grp, unit = blockIdx.x % per_grp;
+  const int rrel = unit / a.nblk;
+  const int arow = a.row0 + rrel - 2 * a.L;  // kv * L + l
+  const int cb = unit % a.nblk;
+  if (wave == 0) {
+    // cumulative table: lane k sums entries 4k .. 4k + 3, then a wave scan
+    const uint16_t* f = a.afreq + (size_t)arow * kASym + 4 * lane;
+    const uint32_t f0 = f[0], f1 = f[1], f2 = f[2], f3 = f[3];
+    uint32_t incl = f0 + f1 + f2 + f3;
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    const uint32_t base = incl - (f0 + f1 + f2 + f3);
+    cum[4 * lane] = base;
+    cum[4 * lane + 1] = base + f0;
+    cum[4 * lane + 2] = base + f0 + f1;
+    cum[4 * lane + 3] = base + f0 + f1 + f2;
+    if (lane == 63) cum[kASym] = incl;
+  }
+  __syncthreads();
+  const EncGroup eg = a.groups[grp];
+  const int bi = __builtin_amdgcn_readfirstlane(eg.blob[wave]);
+  if (bi < 0) return;
+  const EncBlob& B = a.b[bi];
+  const int kv = arow / a.L, l = arow % a.L;
+  const int c = cb * kLanes + lane;
+  if (c >= a.C) return;
+  const float inv_a = a.inv_a[(size_t)arow * a.C + c];
+  // the chunk's rows of this (kv, layer), as in k_encode: no load may name a
+  // row at or past tc (g G < tc for every group g)
+  const uint32_t row_bytes = 2u * (uint32_t)a.C;
+  const __amdgpu_buffer_rsrc_t xin = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((kv ? a.v : a.k) + ((size_t)l * a.T + B.t0) * a.C), 0,
+      (int)((uint32_t)B.tc * row_bytes), kBufRsrcWord3);
+  const uint32_t lane_off = 2u * (uint32_t)c;
+  Sink o;
+  const size_t block = (size_t)rrel * a.nblk + cb;
+  o.rs = __builtin_amdgcn_make_buffer_rsrc(B.scratch + block * kLanes * a.swb, 0,
+                                           (int)(kRowBytes * (uint32_t)a.swb), kBufRsrcWord3);
+  o.woff = 4u * (uint32_t)lane;
+  const uint32_t woff0 = o.woff + kRowBytes;
+  RcEnc e = {0, 0u, 0u, 0xFFFFFFFFu, 0u, 0u};
+  const uint32_t gstep = (uint32_t)a.G * row_bytes;
+  uint32_t hx = ld_half(xin, lane_off, 0u);
+  for (int g = 0; g < B.ng; g++) {
+    // the next group's anchor token is loaded a group ahead (past the last
+    // group: the last one again, inside the chunk)
+    const uint32_t h = hx;
+    hx = ld_half(xin, lane_off, (uint32_t)min(g + 1, B.ng - 1) * gstep);
+    const uint32_t s = (uint32_t)(quant_anchor(half_bits_to_float(h), inv_a) + 128);
+    const uint32_t c0 = cum[s];
+    rc_put(e, c0, cum[s + 1] - c0, o);
+  }
+  rc_finish(e, o);  // every chunk has at least one group
+  const uint32_t nwords = (o.woff - woff0) / kRowBytes;
+  B.lens[(size_t)rrel * a.C + c] = nwords;
+  reinterpret_cast<uint16_t*>(B.blob + B.lay.off_len)[(size_t)(a.row0 + rrel) * a.C + c] =
+      (uint16_t)nwords;
+}
+
+// words of every 64-stream block and of every payload row of the launch's
 // range, for every blob
 __global__ __launch_bounds__(256) void k_row_totals(EncodeArgs a) {
   __shared__ uint32_t part[4];
@@ -318,10 +394,10 @@ __global__ void k_row_scan(EncodeArgs a) {
   const size_t total = blob_bytes(B.lay, w);
   B.status[0] = (uint32_t)w;
   if (total > B.cap || w > 0x3FFFFFFFull) B.status[1] = 1u;
-  if (a.row0 + a.nrows != 2 * a.L) return;
+  if (a.row0 + a.nrows != a.rows_total) return;
   uint32_t* h = reinterpret_cast<uint32_t*>(B.blob);
   h[0] = kBlobMagic;
-  h[1] = kBlobVersion;
+  h[1] = B.lay.off_anchor ? kBlobVersion : kBlobVersionCoded;
   h[2] = (uint32_t)a.L;
   h[3] = (uint32_t)a.C;
   h[4] = (uint32_t)a.T;
@@ -343,7 +419,7 @@ __global__ __launch_bounds__(256) void k_pad(EncodeArgs a) {
   const EncBlob& B = a.b[blockIdx.x];
   if (B.status[1]) return;
   const size_t W = B.status[0];
-  const size_t gap0 = B.lay.off_len + 4 * (size_t)a.L * a.C, gap1 = B.lay.off_pay;
+  const size_t gap0 = B.lay.off_len + 2 * (size_t)B.lay.rows * a.C, gap1 = B.lay.off_pay;
   const size_t tail0 = B.lay.off_pay + 4 * W, tail1 = blob_bytes(B.lay, W);
   for (size_t j = gap0 + threadIdx.x; j < gap1; j += 256) B.blob[j] = 0;
   for (size_t j = tail0 + threadIdx.x; j < tail1; j += 256) B.blob[j] = 0;
@@ -416,13 +492,15 @@ __global__ __launch_bounds__(256) void k_pack(EncodeArgs a) {
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t st) {
   const unsigned nb = (unsigned)a.nblobs;
   const unsigned blocks = (unsigned)(a.n_groups * a.nrows * a.nblk);
-  if (a.G == 10)
+  if (a.row0 >= 2 * a.L)
+    k_anchor_encode<<<blocks, kLanes * a.waves, 0, st>>>(a);
+  else if (a.G == 10)
     k_encode<10><<<blocks, kLanes * a.waves, 0, st>>>(a);
   else
     k_encode<0><<<blocks, kLanes * a.waves, 0, st>>>(a);
   k_row_totals<<<dim3(a.nrows, nb), 256, 0, st>>>(a);
   k_row_scan<<<nb, 64, 0, st>>>(a);
-  if (a.row0 + a.nrows == 2 * a.L) k_pad<<<nb, 256, 0, st>>>(a);
+  if (a.row0 + a.nrows == a.rows_total) k_pad<<<nb, 256, 0, st>>>(a);
   k_pack<<<dim3(a.nrows * a.nblk, nb), 256, 0, st>>>(a);
   return hipGetLastError();
 }

@@ -24,7 +24,11 @@ constexpr int kTabHdr = 80;
 constexpr int kBlobHdr = 64;
 constexpr uint32_t kTabMagic = 0x31544743u;   // "CGT1"
 constexpr uint32_t kBlobMagic = 0x314B4743u;  // "CGK1"
-constexpr uint32_t kBlobVersion = 2;           // payload blocks interleaved unit by unit
+constexpr uint32_t kTabVersion = 1;            // tables without anchor tables
+constexpr uint32_t kTabVersionCoded = 2;       // tables with one anchor table per (kv, layer)
+constexpr uint32_t kBlobVersion = 2;           // raw anchors; payload blocks interleaved by unit
+constexpr uint32_t kBlobVersionCoded = 3;      // the same with range-coded anchors
+constexpr int kASym = 256;                     // anchor symbols: value a is a + 128
 constexpr uint32_t kUnitWords = 4;             // a 16-byte unit of a stream
 constexpr int kMaxTokens = 1 << 21;
 constexpr int kMaxChunk = 65536;
@@ -34,17 +38,19 @@ constexpr int kImgRows = kNSym + 1;    // cumulative table cum[0..64]
 constexpr int kLanes = 64;             // one wave64 = 64 channels
 
 // Serialized tables: header, scale_a, inv_a, then per quality in the mask:
-// step, inv_step, freq[64] — all per (kv, layer, channel).
+// step, inv_step, freq[64] — all per (kv, layer, channel); with coded anchors
+// (version 2) then u16 afreq[2][L][256], the anchor table of each (kv, layer).
 struct TabLayout {
   size_t n = 0;  // 2 * L * C
   size_t off_scale_a = 0, off_inv_a = 0;
   size_t off_step[3] = {0, 0, 0}, off_inv_step[3] = {0, 0, 0}, off_freq[3] = {0, 0, 0};
+  size_t off_afreq = 0;  // 0: no anchor tables (raw anchors)
   size_t total = 0;
   int nq = 0;
   int qslot[3] = {-1, -1, -1};  // index of quality q among the built ones
 };
 
-inline TabLayout tab_layout(int L, int C, uint32_t mask) {
+inline TabLayout tab_layout(int L, int C, uint32_t mask, bool coded) {
   TabLayout t;
   t.n = (size_t)2 * L * C;
   size_t off = kTabHdr;
@@ -62,24 +68,35 @@ inline TabLayout tab_layout(int L, int C, uint32_t mask) {
     t.off_freq[q] = off;
     off += 2 * kNSym * t.n;
   }
+  if (coded) {
+    t.off_afreq = off;
+    off += (size_t)2 * L * kASym * 2;
+  }
   t.total = off;
   return t;
 }
 
 constexpr size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
-// Chunk blob: header, u32 row_offset[2][L], i8 anchors[2][L][ng][C],
-// u16 lengths[2][L][C] (words), pad to 16, u32 payload[W], >= 16 zero bytes.
+// Chunk blob, raw anchors (version 2): header, u32 row_offset[2L], i8
+// anchors[2][L][ng][C], u16 lengths[2L][C] (words), pad to 16, u32 payload[W],
+// >= 16 zero bytes.  Coded anchors (version 3): header, u32 row_offset[4L],
+// u16 lengths[4L][C], pad to 16, payload, >= 16 zero bytes; payload rows
+// 0 .. 2L-1 are the delta streams of (kv, layer) = (r / L, r % L), rows
+// 2L .. 4L-1 the anchor streams of (kv, layer) = ((r - 2L) / L, (r - 2L) % L).
 struct BlobLayout {
-  size_t off_rows, off_anchor, off_len, off_pay;
+  int rows;  // payload rows: 2L, or 4L with coded anchors
+  size_t off_rows, off_anchor, off_len, off_pay;  // off_anchor 0: coded anchors
 };
 
-inline BlobLayout blob_layout(int L, int C, int ng) {
+inline BlobLayout blob_layout(int L, int C, int ng, bool coded) {
   BlobLayout b;
+  b.rows = coded ? 4 * L : 2 * L;
   b.off_rows = kBlobHdr;
-  b.off_anchor = b.off_rows + 8 * (size_t)L;
-  b.off_len = b.off_anchor + 2 * (size_t)L * ng * C;
-  b.off_pay = align16(b.off_len + 4 * (size_t)L * C);
+  const size_t after_rows = b.off_rows + 4 * (size_t)b.rows;
+  b.off_anchor = coded ? 0 : after_rows;
+  b.off_len = coded ? after_rows : after_rows + 2 * (size_t)L * ng * C;
+  b.off_pay = align16(b.off_len + 2 * (size_t)b.rows * C);
   return b;
 }
 

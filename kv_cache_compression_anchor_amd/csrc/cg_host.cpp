@@ -66,12 +66,17 @@ int check_params(const cg_params* p) {
   if (prev != p->layers) return fail(CG_E_INVAL, "last layer_group_end must equal layers");
   if ((p->quality_mask & ~7u) || !p->quality_mask)
     return fail(CG_E_INVAL, "quality_mask must be a non-empty subset of {H,M,L}");
+  if (p->anchor_coding != 0 && p->anchor_coding != 1)
+    return fail(CG_E_INVAL, "anchor_coding must be 0 or 1");
+  // an anchor table counts the channels x groups of a layer in 32 bits
+  if (p->anchor_coding && (uint64_t)p->channels * (uint64_t)p->tokens >= (1ull << 32))
+    return fail(CG_E_INVAL, "coded anchors need channels x tokens below 2^32");
   for (int q = 0; q < 3; q++)
     if ((p->quality_mask >> q) & 1)
       if (!(p->quality_mult[q] > 0.0f) || !isfinite(p->quality_mult[q]))
         return fail(CG_E_INVAL, "quality_mult must be positive and finite");
   const size_t n = (size_t)2 * p->layers * p->channels;
-  const TabLayout lay = tab_layout(p->layers, p->channels, p->quality_mask);
+  const TabLayout lay = tab_layout(p->layers, p->channels, p->quality_mask, p->anchor_coding != 0);
   if (lay.total > 0x7FFFFFFFull || n > 0x7FFFFFFFull)
     return fail(CG_E_INVAL, "tables larger than 2 GiB");
   return CG_OK;
@@ -82,7 +87,8 @@ int parse_info(const uint8_t* b, size_t len, cg_chunk_info* o) {
   if (len < (size_t)kBlobHdr) return fail(CG_E_INVAL, "blob shorter than its header");
   uint32_t u[16];
   memcpy(u, b, 64);
-  if (u[0] != kBlobMagic || u[1] != kBlobVersion) return fail(CG_E_INVAL, "not a CGK1 v2 blob");
+  if (u[0] != kBlobMagic || (u[1] != kBlobVersion && u[1] != kBlobVersionCoded))
+    return fail(CG_E_INVAL, "not a CGK1 version 2 or 3 blob");
   if (u[11] != (uint32_t)kProbBits) return fail(CG_E_INVAL, "unsupported probability precision");
   o->layers = (int32_t)u[2];
   o->channels = (int32_t)u[3];
@@ -93,7 +99,7 @@ int parse_info(const uint8_t* b, size_t len, cg_chunk_info* o) {
   o->n_groups = (int32_t)u[8];
   o->quality = (int32_t)u[9];
   o->payload_words = u[10];
-  o->reserved = 0;
+  o->version = u[1];
   memcpy(&o->tables_id, &u[12], 8);
   if (o->layers < 1 || o->layers > 4096 || o->channels < 1 || o->channels > 65536 ||
       o->total_tokens < 1 || o->total_tokens > kMaxTokens || o->chunk_tokens < 1 ||
@@ -106,7 +112,7 @@ int parse_info(const uint8_t* b, size_t len, cg_chunk_info* o) {
   if ((uint64_t)o->chunk_tokens * (uint64_t)o->channels * 2u >= (1ull << 32))
     return fail(CG_E_INVAL, "a chunk of one layer (chunk_tokens x channels x 2 bytes) must be "
                             "smaller than 4 GiB");
-  const BlobLayout bl = blob_layout(o->layers, o->channels, o->n_groups);
+  const BlobLayout bl = blob_layout(o->layers, o->channels, o->n_groups, o->version == kBlobVersionCoded);
   o->blob_bytes = blob_bytes(bl, o->payload_words);
   if (o->blob_bytes > 0xFFFFFFFFull) return fail(CG_E_INVAL, "blob larger than 4 GiB");
   return CG_OK;
@@ -117,8 +123,9 @@ int check_tables_image(const uint8_t* b, size_t len, cg_params* out) {
   if (len < (size_t)kTabHdr) return fail(CG_E_INVAL, "tables shorter than their header");
   uint32_t u[20];
   memcpy(u, b, kTabHdr);
-  if (u[0] != kTabMagic || u[1] != 1 || u[18] != (uint32_t)kProbBits || u[19] != (uint32_t)kNSym)
-    return fail(CG_E_INVAL, "not CGT1 v1 tables");
+  if (u[0] != kTabMagic || (u[1] != kTabVersion && u[1] != kTabVersionCoded) ||
+      u[18] != (uint32_t)kProbBits || u[19] != (uint32_t)kNSym)
+    return fail(CG_E_INVAL, "not CGT1 version 1 or 2 tables");
   cg_params p;
   memset(&p, 0, sizeof(p));
   p.layers = (int32_t)u[2];
@@ -133,9 +140,10 @@ int check_tables_image(const uint8_t* b, size_t len, cg_params* out) {
     memcpy(&p.quality_mult[i], &u[14 + i], 4);
   }
   p.quality_mask = u[17];
+  p.anchor_coding = u[1] == kTabVersionCoded ? 1 : 0;
   const int rc = check_params(&p);
   if (rc) return rc;
-  const TabLayout lay = tab_layout(p.layers, p.channels, p.quality_mask);
+  const TabLayout lay = tab_layout(p.layers, p.channels, p.quality_mask, p.anchor_coding != 0);
   if (len != lay.total) return fail(CG_E_INVAL, "tables size does not match their header");
   // every value the kernels rely on: positive normal steps, finite inverses,
   // frequency tables of 64 positive entries summing to 2^15
@@ -161,6 +169,18 @@ int check_tables_image(const uint8_t* b, size_t len, cg_params* out) {
         sum += f[k];
       }
       if (sum != kProbTotal) return fail(CG_E_INVAL, "frequencies do not sum to 2^15");
+    }
+  }
+  if (lay.off_afreq) {
+    for (size_t i = 0; i < (size_t)2 * p.layers; i++) {
+      uint16_t f[kASym];
+      memcpy(f, b + lay.off_afreq + 2 * kASym * i, sizeof(f));
+      uint32_t sum = 0;
+      for (int k = 0; k < kASym; k++) {
+        if (!f[k]) return fail(CG_E_INVAL, "zero anchor frequency");
+        sum += f[k];
+      }
+      if (sum != kProbTotal) return fail(CG_E_INVAL, "anchor frequencies do not sum to 2^15");
     }
   }
   *out = p;

@@ -59,7 +59,11 @@ struct DecChunk {
   const uint8_t* blob;
   uint32_t blob_bytes;
   int32_t t0, tc, ng, q;
-  uint32_t off_anchor, off_len, off_pay, W;
+  uint32_t off_len, off_pay, W;
+  // the chunk's anchors, i8 [2][L][ng][C]: the blob's raw anchor section, or
+  // with coded anchors where k_anchor_decode wrote them
+  const int8_t* anc;
+  uint32_t anc_bytes;
 };
 struct DecGroup {  // chunks of one quality decoded by one workgroup (one wave each)
   int8_t chunk[4];
@@ -87,5 +91,22 @@ struct DecodeArgs {
   uint32_t n_blocks, num_pages, page_shift;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+
+// Anchor streams of coded-anchor blobs (payload rows 2L .. 4L-1) back to i8
+// anchors [2][L][ng][C] at each chunk's `out`.
+struct AncChunk {
+  const uint8_t* blob;
+  uint32_t blob_bytes;
+  int32_t ng;
+  uint32_t off_len, off_pay, W;
+  int8_t* out;
+};
+struct AnchorDecodeArgs {
+  int L, C, nblk, nchunks;
+  AncChunk chunks[kDecMaxChunks];
+  const uint16_t* afreq;  // [2][L][256]
+  uint32_t* status;       // bit 0: a corrupt stream
+};
+hipError_t launch_anchor_decode(const AnchorDecodeArgs& a, hipStream_t st);
 
 }  // namespace cg

@@ -168,20 +168,25 @@ struct HistArgs {
   const float* inv_a;
   const float* inv_step[3];  // by slot
   uint32_t* counts;          // [2][nq][L][C][64]
+  uint32_t* acounts;         // [2][L][256] anchor-symbol counts, or null (raw anchors)
 };
 
 // Delta-symbol histogram of one (kv, layer, 64-channel block, chunk): each lane
 // owns a channel, the four waves take interleaved groups; counts go to LDS with
 // atomics, laid out [slot][symbol][lane] so that the 64 lanes hit distinct
 // banks and a count's address is one shift-add of the delta level; then to
-// global memory with one atomic per non-zero bin.  LDS: nq * 16 KB, dynamic.
+// global memory with one atomic per non-zero bin.  With coded anchors the
+// anchors' symbols a + 128 are counted too, into 256 more LDS words.  LDS:
+// nq * 16 KB (+ 1 KB), dynamic.
 template <int GS, int NQ>
 __global__ __launch_bounds__(256) void k_histogram(HistArgs a) {
   extern __shared__ uint32_t hist[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // token rows are scalar offsets
   const int words = NQ * kNSym * kLanes;
-  for (int j = tid; j < words; j += 256) hist[j] = 0;
+  const bool anchors = a.acounts != nullptr;
+  uint32_t* ahist = hist + words;
+  for (int j = tid; j < words + (anchors ? kASym : 0); j += 256) hist[j] = 0;
   __syncthreads();
   const int c = blockIdx.x * kLanes + lane;
   const int chunk = blockIdx.y, l = blockIdx.z;
@@ -213,7 +218,9 @@ __global__ __launch_bounds__(256) void k_histogram(HistArgs a) {
                                             ((uint32_t)level << 8)), 1u);
     };
     auto group = [&](int n, auto half_of) {
-      const float ahat = anchor_value(quant_anchor(half_bits_to_float(half_of(0)), inv_a), scale_a);
+      const int av = quant_anchor(half_bits_to_float(half_of(0)), inv_a);
+      if (anchors) atomicAdd(&ahist[av + 128], 1u);
+      const float ahat = anchor_value(av, scale_a);
       for (int j = 1; j < n; j++) {
         const float xv = half_bits_to_float(half_of(j));
         count(at0, quant_delta_level(xv, ahat, is0));
@@ -263,6 +270,53 @@ __global__ __launch_bounds__(256) void k_histogram(HistArgs a) {
     const size_t ti = (((size_t)a.kv * NQ + s) * a.L + l) * a.C + cc;
     atomicAdd(&a.counts[ti * kNSym + sym], v);
   }
+  if (anchors && tid < kASym && ahist[tid])
+    atomicAdd(&a.acounts[((size_t)a.kv * a.L + l) * kASym + tid], ahist[tid]);
+}
+
+// Anchor tables: the counts of a (kv, layer) -> 256 frequencies summing to
+// 2^15 by the same rule as the delta tables (one slot each, the rest in
+// proportion rounded down, the remainder to the most counted symbol, lowest
+// on ties).  One wave per table, lane k holds symbols k, k + 64, k + 128,
+// k + 192.
+__global__ __launch_bounds__(64) void k_normalize_anchors(const uint32_t* acounts, uint16_t* afreq) {
+  const int k = threadIdx.x;
+  const uint32_t* c = acounts + (size_t)blockIdx.x * kASym;
+  uint32_t ck[4];
+  uint64_t N = 0;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    ck[j] = c[k + 64 * j];
+    N += ck[j];
+  }
+  for (int o = 32; o; o >>= 1) N += __shfl_xor(N, o);
+  const double spare = (double)(kProbTotal - kASym);
+  const double den = N ? (double)N : (double)kASym;
+  uint32_t f[4], total = 0, bc = 0, bk = 0;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const uint32_t cj = N ? ck[j] : 1u;
+    // the floor of an exact quotient of integers below 2^47 and 2^32: the
+    // correctly rounded binary64 quotient never crosses an integer
+    f[j] = 1u + (uint32_t)floor((double)cj * spare / den);
+    total += f[j];
+    if (j == 0 || cj > bc) {  // this lane's most counted, lowest symbol on ties
+      bc = cj;
+      bk = (uint32_t)(k + 64 * j);
+    }
+  }
+  for (int o = 32; o; o >>= 1) total += __shfl_xor(total, o);
+  for (int o = 32; o; o >>= 1) {
+    const uint32_t oc = __shfl_xor(bc, o), ok = __shfl_xor(bk, o);
+    if (oc > bc || (oc == bc && ok < bk)) {
+      bc = oc;
+      bk = ok;
+    }
+  }
+  uint16_t* out = afreq + (size_t)blockIdx.x * kASym;
+#pragma unroll
+  for (int j = 0; j < 4; j++)
+    out[k + 64 * j] = (uint16_t)(f[j] + ((uint32_t)(k + 64 * j) == bk ? kProbTotal - total : 0u));
 }
 
 struct NormArgs {
@@ -488,7 +542,7 @@ hipError_t launch_finalize(const cg_params& p, const StatsBuf& sb, DevTables& t,
 }
 
 hipError_t launch_histogram(const uint16_t* x, int kv, const DevTables& t, uint32_t* counts,
-                            hipStream_t st) {
+                            uint32_t* acounts, hipStream_t st) {
   HistArgs a;
   a.x = x;
   a.kv = kv;
@@ -503,9 +557,10 @@ hipError_t launch_histogram(const uint16_t* x, int kv, const DevTables& t, uint3
   for (int q = 0, s = 0; q < 3; q++)
     if ((t.mask >> q) & 1u) a.inv_step[s++] = reinterpret_cast<const float*>(t.ser + t.lay.off_inv_step[q]);
   a.counts = counts;
+  a.acounts = t.lay.off_afreq ? acounts : nullptr;
   const int nchunks = (t.T + t.CH - 1) / t.CH;
   dim3 grid((unsigned)t.nblk, (unsigned)nchunks, (unsigned)t.L);
-  const size_t lds = (size_t)a.nq * kNSym * kLanes * 4;
+  const size_t lds = (size_t)a.nq * kNSym * kLanes * 4 + (a.acounts ? 4 * kASym : 0);
   const bool g10 = t.G == 10;
   if (a.nq == 1) {
     if (g10) k_histogram<10, 1><<<grid, 256, lds, st>>>(a);
@@ -517,6 +572,13 @@ hipError_t launch_histogram(const uint16_t* x, int kv, const DevTables& t, uint3
     if (g10) k_histogram<10, 3><<<grid, 256, lds, st>>>(a);
     else k_histogram<0, 3><<<grid, 256, lds, st>>>(a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_normalize_anchors(const DevTables& t, const uint32_t* acounts, hipStream_t st) {
+  if (!t.lay.off_afreq) return hipSuccess;
+  k_normalize_anchors<<<2 * t.L, 64, 0, st>>>(acounts,
+                                             reinterpret_cast<uint16_t*>(t.ser + t.lay.off_afreq));
   return hipGetLastError();
 }
 

@@ -16,15 +16,16 @@ def to_dev(a: np.ndarray):
     return t.from_numpy(np.ascontiguousarray(a)).to("cuda")
 
 
-def params_of(w):
+def params_of(w, anchor_coding=0):
     import kv_cache_compression_anchor_amd as cg
     return cg.make_params(w.layers, w.tokens, w.channels, w.chunk_tokens, w.group_tokens,
-                          w.layer_group_end, w.layer_step, w.quality_mult, w.quality_mask)
+                          w.layer_group_end, w.layer_step, w.quality_mult, w.quality_mask,
+                          anchor_coding)
 
 
-def gpu_tables(w, kd, vd):
+def gpu_tables(w, kd, vd, anchor_coding=0):
     import kv_cache_compression_anchor_amd as cg
-    return cg.cg_build_tables(params_of(w), kd, vd)
+    return cg.cg_build_tables(params_of(w, anchor_coding), kd, vd)
 
 
 def gpu_encode(tab, kd, vd, chunk, q):

@@ -51,7 +51,7 @@ struct Rng {
 // last group of the chunk shorter than the others
 constexpr int L = 2, T = 50, C = 70, CH = 24, G = 5;
 
-cgo_params oracle_params() {
+cgo_params oracle_params(int anchor_coding) {
   cgo_params p;
   memset(&p, 0, sizeof(p));
   p.layers = L;
@@ -68,11 +68,12 @@ cgo_params oracle_params() {
   p.quality_mult[1] = 2.0f;
   p.quality_mult[2] = 4.0f;
   p.quality_mask = 7;
+  p.anchor_coding = anchor_coding;
   return p;
 }
 
 cg_params lib_params() {
-  const cgo_params o = oracle_params();
+  const cgo_params o = oracle_params(0);
   cg_params p;
   memset(&p, 0, sizeof(p));
   p.layers = o.layers;
@@ -194,10 +195,11 @@ void plan_cases() {
   expect(cg_plan_chunk(&in, nullptr, ratio) == CG_E_INVAL, "plan: NULL output");
 }
 
-void table_cases(const std::vector<uint8_t>& tab, const uint8_t* blob, size_t blen) {
+void table_cases(const std::vector<uint8_t>& tab, const uint8_t* blob, size_t blen, bool coded) {
   cg_params p;
   expect(cg::check_tables_image(tab.data(), tab.size(), &p) == CG_OK, "valid table image");
-  expect(p.layers == L && p.channels == C && p.tokens == T, "table image params");
+  expect(p.layers == L && p.channels == C && p.tokens == T && p.anchor_coding == (int)coded,
+         "table image params");
   int32_t t0, tc, ng;
   expect(cgo_chunk_geometry(tab.data(), tab.size(), 2, &t0, &tc, &ng) == 0 && tc == T - 2 * CH,
          "oracle geometry of the short chunk");
@@ -222,7 +224,8 @@ void table_cases(const std::vector<uint8_t>& tab, const uint8_t* blob, size_t bl
     size_t off;
     uint32_t value;
   };
-  const Field fields[] = {{0, 0}, {4, 2}, {8, 0}, {12, 0xFFFFFFFFu}, {16, 0}, {20, 0},
+  // version 1 <-> 2 changes the expected size: rejected too
+  const Field fields[] = {{0, 0}, {4, coded ? 1u : 2u}, {4, 3}, {8, 0}, {12, 0xFFFFFFFFu}, {16, 0}, {20, 0},
                           {24, 1000}, {28, 0}, {28, 5}, {32, 0}, {36, 0}, {44, 0x7FC00000u},
                           {48, 0xFF800000u}, {68, 0}, {68, 8}, {72, 14}, {76, 63}};
   for (const Field& f : fields) {
@@ -236,7 +239,7 @@ void table_cases(const std::vector<uint8_t>& tab, const uint8_t* blob, size_t bl
   }
 
   // body values the kernels rely on: scales, steps, frequency tables
-  const cg::TabLayout lay = cg::tab_layout(L, C, 7);
+  const cg::TabLayout lay = cg::tab_layout(L, C, 7, coded);
   struct Body {
     size_t off;
     uint32_t value;
@@ -263,6 +266,15 @@ void table_cases(const std::vector<uint8_t>& tab, const uint8_t* blob, size_t bl
     memcpy(t.data() + f + 2 * 5, &big, 2);
     expect(cg::check_tables_image(t.data(), t.size(), &p) != CG_OK, "frequencies off 2^15");
   }
+  if (coded) {
+    std::vector<uint8_t> t(tab);
+    const size_t f = lay.off_afreq + 2 * cg::kASym * 3;
+    const uint16_t z = 0, big = 40000;
+    memcpy(t.data() + f + 2 * 200, &z, 2);
+    expect(cg::check_tables_image(t.data(), t.size(), &p) != CG_OK, "zero anchor frequency rejected");
+    memcpy(t.data() + f + 2 * 200, &big, 2);
+    expect(cg::check_tables_image(t.data(), t.size(), &p) != CG_OK, "anchor frequencies off 2^15");
+  }
 
   // random bit flips anywhere: either check gives an answer, neither faults
   Rng r{12345};
@@ -280,11 +292,14 @@ void table_cases(const std::vector<uint8_t>& tab, const uint8_t* blob, size_t bl
 // a frequency table that no longer sums to 2^15 reaches the oracle's decoder
 // only through tables whose id the blob names: the blob's tables id is
 // patched to the damaged tables' id (the blob is coded at quality M)
-void unbalanced_frequency_case(const std::vector<uint8_t>& tab, const std::vector<uint8_t>& blob) {
+void unbalanced_frequency_case(const std::vector<uint8_t>& tab, const std::vector<uint8_t>& blob,
+                               bool coded) {
   std::vector<uint8_t> t(tab);
-  const cg::TabLayout lay = cg::tab_layout(L, C, 7);
+  const cg::TabLayout lay = cg::tab_layout(L, C, 7, coded);
   const uint16_t z = 0;
-  memcpy(t.data() + lay.off_freq[1] + 2 * cg::kNSym * 3 + 2 * 10, &z, 2);
+  memcpy(t.data() + (coded ? lay.off_afreq + 2 * cg::kASym * 2 + 2 * 130
+                           : lay.off_freq[1] + 2 * cg::kNSym * 3 + 2 * 10),
+         &z, 2);
   std::vector<uint8_t> b(blob);
   const uint64_t id = cgo_tables_id(t.data(), t.size());
   memcpy(b.data() + 48, &id, 8);
@@ -293,17 +308,18 @@ void unbalanced_frequency_case(const std::vector<uint8_t>& tab, const std::vecto
   expect(rc != 0 || corrupt, "oracle flags a stream whose table does not sum to 2^15");
 }
 
-void blob_cases(const std::vector<uint8_t>& tab, const std::vector<uint8_t>& blob) {
+void blob_cases(const std::vector<uint8_t>& tab, const std::vector<uint8_t>& blob, bool coded) {
   cg_chunk_info info;
   expect(cg_chunk_info_parse(blob.data(), blob.size(), &info) == CG_OK, "valid blob header");
-  expect(info.blob_bytes == blob.size(), "blob size from its header");
+  expect(info.blob_bytes == blob.size() && info.version == (coded ? 3u : 2u),
+         "blob size and version from its header");
   int corrupt = 1;
   expect(oracle_decode(tab, blob.data(), blob.size(), &corrupt) == 0 && corrupt == 0,
          "oracle decodes the valid blob");
   expect(cg_chunk_info_parse(nullptr, 64, &info) == CG_E_INVAL, "NULL blob");
   expect(cg_chunk_info_parse(blob.data(), 64, nullptr) == CG_E_INVAL, "NULL info");
 
-  const cg::BlobLayout bl = cg::blob_layout(L, C, info.n_groups);
+  const cg::BlobLayout bl = cg::blob_layout(L, C, info.n_groups, coded);
   const size_t cuts[] = {0, 1, 63, 64, 65, bl.off_pay, blob.size() - 17, blob.size() - 1};
   for (size_t n : cuts) {
     std::vector<uint8_t> b(blob.begin(), blob.begin() + n);
@@ -316,7 +332,7 @@ void blob_cases(const std::vector<uint8_t>& tab, const std::vector<uint8_t>& blo
     size_t off;
     uint32_t value;
   };
-  const Field fields[] = {{0, 0x324B4743u}, {4, 1}, {4, 3}, {8, 0}, {8, 5000}, {12, 0},
+  const Field fields[] = {{0, 0x324B4743u}, {4, 1}, {4, 4}, {8, 0}, {8, 5000}, {12, 0},
                           {16, 0}, {20, 0xFFFFFFFFu}, {20, 60}, {24, 0}, {24, 100000},
                           {28, 0}, {32, 999}, {36, 3}, {40, 0x40000000u}, {44, 14}};
   for (const Field& f : fields) {
@@ -340,6 +356,15 @@ void blob_cases(const std::vector<uint8_t>& tab, const std::vector<uint8_t>& blo
     b[48] ^= 1;
     expect(oracle_decode(tab, b.data(), b.size(), &corrupt) != 0, "oracle: other tables id");
   }
+  {
+    // the other format version: a valid header of another layout, refused by
+    // the tables
+    std::vector<uint8_t> b(blob);
+    put32(b, 4, coded ? 2u : 3u);
+    expect(cg_chunk_info_parse(b.data(), b.size(), &info) == CG_OK && info.blob_bytes != blob.size(),
+           "header of the other format version");
+    expect(oracle_decode(tab, b.data(), b.size(), &corrupt) != 0, "oracle: other format version");
+  }
 
   // lengths and row offsets that point past the payload
   {
@@ -357,7 +382,7 @@ void blob_cases(const std::vector<uint8_t>& tab, const std::vector<uint8_t>& blo
   }
   {
     std::vector<uint8_t> b(blob);
-    memset(b.data() + bl.off_len, 0, 4 * (size_t)L * C);
+    memset(b.data() + bl.off_len, 0, 2 * (size_t)bl.rows * C);
     expect(oracle_decode(tab, b.data(), b.size(), &corrupt) == 0 && corrupt,
            "oracle flags streams of zero length");
   }
@@ -387,21 +412,25 @@ int main() {
   plan_cases();
   std::vector<uint16_t> k, v;
   make_kv(k, v);
-  const cgo_params op = oracle_params();
-  std::vector<uint8_t> tab(cgo_tables_size(&op));
-  size_t tlen = 0;
-  expect(cgo_build_tables(&op, k.data(), v.data(), 1, tab.data(), tab.size(), &tlen, nullptr) == 0 &&
-             tlen == tab.size(),
-         "oracle builds the tables");
-  std::vector<uint8_t> blob(cgo_encode_bound(tab.data(), tab.size(), 0));
-  size_t blen = 0;
-  expect(cgo_encode_chunk(tab.data(), tab.size(), k.data(), v.data(), 0, 1, 1, blob.data(),
-                          blob.size(), &blen) == 0,
-         "oracle encodes chunk 0");
-  blob.resize(blen);
-  table_cases(tab, blob.data(), blob.size());
-  unbalanced_frequency_case(tab, blob);
-  blob_cases(tab, blob);
+  // raw anchors (tables version 1, blobs version 2), then coded anchors
+  // (tables version 2, blobs version 3)
+  for (int coded = 0; coded < 2; coded++) {
+    const cgo_params op = oracle_params(coded);
+    std::vector<uint8_t> tab(cgo_tables_size(&op));
+    size_t tlen = 0;
+    expect(cgo_build_tables(&op, k.data(), v.data(), 1, tab.data(), tab.size(), &tlen, nullptr) == 0 &&
+               tlen == tab.size(),
+           "oracle builds the tables");
+    std::vector<uint8_t> blob(cgo_encode_bound(tab.data(), tab.size(), 0));
+    size_t blen = 0;
+    expect(cgo_encode_chunk(tab.data(), tab.size(), k.data(), v.data(), 0, 1, 1, blob.data(),
+                            blob.size(), &blen) == 0,
+           "oracle encodes chunk 0");
+    blob.resize(blen);
+    table_cases(tab, blob.data(), blob.size(), coded);
+    unbalanced_frequency_case(tab, blob, coded);
+    blob_cases(tab, blob, coded);
+  }
   if (g_failures) {
     fprintf(stderr, "fault corpus: %d of %d cases failed\n", g_failures, g_cases);
     return 1;

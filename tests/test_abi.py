@@ -90,7 +90,7 @@ def test_chunk_info_parse_rejects_bad_headers(cg):
     k, v = synth.gen_kv(w)
     t = oracle.build_tables(oracle.params_for(w), k, v)
     b = bytearray(oracle.encode_chunk(t, k, v, 0, 0))
-    for off, val in ((0, 0x58), (4, 1), (4, 3), (44, 14), (32, 99), (36, 3), (8, 0)):
+    for off, val in ((0, 0x58), (4, 1), (4, 4), (44, 14), (32, 99), (36, 3), (8, 0)):
         bad = bytearray(b)
         bad[off] = val
         with pytest.raises(cg.CgError) as e:
@@ -98,6 +98,22 @@ def test_chunk_info_parse_rejects_bad_headers(cg):
         assert e.value.code == cg.CG_E_INVAL
     with pytest.raises(cg.CgError):
         cg.cg_chunk_info_parse(bytes(b[:63]))
+    # version 3 (coded anchors) is a valid header: its layout gives another size
+    info2, info3 = cg.cg_chunk_info_parse(bytes(b)), None
+    b3 = bytearray(b)
+    b3[4] = 3
+    info3 = cg.cg_chunk_info_parse(bytes(b3))
+    assert info2.version == 2 and info3.version == 3 and info3.blob_bytes != info2.blob_bytes
+
+
+def test_chunk_info_of_coded_anchor_blobs(cg):
+    w = synth.workload("tiny")
+    k, v = synth.gen_kv(w)
+    t = oracle.build_tables(oracle.params_for(w, anchor_coding=1), k, v)
+    b = oracle.encode_chunk(t, k, v, 0, 0)
+    info = cg.cg_chunk_info_parse(b)
+    assert info.version == 3 and info.blob_bytes == len(b)
+    assert info.tables_id == oracle.tables_id(t)
 
 
 def test_invalid_params_fail_before_any_gpu_work(cg):
