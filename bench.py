@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--decode-reps", type=int, default=1,
                     help="timed decode launches per step (the selection is decoded this many times)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-anchor-coded", action="store_true",
+                    help="skip the coded-anchor format's figures on the main workload")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the other workloads' figures (the 'workloads' key of the line)")
     ap.add_argument("--other-steps", type=int, default=3,
@@ -272,6 +274,9 @@ def main():
         "cpu_baseline_encode": cpu_enc,
         "input_generation_s": round(t_gen, 2),
     }
+    if not args.no_anchor_coded:
+        line["anchor_coded"] = anchor_coded_figures(w, kd, vd, args.other_steps, 1, sel_blob_bytes,
+                                                    dec_avg_ms, enc_ms, build_ms)
     if w.name == "mistral7b_9k" and not args.no_other_workloads:
         # the other workloads' figures, each in its own memory: the metric's
         # tensors are freed first
@@ -285,6 +290,50 @@ def main():
                                                      else args.other_cpu_seconds)
             torch.cuda.empty_cache()
     print(json.dumps(line), flush=True)
+
+
+def anchor_coded_figures(w, kd, vd, steps, warmup, raw_sel_bytes, raw_dec_ms, raw_enc_ms,
+                         raw_build_ms):
+    """The same step with coded anchors (tables version 2, blobs version 3):
+    the selection's bytes and compression ratio, and the decode (anchor streams
+    first, then the delta streams), encode and build times, beside the raw-anchor
+    figures of the main line."""
+    import torch
+
+    import kv_cache_compression_anchor_amd as cg
+    p = cg.make_params(w.layers, w.tokens, w.channels, w.chunk_tokens, w.group_tokens,
+                       w.layer_group_end, w.layer_step, w.quality_mult, w.quality_mask,
+                       anchor_coding=1)
+    step, bufs, ko, vo, status = make_stepper(w, p, kd, vd)
+    for _ in range(warmup):
+        step()
+    res = [step() for _ in range(steps)]
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise SystemExit("coded-anchor decode reported a corrupt stream")
+    sizes = res[-1]["sizes"]
+    sel = w.selection()
+    sel_bytes = sum(sizes[(c, q)] for c, q in enumerate(sel))
+    dec = [d for r in res for d in r["decode_ms"]]
+    dec_ms = sum(dec) / len(dec)
+    enc_ms = sum(r["encode_ms"] for r in res) / len(res)
+    build_ms = sum(r["build_ms"] for r in res) / len(res)
+    fp16 = 2 * w.elements
+    del bufs, ko, vo
+    return {
+        "format": "tables version 2, blobs version 3 (anchors range-coded per (kv, layer))",
+        "selection_blob_bytes": sel_bytes,
+        "bytes_vs_raw_anchors": round(sel_bytes / raw_sel_bytes, 4),
+        "compress_ratio_vs_8bit": round(w.elements / sel_bytes, 4),
+        "decode_ms": round(dec_ms, 4),
+        "decode_ms_raw_anchors": round(raw_dec_ms, 4),
+        "decode_frac": round((fp16 + sel_bytes) / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "encode_ms_all_chunks_all_qualities": round(enc_ms, 3),
+        "encode_ms_raw_anchors": round(raw_enc_ms, 3),
+        "build_tables_ms": round(build_ms, 3),
+        "build_tables_ms_raw_anchors": round(raw_build_ms, 3),
+        "steps": steps,
+    }
 
 
 def make_stepper(w, p, kd, vd, decode_reps=1):

@@ -224,6 +224,27 @@ struct Lane {
   uint32_t tok0;
 };
 
+// Words of the streams of a row's 64-channel blocks before block cb: the sum
+// of their u16 lengths at len_base, summed over the wave (every lane gets the
+// total).  Four loads in flight per lane; an index past them points past the
+// blob's end (no memory access).
+__device__ __forceinline__ uint32_t words_before(__amdgpu_buffer_rsrc_t rs, uint32_t len_base,
+                                                 int cb, int lane) {
+  const uint32_t n = (uint32_t)(cb * kLanes);
+  uint32_t before = 0;
+  for (uint32_t j = (uint32_t)lane; j < n; j += 4u * kLanes) {
+    uint32_t q[4];
+#pragma unroll
+    for (uint32_t i = 0; i < 4; i++) {
+      const uint32_t jj = j + i * kLanes;
+      q[i] = ld16(rs, jj < n ? len_base + 2u * jj : 0xFFFFFFF0u);
+    }
+    before += q[0] + q[1] + q[2] + q[3];
+  }
+  for (int o = 32; o; o >>= 1) before += __shfl_xor(before, o);
+  return before;
+}
+
 // The warming wave of a workgroup: reads one word of every 64 bytes of the
 // block's streams of each chunk and kv (a contiguous byte range of the blob;
 // its first 64 KB), 16 loads in flight at a time.  A lane fetches its stream
@@ -243,14 +264,10 @@ __device__ __forceinline__ void warm_block(const DecodeArgs& a, int grp, int l, 
     for (int kv = 0; kv < 2; kv++) {
       const int row = kv * a.L + l;
       const uint32_t len_base = ch.off_len + 2u * (uint32_t)row * (uint32_t)a.C;
-      uint32_t before = 0;
-      for (int j = lane; j < cb * kLanes; j += kLanes) before += ld16(rs, len_base + 2u * j);
+      const uint32_t before = words_before(rs, len_base, cb, lane);
       const int c = cb * kLanes + lane;
       uint32_t mine = c < a.C ? ld16(rs, len_base + 2u * c) : 0u;
-      for (int o = 32; o; o >>= 1) {
-        before += __shfl_xor(before, o);
-        mine += __shfl_xor(mine, o);
-      }
+      for (int o = 32; o; o >>= 1) mine += __shfl_xor(mine, o);
       const uint32_t start = ld32(rs, 64u + 4u * row) + before;  // words into the payload
       const uint32_t lo = (ch.off_pay + 4u * start) & ~63u;
       const uint32_t hi = ch.off_pay + 4u * (start + mine);
@@ -302,12 +319,10 @@ __device__ __forceinline__ bool setup(const DecodeArgs& a, int wave, int lane, L
   // earlier blocks), its units m and the lane's tail offset (the whole wave
   // takes part in the reductions and the scan)
   const uint32_t len_base = s.ch.off_len + 2u * (uint32_t)row * (uint32_t)a.C;
-  uint32_t before = 0;
-  for (int j = lane; j < cb * kLanes; j += kLanes) before += ld16(s.rs, len_base + 2u * j);
+  const uint32_t before = words_before(s.rs, len_base, cb, lane);
   const uint32_t my_len = active ? ld16(s.rs, len_base + 2u * c) : 0u;
   uint32_t total = my_len, mu = active ? my_len >> 2 : 0xFFFFFFFFu;
   for (int o = 32; o; o >>= 1) {
-    before += __shfl_xor(before, o);
     total += __shfl_xor(total, o);
     mu = min(mu, __shfl_xor(mu, o));
   }
@@ -739,19 +754,42 @@ __global__ __launch_bounds__(512) void k_decode_reg(DecodeArgs a) {
 
 // ---------------------------------------------------------------------------
 // Anchor streams of coded-anchor blobs.  One lane per stream (kv, layer,
-// channel) of a chunk, one wave per (64-channel block, (kv, layer), chunk); the
-// wave stages the (kv, layer) anchor table's cumulative counts in LDS.  A lane
-// reads its stream through the payload layout (as the delta decoders do),
-// decodes its n_groups symbols (the largest s with r cum[s] <= code, by an
-// eight-level bisection of the 257 cumulative counts; bytes shifted in while
-// range < 2^24) and writes anchor s - 128 of every group to the chunk's
-// anchor array, 64 bytes per wave and group.
-__global__ __launch_bounds__(64) void k_anchor_decode(AnchorDecodeArgs a) {
-  __shared__ uint32_t cum[kASym + 1];
-  const int lane = threadIdx.x;
-  const int cb = blockIdx.x, arow = blockIdx.y;  // arow = kv * L + l
+// channel) of a chunk, one wave per 64-channel block, a workgroup per (four
+// blocks, (kv, layer), chunk) sharing the (kv, layer) anchor table's cumulative
+// counts in LDS.  A lane
+// reads its stream through the payload layout (as the delta decoders do) and
+// writes anchor s - 128 of every group to the chunk's anchor array, 64 bytes
+// per wave and group.
+//
+// Symbols go in rounds of eight, wave-uniform like the delta decoders' groups:
+// at the end of a round a lane lands the 16-byte unit it fetched one round
+// earlier into its 16-word LDS ring and fetches the next unit if the ring has
+// room, so no wait inside a round is for memory, and every wait for a unit
+// comes after the same eight stores (an exact count).  A symbol takes at most
+// 16 bits (r freq >= 2^9), a round at most 128: one unit per round keeps up,
+// and a lead of two units (the ring starts with two landed) always covers the
+// round's windows.  Two symbols at a time take their bits from one 64-bit
+// window (three ring words); the symbol is the largest s with r cum[s] <= code,
+// found by an eight-level bisection (each level one v_mad_u64_u32 mask, as in
+// the delta search); the code is held complemented, shifted a whole byte at a
+// time with v_perm_b32.
+constexpr uint32_t kAncRing = 16;  // ring words per lane
+constexpr int kAncRound = 8;       // symbols per round
+constexpr int kAncWaves = 4;       // blocks (waves) per workgroup
+// dynamic LDS (from address 0): cum[0..256], then a ring [16 slots][64 lanes]
+// per wave
+constexpr uint32_t kAncRingAt = 4u * (kASym + 4);
+constexpr uint32_t kAncRingBytes = 4u * kAncRing * kLanes;
+constexpr uint32_t kAncLds = kAncRingAt + kAncWaves * kAncRingBytes;
+
+__global__ __launch_bounds__(64 * kAncWaves) void k_anchor_decode(AnchorDecodeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  auto cum = lds_at<uint32_t>(0);
+  auto ring = lds_at<uint32_t>(kAncRingAt + (uint32_t)wave * kAncRingBytes);
+  const int cb = blockIdx.x * kAncWaves + wave, arow = blockIdx.y;  // arow = kv * L + l
   const AncChunk ch = a.chunks[blockIdx.z];
-  {
+  if (wave == 0) {
     const uint16_t* f = a.afreq + (size_t)arow * kASym + 4 * lane;
     const uint32_t f0 = f[0], f1 = f[1], f2 = f[2], f3 = f[3];
     uint32_t incl = f0 + f1 + f2 + f3;
@@ -766,7 +804,6 @@ __global__ __launch_bounds__(64) void k_anchor_decode(AnchorDecodeArgs a) {
     cum[4 * lane + 3] = base + f0 + f1 + f2;
     if (lane == 63) cum[kASym] = incl;
   }
-  __syncthreads();
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc((void*)ch.blob, 0, (int)ch.blob_bytes, kBufRsrcWord3);
   const int prow = 2 * a.L + arow;  // the payload row of these streams
@@ -774,12 +811,10 @@ __global__ __launch_bounds__(64) void k_anchor_decode(AnchorDecodeArgs a) {
   const bool active = c < a.C;
   // the stream's words in the payload layout, as in the delta decoders' setup
   const uint32_t len_base = ch.off_len + 2u * (uint32_t)prow * (uint32_t)a.C;
-  uint32_t before = 0;
-  for (int j = lane; j < cb * kLanes; j += kLanes) before += ld16(rs, len_base + 2u * j);
+  const uint32_t before = words_before(rs, len_base, cb, lane);
   const uint32_t my_len = active ? ld16(rs, len_base + 2u * c) : 0u;
   uint32_t total = my_len, mu = active ? my_len >> 2 : 0xFFFFFFFFu;
   for (int o = 32; o; o >>= 1) {
-    before += __shfl_xor(before, o);
     total += __shfl_xor(total, o);
     mu = min(mu, __shfl_xor(mu, o));
   }
@@ -791,7 +826,8 @@ __global__ __launch_bounds__(64) void k_anchor_decode(AnchorDecodeArgs a) {
     const uint32_t y = __shfl_up(incl, o);
     if (lane >= o) incl += y;
   }
-  if (!active) return;
+  __syncthreads();  // the cumulative table
+  if (cb >= a.nblk || !active) return;
   const uint32_t blk = ld32(rs, 64u + 4u * (uint32_t)prow) + before;
   uint32_t bad = ((uint64_t)blk + total > ch.W) ? 1u : 0u;
   const uint32_t blk_byte = ch.off_pay + 4u * blk;
@@ -801,44 +837,93 @@ __global__ __launch_bounds__(64) void k_anchor_decode(AnchorDecodeArgs a) {
   wd.a0 = blk_byte + 16u * (uint32_t)lane;
   wd.t0 = blk_byte + 4u * (4u * m * ns + incl - tl) - 16u * m;
 
-  // stream bytes (a word holds four, the first in its top byte): the next
-  // ones in the top `avail` bits of bb, the word after them prefetched in pf
-  uint64_t bb = ((uint64_t)ld32(rs, wd.word(0)) << 32) | ld32(rs, wd.word(1));
-  uint32_t avail = 64, nextw = 2;
-  uint32_t pf = ld32(rs, wd.word(nextw));
-  auto take_byte = [&]() -> uint32_t {
-    const uint32_t b = (uint32_t)(bb >> 56);
-    bb <<= 8;
-    avail -= 8;
-    if (avail <= 32) {
-      bb |= (uint64_t)pf << (32 - avail);
-      avail += 32;
-      pf = ld32(rs, wd.word(++nextw));
-    }
-    return b;
+  // ring word k (stream word k, complemented) in slot k mod 16
+  auto put = [&](uint32_t k, uint32_t w) { ring[((k % kAncRing) << 6) + lane] = ~w; };
+  auto get = [&](uint32_t k) { return ring[((k % kAncRing) << 6) + lane]; };
+  auto put_unit = [&](uint32_t k, const u32x4& u) {
+    put(k, u.x);
+    put(k + 1, u.y);
+    put(k + 2, u.z);
+    put(k + 3, u.w);
   };
-  uint32_t code = 0;
-  for (int i = 0; i < 4; i++) code = (code << 8) | take_byte();
-  uint32_t range = 0xFFFFFFFFu;
-  int8_t* out = ch.out + (size_t)arow * ch.ng * a.C + c;
-  for (int g = 0; g < ch.ng; g++) {
-    const uint32_t r = range >> kProbBits;
-    if ((uint64_t)r * kProbTotal <= code) bad = 1u;  // code outside every symbol
-    uint32_t sym = 0;
-#pragma unroll
-    for (uint32_t stp = 128; stp; stp >>= 1)
-      if (r * cum[sym + stp] <= code) sym += stp;
-    const uint32_t c0 = cum[sym];
-    code -= r * c0;
-    range = r * (cum[sym + 1] - c0);
-    while (range < kTop) {
-      code = (code << 8) | take_byte();
-      range <<= 8;
-    }
-    out[(size_t)g * a.C] = (int8_t)((int)sym - 128);
+  {
+    const u32x4 u0 = Block<4>::load(rs, wd.unit(0)).v, u1 = Block<4>::load(rs, wd.unit(1)).v;
+    put_unit(0, u0);
+    put_unit(4, u1);
   }
-  // a valid stream keeps code < range throughout
-  bad |= code >= range ? 1u : 0u;
+  uint32_t landed = 8;  // ring words landed
+  u32x4 pend = Block<4>::load(rs, wd.unit(2)).v;
+  bool inflight = true;
+  uint32_t ncode = get(0), range = 0xFFFFFFFFu;
+  uint32_t p = 32;  // stream bits shifted into the code
+  // the bisection's first two levels are the same keys for every lane:
+  // cum[128], then cum[64] or cum[192]
+  const uint32_t key128 = cum[128], key64 = cum[64], key192 = cum[192];
+
+  // one symbol whose next stream bits are x (complemented); returns s and
+  // leaves the shift and its selector in sh, sel
+  constexpr uint32_t cum0 = 0;  // LDS byte address of cum[0]
+  auto symbol = [&](uint32_t x, uint32_t& sh, uint32_t& sel) -> uint32_t {
+    const uint32_t r = range >> kProbBits;
+    // ad = byte offset 4 s of the symbol being bisected
+    const uint32_t m1 = le_mask(r, key128, ncode);
+    uint32_t ad = m1 & (128u * 4u);
+    ad |= le_mask(r, bit_select(m1, key192, key64), ncode) & (64u * 4u);
+#pragma unroll
+    for (uint32_t stp = 32; stp; stp >>= 1) ad |= le_mask(r, lds32(cum0 + ad + 4u * stp), ncode) & (4u * stp);
+    const uint32_t c0 = lds32(cum0 + ad), c1 = lds32(cum0 + ad + 4u);
+    const uint32_t sym = ad >> 2;
+    ncode += mul24(r, c0);  // code -= r * cum[s]
+    const uint32_t rn = mul24(r, c1 - c0);
+    sh = (uint32_t)__builtin_clz(rn) & 24u;
+    range = rn << sh;
+    sel = shift_sel(sh);
+    ncode = __builtin_amdgcn_perm(ncode, x, sel);
+    return sym;
+  };
+  // this (kv, layer)'s anchors [ng][C] through a buffer resource: the channel is
+  // the vector offset, the group's row a wave-uniform scalar offset
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(ch.out + (size_t)arow * ch.ng * a.C), 0, (int)((uint32_t)ch.ng * (uint32_t)a.C),
+      kBufRsrcWord3);
+  auto put_anchor = [&](int g, uint32_t sym) {
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(sym ^ 0x80u), ro, (uint32_t)c,
+                                         (uint32_t)g * (uint32_t)a.C, 0);
+  };
+  // n (1 or 2) symbols from the 64-bit window at bit p
+  auto pair = [&](int g, int n) {
+    const uint32_t j = p >> 5, o = p & 31u;
+    const uint32_t w0 = get(j), w1 = get(j + 1), w2 = get(j + 2);
+    const uint32_t hi = (uint32_t)((((uint64_t)w0 << 32) | w1) << o >> 32);
+    const uint32_t lo = (uint32_t)((((uint64_t)w1 << 32) | w2) << o >> 32);
+    uint32_t sh1, sel1, sh2, sel2;
+    put_anchor(g, symbol(hi, sh1, sel1));  // anchor s - 128: s with its top bit flipped
+    p += sh1;
+    if (n == 2) {
+      put_anchor(g + 1, symbol(__builtin_amdgcn_perm(hi, lo, sel1), sh2, sel2));
+      p += sh2;
+    }
+  };
+  auto ring_step = [&]() {
+    if (inflight) {
+      put_unit(landed, pend);
+      landed += 4;
+    }
+    // the next unit lands over ring words already consumed (lanes without
+    // room point their load past the blob end: no memory access)
+    inflight = landed + 4u - (p >> 5) <= kAncRing;
+    pend = Block<4>::load(rs, inflight ? wd.unit(landed >> 2) : 0xFFFFFFF0u).v;
+  };
+  int g = 0;
+  for (; g + kAncRound <= ch.ng; g += kAncRound) {
+#pragma unroll
+    for (int i = 0; i < kAncRound; i += 2) pair(g + i, 2);
+    ring_step();
+  }
+  for (; g + 1 < ch.ng; g += 2) pair(g, 2);  // the last round needs no more words
+  if (g < ch.ng) pair(g, 1);
+  // a valid stream keeps code < range throughout; a corrupt one breaks it for good
+  bad |= (~ncode >= range) ? 1u : 0u;
   if (bad) atomicOr(a.status, 1u);
 }
 
@@ -867,7 +952,9 @@ void launch_decode_t(const DecodeArgs& a, hipStream_t st) {
 
 hipError_t launch_anchor_decode(const AnchorDecodeArgs& a, hipStream_t st) {
   if (a.nchunks > 0)
-    k_anchor_decode<<<dim3((unsigned)a.nblk, (unsigned)(2 * a.L), (unsigned)a.nchunks), 64, 0, st>>>(a);
+    k_anchor_decode<<<dim3((unsigned)((a.nblk + kAncWaves - 1) / kAncWaves), (unsigned)(2 * a.L),
+                           (unsigned)a.nchunks),
+                      64 * kAncWaves, kAncLds, st>>>(a);
   return hipGetLastError();
 }
 

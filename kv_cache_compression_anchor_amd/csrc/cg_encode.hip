@@ -340,15 +340,30 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_anchor_encode(EncodeA
   const uint32_t woff0 = o.woff + kRowBytes;
   RcEnc e = {0, 0u, 0u, 0xFFFFFFFFu, 0u, 0u};
   const uint32_t gstep = (uint32_t)a.G * row_bytes;
-  uint32_t hx = ld_half(xin, lane_off, 0u);
-  for (int g = 0; g < B.ng; g++) {
-    // the next group's anchor token is loaded a group ahead (past the last
-    // group: the last one again, inside the chunk)
-    const uint32_t h = hx;
-    hx = ld_half(xin, lane_off, (uint32_t)min(g + 1, B.ng - 1) * gstep);
-    const uint32_t s = (uint32_t)(quant_anchor(half_bits_to_float(h), inv_a) + 128);
-    const uint32_t c0 = cum[s];
-    rc_put(e, c0, cum[s + 1] - c0, o);
+  // anchor tokens in batches of kAB, loaded one batch ahead (a batch past the
+  // last group re-reads the last group, inside the chunk)
+  constexpr int kAB = 16;
+  uint32_t xa[kAB], xb[kAB];
+  auto load = [&](uint32_t (&x)[kAB], int g0) {
+#pragma unroll
+    for (int j = 0; j < kAB; j++) x[j] = ld_half(xin, lane_off, (uint32_t)min(g0 + j, B.ng - 1) * gstep);
+  };
+  auto code = [&](const uint32_t (&x)[kAB], int g0) {
+#pragma unroll
+    for (int j = 0; j < kAB; j++) {
+      if (g0 + j >= B.ng) break;  // wave-uniform
+      const uint32_t s = (uint32_t)(quant_anchor(half_bits_to_float(x[j]), inv_a) + 128);
+      const uint32_t c0 = cum[s];
+      rc_put(e, c0, cum[s + 1] - c0, o);
+    }
+  };
+  load(xa, 0);
+  load(xb, kAB);
+  for (int g0 = 0; g0 < B.ng; g0 += 2 * kAB) {
+    code(xa, g0);
+    load(xa, g0 + 2 * kAB);
+    code(xb, g0 + kAB);
+    load(xb, g0 + 3 * kAB);
   }
   rc_finish(e, o);  // every chunk has at least one group
   const uint32_t nwords = (o.woff - woff0) / kRowBytes;
