@@ -131,10 +131,12 @@ int cg_build_tables_grouped(const cg_params* params, int32_t grouping, const voi
  * sure no enqueued work still uses it. */
 void cg_tables_free(cg_tables* tables);
 
-/* Serialized tables (the codebook shipped to a decoder).  cg_tables_serialize
+/* Serialized tables (the codebook shipped to a decoder): CGT1 version 1, or
+ * version 2 with the anchor tables of coded anchors.  cg_tables_serialize
  * copies them into the host buffer `buf` of `cap` bytes; *len receives the size
  * (call with buf == NULL to query it).  cg_tables_deserialize validates host
- * bytes and uploads them to the current device. */
+ * bytes (header, parameters, size, every scale, step and frequency table) and
+ * uploads them to the current device; CG_E_INVAL for anything malformed. */
 int cg_tables_serialize(const cg_tables* tables, void* buf, size_t cap, size_t* len);
 int cg_tables_deserialize(const void* buf, size_t len, cg_tables** out);
 
@@ -186,9 +188,10 @@ int cg_encode_batch_noalloc(const cg_tables* tables, const void* k_dev, const vo
                             void* stream);
 
 /* Parses and checks a blob header from host memory (len >= 64). Host only.
- * CG_E_INVAL for a header that is not CGK1 v1, whose fields disagree with each
- * other, whose blob would exceed 4 GiB, or whose chunk of one layer
- * (chunk_tokens x channels x 2 bytes) is 4 GiB or more. */
+ * CG_E_INVAL for a header that is not CGK1 version 2 (raw anchors) or 3
+ * (range-coded anchors), whose fields disagree with each other, whose blob
+ * would exceed 4 GiB, or whose chunk of one layer (chunk_tokens x channels x 2
+ * bytes) is 4 GiB or more.  out->version is the blob's format version. */
 int cg_chunk_info_parse(const void* blob_host, size_t len, cg_chunk_info* out);
 
 /* Decodes n blobs (device addresses blobs_dev[i]) into K/V fp16
@@ -204,7 +207,12 @@ int cg_decode(const cg_tables* tables, int32_t n, const void* const* blobs_dev,
  * copy); the device blob must hold the same bytes.  Bit 0 of *status_dev
  * (caller-owned device uint32, never cleared by the library) is set if a
  * stream of a blob is inconsistent (offsets past the payload, impossible code
- * value).  Corrupt payloads never cause out-of-bounds accesses. */
+ * value).  Corrupt payloads never cause out-of-bounds accesses.  A blob whose
+ * format (cg_chunk_info.version) differs from the tables' anchor coding is
+ * CG_E_MISMATCH.  With coded anchors the call first decodes the anchor
+ * streams into 2 x layers x n_groups x channels bytes per blob, allocated
+ * stream-ordered on `stream` (hipMallocAsync) and freed there after the
+ * decode (hipFreeAsync); the other decode entry points do the same. */
 int cg_decode_async(const cg_tables* tables, int32_t n, const void* const* blobs_dev,
                     const cg_chunk_info* infos, void* k_out_dev, void* v_out_dev,
                     uint32_t* status_dev, void* stream);
