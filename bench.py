@@ -273,6 +273,8 @@ def main():
                            "unit": "GB/s", "frac": round(build_achieved / HBM_PEAK_GBPS, 4)},
         "cpu_baseline_encode": cpu_enc,
         "input_generation_s": round(t_gen, 2),
+        "versions": {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+                     "device": torch.cuda.get_device_name(0)},
     }
     if not args.no_anchor_coded:
         line["anchor_coded"] = anchor_coded_figures(w, kd, vd, args.other_steps, 1, sel_blob_bytes,
