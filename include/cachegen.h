@@ -211,8 +211,10 @@ int cg_decode(const cg_tables* tables, int32_t n, const void* const* blobs_dev,
  * format (cg_chunk_info.version) differs from the tables' anchor coding is
  * CG_E_MISMATCH.  With coded anchors the call first decodes the anchor
  * streams into 2 x layers x n_groups x channels bytes per blob, allocated
- * stream-ordered on `stream` (hipMallocAsync) and freed there after the
- * decode (hipFreeAsync); the other decode entry points do the same. */
+ * stream-ordered on `stream` from a memory pool the library keeps per device
+ * (hipMallocFromPoolAsync) and freed there after the decode (hipFreeAsync);
+ * the pool keeps the blocks it has held until the process ends.  The other
+ * decode entry points do the same. */
 int cg_decode_async(const cg_tables* tables, int32_t n, const void* const* blobs_dev,
                     const cg_chunk_info* infos, void* k_out_dev, void* v_out_dev,
                     uint32_t* status_dev, void* stream);

@@ -312,9 +312,45 @@ int enqueue_decode_chunks(const cg_tables* h, int n, const void* const* blobs,
   return CG_OK;
 }
 
+// Stream-ordered memory pool of the coded-anchor decode workspaces, one per
+// device, made on first use and kept, with the blocks it has cached, until the
+// process ends.  The device's default pool hands freed blocks back to the
+// driver at the next synchronisation, and the next hipMalloc on the device then
+// waits for that: about 0.4 ms a decode.  This pool keeps what it has held
+// (the high-water mark of the decode workspaces outstanding at once).
+struct AnchorPool {
+  std::mutex mu;
+  hipMemPool_t pool = nullptr;
+};
+
+int anchor_pool(int dev, hipMemPool_t* out) {
+  static AnchorPool p[kMaxDevices];
+  if (dev < 0 || dev >= kMaxDevices) return fail(CG_E_INVAL, "device index beyond the supported range");
+  std::lock_guard<std::mutex> lock(p[dev].mu);
+  if (!p[dev].pool) {
+    hipMemPoolProps props;
+    memset(&props, 0, sizeof(props));
+    props.allocType = hipMemAllocationTypePinned;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    HIP_TRY(hipMemPoolCreate(&pool, &props), "hipMemPoolCreate(anchors)");
+    uint64_t keep = UINT64_MAX;
+    const hipError_t e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    if (e != hipSuccess) {
+      (void)hipMemPoolDestroy(pool);
+      return hip_fail(e, "hipMemPoolSetAttribute(anchors)");
+    }
+    p[dev].pool = pool;
+  }
+  *out = p[dev].pool;
+  return CG_OK;
+}
+
 // Enqueues the decode of n checked blobs.  Raw anchors are read from the
 // blobs; coded anchors are first decoded into a stream-ordered allocation of
-// 2 L ng C bytes per blob (hipMallocAsync on st, freed on st after the decode).
+// 2 L ng C bytes per blob from the device's anchor pool (allocated on st,
+// freed on st after the decode).
 int enqueue_decode(const cg_tables* h, int n, const void* const* blobs, const cg_chunk_info* infos,
                    void* k_out, void* v_out, uint32_t* status, hipStream_t st,
                    const PagedOut* pg = nullptr) {
@@ -331,9 +367,11 @@ int enqueue_decode(const cg_tables* h, int n, const void* const* blobs, const cg
     off[i] = bytes;
     bytes += align256((size_t)2 * t.L * infos[i].n_groups * t.C);
   }
+  hipMemPool_t pool = nullptr;
+  int rc = anchor_pool(h->dev, &pool);
+  if (rc) return rc;
   int8_t* ws = nullptr;
-  HIP_TRY(hipMallocAsync((void**)&ws, bytes, st), "hipMallocAsync(anchors)");
-  int rc = CG_OK;
+  HIP_TRY(hipMallocFromPoolAsync((void**)&ws, bytes, pool, st), "hipMallocFromPoolAsync(anchors)");
   for (int i0 = 0; i0 < n && rc == CG_OK; i0 += kDecMaxChunks) {
     AnchorDecodeArgs a;
     memset(&a, 0, sizeof(a));
