@@ -21,7 +21,6 @@ namespace {
 struct RcEnc {
   uint64_t L;      // window (bits 0..31) and the bytes above it (bits 32..32+kh-1)
   uint32_t kh;     // 8 * bytes above the window: 0..24
-  uint32_t hmask;  // (1 << kh) - 1, the held bytes' bits in the high word of L
   uint32_t range;
   uint32_t W;      // last word taken out of L, not final yet
   uint32_t P;      // 0xFFFFFFFF words after W, not final yet
@@ -57,9 +56,10 @@ __device__ __forceinline__ void carry_into_run(RcEnc& e, Sink& o) {
 // the carry out of the held bytes after an addition to L: into W, or through
 // an all-ones run
 __device__ __forceinline__ void settle_carry(RcEnc& e, Sink& o) {
+  const uint32_t hmask = (1u << e.kh) - 1u;
   uint32_t hi = (uint32_t)(e.L >> 32);
-  const bool c = hi > e.hmask;
-  hi &= e.hmask;
+  const bool c = hi > hmask;
+  hi &= hmask;
   e.L = ((uint64_t)hi << 32) | (uint32_t)e.L;
   if (c && e.P) {
     carry_into_run(e, o);
@@ -79,7 +79,6 @@ __device__ __forceinline__ void shift_bytes(RcEnc& e, uint32_t nb8, Sink& o) {
   const uint32_t hi_k = ext ? 0u : hi;
   e.L = (((uint64_t)hi_k << 32) | lo_k) << nb8;
   e.kh = kh2 & 31u;
-  e.hmask = (1u << e.kh) - 1u;
   if (ext) {
     if (wn == 0xFFFFFFFFu) {
       e.P++;  // may still wrap
@@ -101,34 +100,36 @@ __device__ __forceinline__ void rc_put(RcEnc& e, uint32_t c0, uint32_t freq, Sin
   const uint32_t r = e.range >> kProbBits;
   const uint64_t L1 = e.L + (uint64_t)r * c0;  // one 32 x 32 -> 64 multiply-add
   const uint32_t lo = (uint32_t)L1, hx = (uint32_t)(L1 >> 32);
-  const bool c = hx > e.hmask;
-  const uint32_t hi = hx & e.hmask;
+  // the held bytes are below 2^kh and r c0 below 2^32, so the carry out of
+  // them is bit kh of hx, and nothing above it
+  const uint32_t cy = hx >> e.kh;
   const uint32_t rn = mul24(r, freq);
   const uint32_t nb8 = (uint32_t)__builtin_clz(rn) & 24u;  // renormalise while range < 2^24
   const uint32_t kh2 = e.kh + nb8;
   const bool ext = kh2 >= 32u;
-  const uint32_t wn = __builtin_amdgcn_alignbit(hi, lo, e.kh);
-  const bool rare = e.P != 0u ? (c || ext) : (ext && wn == 0xFFFFFFFFu);
-  const uint32_t W1 = e.W + (c ? 1u : 0u);
+  // the four top bytes of the window and held bytes (the carry bit lies above)
+  const uint32_t wn = __builtin_amdgcn_alignbit(hx, lo, e.kh);
+  const bool open = e.P != 0u;
+  const bool rare = (ext & (open | (wn == 0xFFFFFFFFu))) | (open & (cy != 0u));
+  const uint32_t W1 = e.W + cy;
   const bool emit = ext && !rare;
   if (emit) __builtin_amdgcn_raw_buffer_store_b32(W1, o.rs, o.woff, 0, 0);
   o.woff += emit ? kRowBytes : 0u;
   e.W = emit ? wn : W1;
-  const uint32_t lo_k = ext ? __builtin_amdgcn_ubfe(lo, 0u, e.kh) : lo;
-  const uint32_t hi_k = ext ? 0u : hi;
-  e.L = (((uint64_t)hi_k << 32) | lo_k) << nb8;
+  // shifted by nb8, L keeps its low 32 + (kh2 mod 32) bits: without a word
+  // leaving that is all of it less the carry; with one, the window's low kh
+  // bits, moved up
+  const uint64_t Ls = L1 << nb8;
   e.kh = kh2 & 31u;
-  e.hmask = (1u << e.kh) - 1u;
+  e.L = ((uint64_t)__builtin_amdgcn_ubfe((uint32_t)(Ls >> 32), 0u, e.kh) << 32) | (uint32_t)Ls;
   e.range = rn << nb8;
-  if (__builtin_amdgcn_ballot_w64(rare)) {
-    if (rare) {
-      RcEnc s = e0;
-      s.L = L1;
-      settle_carry(s, o);
-      s.range = rn << nb8;
-      shift_bytes(s, nb8, o);
-      e = s;
-    }
+  if (rare) {
+    RcEnc s = e0;
+    s.L = L1;
+    settle_carry(s, o);
+    s.range = rn << nb8;
+    shift_bytes(s, nb8, o);
+    e = s;
   }
 }
 
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
   const bool raw_anchors = B.lay.off_anchor != 0;
   int8_t* anchors = reinterpret_cast<int8_t*>(B.blob + B.lay.off_anchor) +
                     ((size_t)kv * a.L + l) * B.ng * a.C + c;
-  RcEnc e = {0, 0u, 0u, 0xFFFFFFFFu, 0u, 0u};
+  RcEnc e = {0, 0u, 0xFFFFFFFFu, 0u, 0u};
   uint32_t nonfinite = 0;
 
   // one group from its tokens' binary16 bits: the anchor, then the deltas
@@ -338,7 +339,7 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_anchor_encode(EncodeA
                                            (int)(kRowBytes * (uint32_t)a.swb), kBufRsrcWord3);
   o.woff = 4u * (uint32_t)lane;
   const uint32_t woff0 = o.woff + kRowBytes;
-  RcEnc e = {0, 0u, 0u, 0xFFFFFFFFu, 0u, 0u};
+  RcEnc e = {0, 0u, 0xFFFFFFFFu, 0u, 0u};
   const uint32_t gstep = (uint32_t)a.G * row_bytes;
   // anchor tokens in batches of kAB, loaded one batch ahead (a batch past the
   // last group re-reads the last group, inside the chunk)
