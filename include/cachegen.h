@@ -21,12 +21,13 @@
  * channels fastest, in device memory.
  *
  * Memory ownership: every pointer argument is owned by the caller, except the
- * cg_tables handle, which the library allocates (device copies of the tables,
- * encode scratch) and cg_tables_free releases.  Building tables also uses one
- * workspace per device (statistics, symbol counts, digests; it grows to the
- * largest build and is kept until the process ends; builds on one device take
- * turns on it).  Device buffers passed to an *_async / streamed call must stay
- * valid until the stream has executed the work.
+ * cg_tables handle, which the library allocates (device copies of the tables)
+ * and cg_tables_free releases.  Building tables and encoding each use one
+ * workspace per device (statistics, symbol counts, digests; the encoder's
+ * stream scratch, lengths and status words), grown to the largest build or
+ * batch and kept until the process ends; builds on one device take turns on
+ * theirs, and so do encode batches.  Device buffers passed to an *_async /
+ * streamed call must stay valid until the stream has executed the work.
  *
  * Streams: a `void* stream` is a hipStream_t (NULL = the legacy default stream).
  * A handle is used on the device that built or deserialized it; the library
@@ -155,7 +156,7 @@ int cg_encode_bound(const cg_tables* tables, int32_t chunk, size_t* max_bytes);
  * (kv, layer, channel): the group's first token as an int8 anchor, the others
  * as range-coded delta symbols (CacheGen blog, section 2.1 stages 1-3).
  * Runs on `stream` and waits for it; *out_len receives the blob size.
- * A handle encodes on one stream at a time (it owns the encode scratch). */
+ * Encodes on one device take turns on its encode workspace. */
 int cg_encode(const cg_tables* tables, const void* k_dev, const void* v_dev,
               int32_t chunk, int32_t quality, void* out_dev, size_t cap,
               size_t* out_len, void* stream);

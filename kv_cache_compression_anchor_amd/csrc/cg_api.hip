@@ -19,15 +19,7 @@ struct cg_tables {
   int dev = 0;
   DevTables t;
   uint64_t id = 0;
-  std::mutex mu;  // guards the encode buffers and the status words
-  uint32_t* scratch = nullptr;   // per launch slot: [2][L][nblk] blocks of [swb][64] words
-  size_t scratch_words = 0;
-  uint32_t* lens = nullptr;      // per launch slot: [2][L][C]
-  uint32_t* row_words = nullptr; // per launch slot: [2L] rows, then [2L][nblk] blocks
-  int enc_slots = 0;             // blobs one encode launch can hold
-  uint32_t* enc_status = nullptr;   // per blob of a batch: W, too large, non-finite, pad
-  uint32_t* enc_host = nullptr;     // pinned mirror
-  int enc_status_cap = 0;
+  std::mutex mu;  // guards the decode status words
   uint8_t* dev_block = nullptr;  // one allocation: serialized tables, images, status words
   uint32_t* status = nullptr;    // device words: decode status
   uint32_t* host_status = nullptr;  // pinned mirror, allocated on first use
@@ -99,11 +91,6 @@ void free_tables(cg_tables* t) {
   if (!t) return;
   DeviceGuard g(t->dev);
   if (t->dev_block) (void)hipFree(t->dev_block);
-  if (t->scratch) (void)hipFree(t->scratch);
-  if (t->lens) (void)hipFree(t->lens);
-  if (t->row_words) (void)hipFree(t->row_words);
-  if (t->enc_status) (void)hipFree(t->enc_status);
-  if (t->enc_host) (void)hipHostFree(t->enc_host);
   if (t->host_status) (void)hipHostFree(t->host_status);
   delete t;
 }
@@ -703,6 +690,44 @@ int cg_encode_bound(const cg_tables* h, int32_t chunk, size_t* max_bytes) {
 // Scratch memory the encoder may hold: the blobs of one launch share it.
 constexpr size_t kEncScratchBudget = (size_t)3 << 30;
 
+// Device workspace of cg_encode_batch, one per device, grown when a batch needs
+// more and kept until the process ends: per blob slot of a launch the streams'
+// scratch ([2][L][nblk] blocks of [swb][64] words), their lengths ([2][L][C])
+// and row and block totals ([2L], then [2L][nblk]); per blob of a batch four
+// status words (W, too large, non-finite, pad) and their pinned mirror.  A
+// batch holds the mutex until it has synchronised its stream, so batches on
+// one device take turns.  (Allocated per tables handle, the 1 GB of scratch of
+// the Mistral-7B-shape batch cost 0.2 ms of hipMalloc in every step that
+// builds new tables.)
+struct EncWs {
+  std::mutex mu;
+  uint32_t* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  uint32_t* lens = nullptr;
+  size_t lens_bytes = 0;
+  uint32_t* row_words = nullptr;
+  size_t row_bytes = 0;
+  uint32_t* status = nullptr;
+  uint32_t* host = nullptr;
+  size_t status_bytes = 0;
+};
+
+EncWs* enc_ws(int dev) {
+  static EncWs ws[kMaxDevices];
+  return dev >= 0 && dev < kMaxDevices ? &ws[dev] : nullptr;
+}
+
+// with ws->mu held: *buf holds at least `bytes` device bytes
+int reserve_dev(uint32_t** buf, size_t* have, size_t bytes) {
+  if (*have >= bytes) return CG_OK;
+  if (*buf) (void)hipFree(*buf);
+  *buf = nullptr;
+  *have = 0;
+  if (hipMalloc(buf, bytes) != hipSuccess) return fail(CG_E_NOMEM, "encode workspace");
+  *have = bytes;
+  return CG_OK;
+}
+
 // Waves the device can hold at once: compute units x threads per compute unit
 // / 64 (the encoder's VGPR and LDS use leave this bound the binding one).
 size_t resident_waves(int dev) {
@@ -724,7 +749,9 @@ int cg_encode_batch(const cg_tables* ch, const void* k_dev, const void* v_dev, i
   const DevTables& t = h->t;
   DeviceGuard dg(h->dev);
   if (!dg.ok) return fail(CG_E_HIP, "cannot select the tables' device");
-  std::lock_guard<std::mutex> lk(h->mu);
+  EncWs* ws = enc_ws(h->dev);
+  if (!ws) return fail(CG_E_INVAL, "device index beyond the supported range");
+  std::lock_guard<std::mutex> lk(ws->mu);
   const size_t swb = stream_scratch_words(t), aswb = anchor_scratch_words(t);
   // whole 64-stream blocks of 2L rows: the delta rows, then (coded anchors) the
   // anchor rows in the same buffers
@@ -740,31 +767,23 @@ int cg_encode_batch(const cg_tables* ch, const void* k_dev, const void* v_dev, i
   const size_t fit = std::max<size_t>(1, std::min(budget, cap / wpb));
   const bool one_round = (n + fit - 1) / fit <= (n + budget - 1) / budget + 1;
   const int slots = (int)(one_round ? fit : budget);
-  if (h->enc_slots < slots) {
-    if (h->scratch) (void)hipFree(h->scratch);
-    if (h->lens) (void)hipFree(h->lens);
-    if (h->row_words) (void)hipFree(h->row_words);
-    h->scratch = nullptr;
-    h->lens = h->row_words = nullptr;
-    h->enc_slots = 0;
-    if (hipMalloc(&h->scratch, 4 * slot_words * slots) != hipSuccess ||
-        hipMalloc(&h->lens, 4 * t.lay.n * slots) != hipSuccess ||
-        hipMalloc(&h->row_words, 4 * (size_t)2 * t.L * (1 + t.nblk) * slots) != hipSuccess)
-      return fail(CG_E_NOMEM, "encode scratch");
-    h->enc_slots = slots;
-  }
-  if (h->enc_status_cap < n) {
-    if (h->enc_status) (void)hipFree(h->enc_status);
-    if (h->enc_host) (void)hipHostFree(h->enc_host);
-    h->enc_status = h->enc_host = nullptr;
-    h->enc_status_cap = 0;
-    if (hipMalloc(&h->enc_status, 16 * (size_t)n) != hipSuccess ||
-        hipHostMalloc(&h->enc_host, 16 * (size_t)n, hipHostMallocDefault) != hipSuccess)
+  const size_t row_words_per_slot = (size_t)2 * t.L * (1 + t.nblk);
+  if ((rc = reserve_dev(&ws->scratch, &ws->scratch_bytes, 4 * slot_words * slots)) ||
+      (rc = reserve_dev(&ws->lens, &ws->lens_bytes, 4 * t.lay.n * slots)) ||
+      (rc = reserve_dev(&ws->row_words, &ws->row_bytes, 4 * row_words_per_slot * slots)))
+    return rc;
+  if (ws->status_bytes < 16 * (size_t)n) {
+    if (ws->status) (void)hipFree(ws->status);
+    if (ws->host) (void)hipHostFree(ws->host);
+    ws->status = ws->host = nullptr;
+    ws->status_bytes = 0;
+    if (hipMalloc(&ws->status, 16 * (size_t)n) != hipSuccess ||
+        hipHostMalloc(&ws->host, 16 * (size_t)n, hipHostMallocDefault) != hipSuccess)
       return fail(CG_E_NOMEM, "encode status");
-    h->enc_status_cap = n;
+    ws->status_bytes = 16 * (size_t)n;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  HIP_TRY(hipMemsetAsync(h->enc_status, 0, 16 * (size_t)n, st), "clear status");
+  HIP_TRY(hipMemsetAsync(ws->status, 0, 16 * (size_t)n, st), "clear status");
   // blobs in quality order, so that the blobs of one launch fall into few groups
   // of one quality (a group's workgroups stage each table once for all of them)
   std::vector<int> order(n);
@@ -783,11 +802,11 @@ int cg_encode_batch(const cg_tables* ch, const void* k_dev, const void* v_dev, i
       const int i = order[i0 + j];
       EncBlob& B = a.b[j];
       init_enc_blob(B, t, chunks[i], qualities[i], outs_dev[i], caps[i]);
-      B.scratch = h->scratch + (size_t)j * slot_words;
-      B.lens = h->lens + (size_t)j * t.lay.n;
-      B.row_words = h->row_words + (size_t)j * 2 * t.L * (1 + t.nblk);
+      B.scratch = ws->scratch + (size_t)j * slot_words;
+      B.lens = ws->lens + (size_t)j * t.lay.n;
+      B.row_words = ws->row_words + (size_t)j * row_words_per_slot;
       B.block_words = B.row_words + 2 * t.L;
-      B.status = h->enc_status + 4 * (size_t)i;
+      B.status = ws->status + 4 * (size_t)i;
       // open a new group at a quality change or when the current one is full
       if (j == 0 || a.b[j - 1].q != B.q || a.groups[a.n_groups - 1].blob[3] >= 0) {
         EncGroup& eg = a.groups[a.n_groups++];
@@ -807,11 +826,11 @@ int cg_encode_batch(const cg_tables* ch, const void* k_dev, const void* v_dev, i
       HIP_TRY(launch_encode(a, st), "anchor encode launch");
     }
   }
-  HIP_TRY(hipMemcpyAsync(h->enc_host, h->enc_status, 16 * (size_t)n, hipMemcpyDeviceToHost, st),
+  HIP_TRY(hipMemcpyAsync(ws->host, ws->status, 16 * (size_t)n, hipMemcpyDeviceToHost, st),
           "encode status");
   HIP_TRY(hipStreamSynchronize(st), "encode");
   rc = CG_OK;
-  for (int i = 0; i < n; i++) finish_blob(t, chunks[i], h->enc_host + 4 * (size_t)i, &out_lens[i], &rc);
+  for (int i = 0; i < n; i++) finish_blob(t, chunks[i], ws->host + 4 * (size_t)i, &out_lens[i], &rc);
   return rc;
 }
 
