@@ -21,8 +21,10 @@
  * channels fastest, in device memory.
  *
  * Memory ownership: every pointer argument is owned by the caller, except the
- * cg_tables handle, which the library allocates (device copies of the tables)
- * and cg_tables_free releases.  Building tables and encoding each use one
+ * cg_tables handle, which the library allocates (device copies of the tables,
+ * from a stream-ordered memory pool it keeps per device, which holds on to the
+ * blocks it has cached until the process ends) and cg_tables_free releases
+ * (after waiting for the device).  Building tables and encoding each use one
  * workspace per device (statistics, symbol counts, digests; the encoder's
  * stream scratch, lengths and status words), grown to the largest build or
  * batch and kept until the process ends; builds on one device take turns on

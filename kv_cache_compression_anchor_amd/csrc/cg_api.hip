@@ -87,10 +87,53 @@ void write_header(uint8_t* h, const cg_params& p) {
   memcpy(h, u, kTabHdr);
 }
 
+constexpr int kMaxDevices = 64;
+
+// Stream-ordered memory pool, one per device, made on first use and kept, with
+// the blocks it has cached, until the process ends: the device copies of each
+// tables handle and the coded-anchor decode workspaces come from it.  The
+// device's default pool hands freed blocks back to the driver at the next
+// synchronisation, and the next hipMalloc on the device then waits for that
+// (about 0.4 ms after a coded-anchor decode); a hipMalloc of the tables' 75 MB
+// of the Mistral-7B shape took 0.05-0.16 ms of every build.  This pool keeps
+// what it has held (the high-water mark of the blocks outstanding at once).
+struct KeepPool {
+  std::mutex mu;
+  hipMemPool_t pool = nullptr;
+};
+
+int keep_pool(int dev, hipMemPool_t* out) {
+  static KeepPool p[kMaxDevices];
+  if (dev < 0 || dev >= kMaxDevices) return fail(CG_E_INVAL, "device index beyond the supported range");
+  std::lock_guard<std::mutex> lock(p[dev].mu);
+  if (!p[dev].pool) {
+    hipMemPoolProps props;
+    memset(&props, 0, sizeof(props));
+    props.allocType = hipMemAllocationTypePinned;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    HIP_TRY(hipMemPoolCreate(&pool, &props), "hipMemPoolCreate");
+    uint64_t keep = UINT64_MAX;
+    const hipError_t e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    if (e != hipSuccess) {
+      (void)hipMemPoolDestroy(pool);
+      return hip_fail(e, "hipMemPoolSetAttribute");
+    }
+    p[dev].pool = pool;
+  }
+  *out = p[dev].pool;
+  return CG_OK;
+}
+
 void free_tables(cg_tables* t) {
   if (!t) return;
   DeviceGuard g(t->dev);
-  if (t->dev_block) (void)hipFree(t->dev_block);
+  if (t->dev_block) {
+    // no work on any stream may still use the block (as hipFree would wait)
+    (void)hipDeviceSynchronize();
+    (void)hipFreeAsync(t->dev_block, nullptr);
+  }
   if (t->host_status) (void)hipHostFree(t->host_status);
   delete t;
 }
@@ -100,7 +143,7 @@ size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // The tables' device memory in one allocation: serialized tables, the LDS
 // images of each built quality, 64 status words.
-int alloc_tables(cg_tables* h) {
+int alloc_tables(cg_tables* h, hipStream_t st) {
   DevTables& t = h->t;
   size_t off = align256(t.lay.total);
   size_t img_off[3] = {0, 0, 0};
@@ -111,7 +154,9 @@ int alloc_tables(cg_tables* h) {
     }
   const size_t status_off = off;
   off += 256;
-  HIP_TRY(hipMalloc(&h->dev_block, off), "hipMalloc(tables)");
+  hipMemPool_t pool = nullptr;
+  if (int rc = keep_pool(h->dev, &pool)) return rc;
+  HIP_TRY(hipMallocFromPoolAsync((void**)&h->dev_block, off, pool, st), "tables allocation");
   t.ser = h->dev_block;
   for (int q = 0; q < 3; q++)
     if ((t.mask >> q) & 1u) t.img[q] = reinterpret_cast<uint16_t*>(h->dev_block + img_off[q]);
@@ -136,7 +181,6 @@ struct BuildWs {
   size_t bytes = 0;
   uint32_t* host = nullptr;
 };
-constexpr int kMaxDevices = 64;
 
 BuildWs* build_ws(int dev) {
   static BuildWs ws[kMaxDevices];
@@ -299,41 +343,6 @@ int enqueue_decode_chunks(const cg_tables* h, int n, const void* const* blobs,
   return CG_OK;
 }
 
-// Stream-ordered memory pool of the coded-anchor decode workspaces, one per
-// device, made on first use and kept, with the blocks it has cached, until the
-// process ends.  The device's default pool hands freed blocks back to the
-// driver at the next synchronisation, and the next hipMalloc on the device then
-// waits for that: about 0.4 ms a decode.  This pool keeps what it has held
-// (the high-water mark of the decode workspaces outstanding at once).
-struct AnchorPool {
-  std::mutex mu;
-  hipMemPool_t pool = nullptr;
-};
-
-int anchor_pool(int dev, hipMemPool_t* out) {
-  static AnchorPool p[kMaxDevices];
-  if (dev < 0 || dev >= kMaxDevices) return fail(CG_E_INVAL, "device index beyond the supported range");
-  std::lock_guard<std::mutex> lock(p[dev].mu);
-  if (!p[dev].pool) {
-    hipMemPoolProps props;
-    memset(&props, 0, sizeof(props));
-    props.allocType = hipMemAllocationTypePinned;
-    props.location.type = hipMemLocationTypeDevice;
-    props.location.id = dev;
-    hipMemPool_t pool = nullptr;
-    HIP_TRY(hipMemPoolCreate(&pool, &props), "hipMemPoolCreate(anchors)");
-    uint64_t keep = UINT64_MAX;
-    const hipError_t e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
-    if (e != hipSuccess) {
-      (void)hipMemPoolDestroy(pool);
-      return hip_fail(e, "hipMemPoolSetAttribute(anchors)");
-    }
-    p[dev].pool = pool;
-  }
-  *out = p[dev].pool;
-  return CG_OK;
-}
-
 // Enqueues the decode of n checked blobs.  Raw anchors are read from the
 // blobs; coded anchors are first decoded into a stream-ordered allocation of
 // 2 L ng C bytes per blob from the device's anchor pool (allocated on st,
@@ -355,7 +364,7 @@ int enqueue_decode(const cg_tables* h, int n, const void* const* blobs, const cg
     bytes += align256((size_t)2 * t.L * infos[i].n_groups * t.C);
   }
   hipMemPool_t pool = nullptr;
-  int rc = anchor_pool(h->dev, &pool);
+  int rc = keep_pool(h->dev, &pool);
   if (rc) return rc;
   int8_t* ws = nullptr;
   HIP_TRY(hipMallocFromPoolAsync((void**)&ws, bytes, pool, st), "hipMallocFromPoolAsync(anchors)");
@@ -541,7 +550,7 @@ int cg_build_tables_grouped(const cg_params* params_in, int32_t grouping, const 
   }
   init_dev_tables(h->t, *params);
   DevTables& t = h->t;
-  if ((rc = alloc_tables(h))) {
+  if ((rc = alloc_tables(h, st))) {
     free_tables(h);
     return rc;
   }
@@ -643,7 +652,7 @@ int cg_tables_deserialize(const void* buf, size_t len, cg_tables** out) {
     return fail(CG_E_HIP, "no HIP device");
   }
   init_dev_tables(h->t, p);
-  if ((rc = alloc_tables(h))) {
+  if ((rc = alloc_tables(h, nullptr))) {
     free_tables(h);
     return rc;
   }
