@@ -706,8 +706,8 @@ constexpr size_t kEncScratchBudget = (size_t)3 << 30;
 // status words (W, too large, non-finite, pad) and their pinned mirror.  A
 // batch holds the mutex until it has synchronised its stream, so batches on
 // one device take turns.  (Allocated per tables handle, the 1 GB of scratch of
-// the Mistral-7B-shape batch cost 0.2 ms of hipMalloc in every step that
-// builds new tables.)
+// an 18-blob Mistral-7B-shape batch cost 0.2 ms of hipMalloc, with the GPU
+// idle, in the first batch on every new tables handle.)
 struct EncWs {
   std::mutex mu;
   uint32_t* scratch = nullptr;
