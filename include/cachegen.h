@@ -287,6 +287,18 @@ typedef struct {
 } cg_chunk_plan_in;
 int cg_plan_chunk(const cg_chunk_plan_in* in, int32_t* quality_out, double* ratio_out);
 
+/* For long-running processes: frees the device memory the library keeps
+ * between calls, on every device it has used — the table-build and encode
+ * workspaces (and their pinned host words), and the blocks its per-device
+ * memory pool has cached that no tables handle or enqueued decode holds (the
+ * blocks in use stay).  Waits for each such device to finish its work first;
+ * calls on other threads that need a workspace wait for it, and the next call
+ * that needs one allocates it again.  The static scratch of
+ * cg_encode_batch_noalloc is not released (it lives until the process ends).
+ * CG_OK, or CG_E_HIP if a device could not be selected, synchronised or its
+ * pool trimmed (the other devices are still released). */
+int cg_release_cached(void);
+
 /* Message of the calling thread's last error ("" if none). */
 const char* cg_last_error(void);
 

@@ -8,7 +8,7 @@ from ._binding import (CG_GROUP_CHANNEL, CG_GROUP_GLOBAL, CG_GROUP_LAYER,  # noq
                        cg_encode_batch, cg_encode_batch_noalloc,
                        cg_encode_bound,
                        cg_chunk_plan_in, cg_last_error, cg_num_chunks, cg_params,
-                       cg_plan_chunk, cg_tables_deserialize,
+                       cg_plan_chunk, cg_release_cached, cg_tables_deserialize,
                        cg_tables_free, cg_tables_id, cg_tables_params, cg_tables_serialize, lib,
                        make_params)
 

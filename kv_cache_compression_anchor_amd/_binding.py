@@ -25,7 +25,7 @@ EXPORTS = ["cg_build_tables", "cg_build_tables_grouped", "cg_tables_free", "cg_t
            "cg_tables_deserialize", "cg_tables_id", "cg_tables_params", "cg_num_chunks", "cg_encode_bound", "cg_encode",
            "cg_encode_batch", "cg_encode_batch_noalloc", "cg_chunk_info_parse", "cg_decode", "cg_decode_async", "cg_decode_paged_async",
            "cg_decode_streamed",
-           "cg_plan_chunk", "cg_last_error"]
+           "cg_plan_chunk", "cg_release_cached", "cg_last_error"]
 
 
 class CgError(RuntimeError):
@@ -91,6 +91,7 @@ def lib():
                                        SZ, P, P, P]),
             "cg_plan_chunk": (I, [C.POINTER(cg_chunk_plan_in), C.POINTER(I32),
                                   C.POINTER(C.c_double)]),
+            "cg_release_cached": (I, []),
             "cg_last_error": (C.c_char_p, []),
         }
         for name, (res, args) in sigs.items():
@@ -359,6 +360,12 @@ def cg_decode_streamed(t: Tables, host_blobs, infos, k_out, v_out, staging, stat
                                     _dev_ptr(staging, torch.uint8, "staging"), staging.numel(),
                                     _dev_ptr(status, torch.int32, "status"),
                                     _stream(copy_stream), _stream(compute_stream)))
+
+
+def cg_release_cached():
+    """Frees the device memory the library keeps between calls (workspaces,
+    cached pool blocks) on every device it has used."""
+    _check(lib().cg_release_cached())
 
 
 def cg_plan_chunk(budget_ms: float, bandwidth_bpms: float, bytes_left, decode_ms_left):

@@ -102,11 +102,16 @@ struct KeepPool {
   hipMemPool_t pool = nullptr;
 };
 
-int keep_pool(int dev, hipMemPool_t* out) {
+KeepPool* keep_pool_of(int dev) {
   static KeepPool p[kMaxDevices];
-  if (dev < 0 || dev >= kMaxDevices) return fail(CG_E_INVAL, "device index beyond the supported range");
-  std::lock_guard<std::mutex> lock(p[dev].mu);
-  if (!p[dev].pool) {
+  return dev >= 0 && dev < kMaxDevices ? &p[dev] : nullptr;
+}
+
+int keep_pool(int dev, hipMemPool_t* out) {
+  KeepPool* p = keep_pool_of(dev);
+  if (!p) return fail(CG_E_INVAL, "device index beyond the supported range");
+  std::lock_guard<std::mutex> lock(p->mu);
+  if (!p->pool) {
     hipMemPoolProps props;
     memset(&props, 0, sizeof(props));
     props.allocType = hipMemAllocationTypePinned;
@@ -120,9 +125,9 @@ int keep_pool(int dev, hipMemPool_t* out) {
       (void)hipMemPoolDestroy(pool);
       return hip_fail(e, "hipMemPoolSetAttribute");
     }
-    p[dev].pool = pool;
+    p->pool = pool;
   }
-  *out = p[dev].pool;
+  *out = p->pool;
   return CG_OK;
 }
 
@@ -1064,3 +1069,51 @@ int cg_decode_streamed(const cg_tables* h, int32_t n, const void* const* blobs_h
 }
 
 }  // extern "C"
+
+// Frees what the library keeps between calls on every device it has used:
+// the table-build and encode workspaces, and the blocks its memory pool has
+// cached but nothing holds.  A device's locks are taken in the order the other
+// calls nest them (a build holds its workspace's lock while it allocates from
+// the pool), then the device is waited for before anything is freed.
+int cg_release_cached(void) {
+  int rc = CG_OK;
+  for (int dev = 0; dev < kMaxDevices; dev++) {
+    BuildWs* b = build_ws(dev);
+    EncWs* e = enc_ws(dev);
+    KeepPool* kp = keep_pool_of(dev);
+    std::unique_lock<std::mutex> lb(b->mu);
+    std::unique_lock<std::mutex> le(e->mu);
+    std::unique_lock<std::mutex> lp(kp->mu);
+    if (!b->dev && !b->host && !e->scratch && !e->lens && !e->row_words && !e->status &&
+        !e->host && !kp->pool)
+      continue;
+    DeviceGuard g(dev);
+    if (!g.ok) {
+      rc = fail(CG_E_HIP, "cannot select device " + std::to_string(dev));
+      continue;
+    }
+    const hipError_t se = hipDeviceSynchronize();
+    if (se != hipSuccess) {
+      rc = hip_fail(se, "release: device synchronize");
+      continue;
+    }
+    if (b->dev) (void)hipFree(b->dev);
+    if (b->host) (void)hipHostFree(b->host);
+    b->dev = nullptr;
+    b->host = nullptr;
+    b->bytes = 0;
+    for (uint32_t** d : {&e->scratch, &e->lens, &e->row_words, &e->status})
+      if (*d) {
+        (void)hipFree(*d);
+        *d = nullptr;
+      }
+    if (e->host) (void)hipHostFree(e->host);
+    e->host = nullptr;
+    e->scratch_bytes = e->lens_bytes = e->row_bytes = e->status_bytes = 0;
+    if (kp->pool) {
+      const hipError_t te = hipMemPoolTrimTo(kp->pool, 0);
+      if (te != hipSuccess) rc = hip_fail(te, "release: pool trim");
+    }
+  }
+  return rc;
+}

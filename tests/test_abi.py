@@ -196,3 +196,8 @@ def test_default_layer_groups_are_resolved_by_the_library(cg):
     p = cg.make_params(48, 64, 128, 64, 10, None, (0.5, 1.0, 1.5))
     assert lib.cg_build_tables(ctypes.byref(p), None, None, None, ctypes.byref(out)) == cg.CG_E_INVAL
     assert "NULL" in cg.cg_last_error()
+
+
+def test_release_cached_without_device_memory_is_a_no_op(cg):
+    # nothing allocated in this process: no HIP call is made, CG_OK
+    assert cg.lib().cg_release_cached() == cg.CG_OK

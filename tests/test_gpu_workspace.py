@@ -8,6 +8,7 @@ built again in a loop keep giving the oracle's bytes (the pool hands freed
 blocks back)."""
 import threading
 
+import numpy as np
 import pytest
 
 import oracle
@@ -89,3 +90,30 @@ def test_tables_built_and_freed_in_a_loop():
                                           kd.cpu().numpy(), vd.cpu().numpy())
                 assert got == ot1, (rep, gu.first_difference(got, ot1))
             cg.cg_tables_free(tab)
+
+
+def test_release_cached_then_work_again():
+    """cg_release_cached frees the workspaces and trims the pool; the next
+    build, encode and coded-anchor decode allocate again and still give the
+    oracle's bytes."""
+    import kv_cache_compression_anchor_amd as cg
+    w = gu.workload(tokens=900, channels=130, chunk_tokens=300)
+    k, v = synth.gen_kv(w)
+    kd, vd = gu.to_dev(k), gu.to_dev(v)
+    ot = oracle.build_tables(oracle.params_for(w, anchor_coding=1), k, v)
+    jobs = [(c, q) for c in range(w.n_chunks) for q in w.qualities]
+    want = [oracle.encode_chunk(ot, k, v, c, q) for c, q in jobs]
+    for rep in range(3):
+        tab = gu.gpu_tables(w, kd, vd, anchor_coding=1)
+        assert cg.cg_tables_serialize(tab) == ot
+        got = _batch(tab, kd, vd, jobs)
+        assert got == want, rep
+        # one blob per chunk (qualities in turn), so no two write the same rows
+        sel = [jobs.index((c, w.qualities[c % len(w.qualities)])) for c in range(w.n_chunks)]
+        dev = [gu.to_dev(np.frombuffer(got[i], dtype=np.uint8).copy()) for i in sel]
+        kg, vg, st = gu.gpu_decode(tab, dev, k.shape)
+        ko, vo, bad = gu.oracle_decode(ot, [want[i] for i in sel], k.shape)
+        assert st == 0 and not bad
+        assert gu.same_bits(kg, ko) and gu.same_bits(vg, vo)
+        cg.cg_release_cached()
+        cg.cg_tables_free(tab)
