@@ -19,17 +19,17 @@ __device__ __forceinline__ int quant_anchor(float x, float inv_a) {
   return (int)r;
 }
 
-// the delta's level in -32 .. 31 (the symbol minus 32)
-__device__ __forceinline__ int quant_delta_level(float x, float ahat, float inv_step) {
-  float d = x - ahat;
-  float u = d * inv_step;
-  float r = __builtin_rintf(u);
-  r = __builtin_amdgcn_fmed3f(r, -32.0f, 31.0f);
-  return (int)r;
-}
-
-__device__ __forceinline__ uint32_t quant_delta(float x, float ahat, float inv_step) {
-  return (uint32_t)(quant_delta_level(x, ahat, inv_step) + 32);
+// The delta's level rint(u) clamped to [-32, 31], u = (x - ahat) * inv_step,
+// returned as the binary32 bits of u + 1.5 2^23 clamped to
+// [kLevelBias - 32, kLevelBias + 31] (level = bits - kLevelBias): for
+// |u| < 2^22 the sum is 1.5 2^23 + rint(u) exactly (its ulp is 1, and rounding
+// to even agrees because 1.5 2^23 is even); beyond that the bits still order
+// as u does (a negative sum has negative bits), so clamping the bits clamps
+// the level.  One add and one v_med3_i32 instead of rint, a clamp and a
+// conversion; callers fold the bias into their table or counter addresses.
+constexpr int32_t kLevelBias = 0x4B400000;
+__device__ __forceinline__ int32_t level_bits(float u) {
+  return min(max(__builtin_bit_cast(int32_t, u + 12582912.0f), kLevelBias - 32), kLevelBias + 31);
 }
 
 struct StatsBuf {

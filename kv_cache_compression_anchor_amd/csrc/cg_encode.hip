@@ -209,7 +209,6 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
       (void*)((kv ? a.v : a.k) + ((size_t)l * a.T + B.t0) * a.C), 0,
       (int)((uint32_t)B.tc * row_bytes), kBufRsrcWord3);
   const uint32_t lane_off = 2u * (uint32_t)c;
-  const uint8_t* tb = reinterpret_cast<const uint8_t*>(tab) + 2 * lane_slot(lane);
   // the wave's block of 64 streams in scratch, [swb rows][64 lanes], row 0
   // holding the placeholders
   Sink o;
@@ -226,6 +225,11 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
   RcEnc e = {0, 0u, 0xFFFFFFFFu, 0u, 0u};
   uint32_t nonfinite = 0;
 
+  // a delta's table row as a byte offset: (level + 32) * 128 + the lane's
+  // column, level + 32 = level_bits(u) - (kLevelBias - 32)
+  const uint32_t row0 = (uint32_t)(2 * lane_slot(lane)) - ((uint32_t)(kLevelBias - 32) << 7);
+  const uint8_t* tab8 = reinterpret_cast<const uint8_t*>(tab);
+
   // one group from its tokens' binary16 bits: the anchor, then the deltas
   auto code_group = [&](int g, int n, auto half_of) {
     const uint32_t ha = half_of(0);
@@ -236,9 +240,9 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
     for (int j = 1; j < n; j++) {
       const uint32_t hx = half_of(j);
       nonfinite |= (hx & 0x7C00u) == 0x7C00u;
-      const uint32_t s = quant_delta(half_bits_to_float(hx), ahat, inv_step);
-      const uint32_t c0 = *reinterpret_cast<const uint16_t*>(tb + s * (2 * kLanes));
-      const uint32_t c1 = *reinterpret_cast<const uint16_t*>(tb + (s + 1) * (2 * kLanes));
+      const uint32_t off = ((uint32_t)level_bits((half_bits_to_float(hx) - ahat) * inv_step) << 7) + row0;
+      const uint32_t c0 = *reinterpret_cast<const uint16_t*>(tab8 + off);
+      const uint32_t c1 = *reinterpret_cast<const uint16_t*>(tab8 + off + 2 * kLanes);
       rc_put(e, c0, c1 - c0, o);
     }
   };

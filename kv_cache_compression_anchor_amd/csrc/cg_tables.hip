@@ -210,18 +210,13 @@ __global__ __launch_bounds__(256) void k_histogram(HistArgs a) {
     auto ld = [&](int t) -> uint32_t {
       return __builtin_amdgcn_raw_buffer_load_b16(xin, lane_off, (uint32_t)t * row_bytes, 0);
     };
-    // The delta's level rint(u) clamped to [-32, 31], from the bits of
-    // u + 1.5 2^23: for |u| < 2^22 the sum is 1.5 2^23 + rint(u) exactly (its
-    // ulp is 1, and rounding to even agrees because 1.5 2^23 is even); beyond
-    // that the bits still order as u does (a negative sum has negative bits),
-    // so clamping the bits clamps the level.  A count's byte address is
-    // bits * 256 plus the slot column's address less 0x4B400000 * 256.
-    constexpr int32_t kMagic = 0x4B400000;
-    const uint32_t at0 = (uint32_t)(32 * kLanes + lane) * 4u - ((uint32_t)kMagic << 8);
+    // a count's byte address: level * 256 plus the slot column's address of
+    // level 0, level = level_bits(u) - kLevelBias
+    const uint32_t at0 = (uint32_t)(32 * kLanes + lane) * 4u - ((uint32_t)kLevelBias << 8);
     const uint32_t at1 = at0 + kNSym * kLanes * 4u, at2 = at1 + kNSym * kLanes * 4u;
     auto count = [&](uint32_t at, float u) {
-      const int32_t bits = min(max(__builtin_bit_cast(int32_t, u + 12582912.0f), kMagic - 32), kMagic + 31);
-      atomicAdd(reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(hist) + (((uint32_t)bits << 8) + at)), 1u);
+      atomicAdd(reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(hist) +
+                                            (((uint32_t)level_bits(u) << 8) + at)), 1u);
     };
     auto group = [&](int n, auto half_of) {
       const int av = quant_anchor(half_bits_to_float(half_of(0)), inv_a);

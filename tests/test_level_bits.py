@@ -1,12 +1,11 @@
-"""The table builder's histogram takes a delta's level rint(u) clamped to
-[-32, 31] from the bits of the binary32 sum u + 1.5 * 2^23, clamped to
-[0x4B400000 - 32, 0x4B400000 + 31] (csrc/cg_tables.hip, k_histogram).  The
-encoder takes it the plain way, rint then clamp (csrc/cg_build.h,
-quant_delta_level), and the two must agree for every binary32 u, or the
-frequency tables would count other symbols than the encoder codes.  This checks
-the identity on the CPU in binary32 arithmetic: exhaustively around every
-half-integer tie in range, over a sweep of magnitudes from subnormals to the
-largest finite values, and at the infinities."""
+"""The kernels take a delta's level rint(u) clamped to [-32, 31] from the bits
+of the binary32 sum u + 1.5 * 2^23, clamped to [0x4B400000 - 32,
+0x4B400000 + 31] (csrc/cg_build.h, level_bits; the histogram and the encoder
+both use it).  The oracle takes it the plain way, rint then clamp, and the two
+must agree for every binary32 u.  This checks the identity on the CPU in
+binary32 arithmetic: exhaustively around every half-integer tie in range, over
+a sweep of magnitudes from subnormals to the largest finite values, and at the
+infinities."""
 import numpy as np
 
 MAGIC = 0x4B400000
