@@ -471,6 +471,9 @@ void init_enc_args(EncodeArgs& a, const cg_tables* h, const void* k_dev, const v
   a.rows_total = coded_anchors(t) ? 4 * t.L : 2 * t.L;
   a.afreq = coded_anchors(t) ? reinterpret_cast<const uint16_t*>(t.ser + t.lay.off_afreq) : nullptr;
   a.waves = 1;
+  int cus = 0;
+  a.ncu = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->dev) == hipSuccess && cus > 0
+              ? cus : 1;
 }
 
 // out_lens[i] and the call's result from blob i's status words {payload words,

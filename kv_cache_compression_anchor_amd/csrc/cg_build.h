@@ -32,6 +32,19 @@ __device__ __forceinline__ int32_t level_bits(float u) {
   return min(max(__builtin_bit_cast(int32_t, u + 12582912.0f), kLevelBias - 32), kLevelBias + 31);
 }
 
+// The anchor's code quant_anchor(x, inv_a) the same way: the bits of
+// x inv_a + 1.5 2^23 clamped to kLevelBias -+ 127, equal to kLevelBias + the
+// code for every finite x.  The low byte of the bits is the code's
+// two's-complement byte (kLevelBias has a zero low byte), and anchor_of_bits
+// gives the code as a binary32 exactly.
+__device__ __forceinline__ int32_t anchor_bits(float x, float inv_a) {
+  return min(max(__builtin_bit_cast(int32_t, x * inv_a + 12582912.0f), kLevelBias - 127),
+             kLevelBias + 127);
+}
+__device__ __forceinline__ float anchor_of_bits(int32_t b) {
+  return __builtin_bit_cast(float, b) - 12582912.0f;
+}
+
 struct StatsBuf {
   uint64_t* s1;    // sum of X = x*2^24 (two's complement)
   uint64_t* sa;    // sum over workgroups of (their sum of X^2) >> 40
@@ -103,6 +116,7 @@ struct EncodeArgs {
   uint64_t tables_id;
   EncGroup groups[kEncMaxBlobs];
   EncBlob b[kEncMaxBlobs];
+  int ncu;  // compute units: workgroups ncu apart in launch order share one
 };
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t st);
 // zeroes n words at p on st (a kernel, so that the clearing also works where

@@ -20,10 +20,11 @@ namespace {
 // (no carry can reach past the first word).
 struct RcEnc {
   uint64_t L;      // window (bits 0..31) and the bytes above it (bits 32..32+kh-1)
-  uint32_t kh;     // 8 * bytes above the window: 0..24
+  uint32_t kh;     // 8 * bytes above the window: 0..24; plus 64 while P != 0
   uint32_t range;
   uint32_t W;      // last word taken out of L, not final yet
   uint32_t P;      // 0xFFFFFFFF words after W, not final yet
+  uint32_t Y;      // 0 while P != 0, else 0xFFFFFFFF
 };
 
 // A lane's output words, through a buffer resource over the wave's 64 streams,
@@ -94,7 +95,10 @@ __device__ __forceinline__ void shift_bytes(RcEnc& e, uint32_t nb8, Sink& o) {
 // The common case (no all-ones run open, and no all-ones word taken) runs
 // branch-free for the whole wave; a lane in a rare case redoes the symbol from
 // its previous state with the general steps, in a branch the wave takes only
-// when some lane needs it.
+// when some lane needs it.  A lane with a run open always takes that branch:
+// its kh carries bit 6, so kh + nb8 >= 32 (shifts and bit-field widths read
+// only the low five bits of kh), and its Y is 0, so wn >= Y; then "a word
+// leaves and it is all ones, or a run is open" is one compare pair.
 __device__ __forceinline__ void rc_put(RcEnc& e, uint32_t c0, uint32_t freq, Sink& o) {
   const RcEnc e0 = e;
   const uint32_t r = e.range >> kProbBits;
@@ -102,34 +106,43 @@ __device__ __forceinline__ void rc_put(RcEnc& e, uint32_t c0, uint32_t freq, Sin
   const uint32_t lo = (uint32_t)L1, hx = (uint32_t)(L1 >> 32);
   // the held bytes are below 2^kh and r c0 below 2^32, so the carry out of
   // them is bit kh of hx, and nothing above it
-  const uint32_t cy = hx >> e.kh;
+  const uint32_t cy = hx >> (e.kh & 31u);
   const uint32_t rn = mul24(r, freq);
   const uint32_t nb8 = (uint32_t)__builtin_clz(rn) & 24u;  // renormalise while range < 2^24
   const uint32_t kh2 = e.kh + nb8;
-  const bool ext = kh2 >= 32u;
   // the four top bytes of the window and held bytes (the carry bit lies above)
   const uint32_t wn = __builtin_amdgcn_alignbit(hx, lo, e.kh);
-  const bool open = e.P != 0u;
-  const bool rare = (ext & (open | (wn == 0xFFFFFFFFu))) | (open & (cy != 0u));
+  // lane masks of "a word leaves" and "it is all ones or a run is open": the
+  // rare lanes are both, the emitting lanes the first only (as masks, so that
+  // each compare is made once)
+  const uint64_t m_ext = __builtin_amdgcn_ballot_w64(kh2 >= 32u);
+  const uint64_t m_ge = __builtin_amdgcn_ballot_w64(wn >= e.Y);
+  const bool rare = __builtin_amdgcn_inverse_ballot_w64(m_ext & m_ge);
   const uint32_t W1 = e.W + cy;
-  const bool emit = ext && !rare;
-  if (emit) __builtin_amdgcn_raw_buffer_store_b32(W1, o.rs, o.woff, 0, 0);
-  o.woff += emit ? kRowBytes : 0u;
+  const bool emit = __builtin_amdgcn_inverse_ballot_w64(m_ext & ~m_ge);
+  if (emit) {
+    __builtin_amdgcn_raw_buffer_store_b32(W1, o.rs, o.woff, 0, 0);
+    // the slot after it (in place, after the store has read the old offset)
+    asm("v_add_u32 %0, 0x100, %0" : "+v"(o.woff));
+  }
   e.W = emit ? wn : W1;
   // shifted by nb8, L keeps its low 32 + (kh2 mod 32) bits: without a word
   // leaving that is all of it less the carry; with one, the window's low kh
   // bits, moved up
   const uint64_t Ls = L1 << nb8;
-  e.kh = kh2 & 31u;
+  e.kh = kh2 & 95u;  // mod 32, keeping bit 6 (an open run's lanes take the branch below)
   e.L = ((uint64_t)__builtin_amdgcn_ubfe((uint32_t)(Ls >> 32), 0u, e.kh) << 32) | (uint32_t)Ls;
   e.range = rn << nb8;
   if (rare) {
     RcEnc s = e0;
+    s.kh &= 31u;
     s.L = L1;
     settle_carry(s, o);
     s.range = rn << nb8;
     shift_bytes(s, nb8, o);
     e = s;
+    e.kh |= s.P != 0u ? 64u : 0u;
+    e.Y = s.P != 0u ? 0u : 0xFFFFFFFFu;
   }
 }
 
@@ -137,6 +150,7 @@ __device__ __forceinline__ void rc_put(RcEnc& e, uint32_t c0, uint32_t freq, Sin
 // [low, low + range), so the stream decodes whatever bytes follow it; then the
 // open words and the bytes still held, the last word padded with zero bytes.
 __device__ __forceinline__ void rc_finish(RcEnc& e, Sink& o) {
+  e.kh &= 31u;
   const uint64_t win = e.L & 0xFFFFFFFFull;
   uint32_t nb8 = 8;
   uint64_t V = (win + 0xFFFFFFull) & ~0xFFFFFFull;
@@ -180,9 +194,19 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int per_grp = a.nrows * a.nblk;
   const int grp = blockIdx.x / per_grp, unit = blockIdx.x % per_grp;
-  const int rrel = unit / a.nblk;  // row within the launch's range
-  const int row = a.row0 + rrel;   // kv * L + l
-  const int cb = unit % a.nblk;
+  // The workgroups that share a compute unit are ncu apart in launch order,
+  // and a stream's cost grows with its bits per symbol: finer steps (shallow
+  // layers) and outlier channels cost more.  So that each compute unit gets a
+  // mix, the second half of the launch's rows is taken in reverse order (the
+  // V rows of a whole-row launch: deep layers beside the K rows' shallow ones)
+  // and the blocks of a row are rotated by 5 per ncu workgroups (neighbouring
+  // rows on one compute unit take different channel blocks).  The map is one
+  // to one on the units of the launch.
+  const int prow = unit / a.nblk, pcb = unit % a.nblk;
+  const int half = a.nrows >> 1;
+  const int rrel = prow >= half ? half + (a.nrows - 1 - prow) : prow;  // row within the launch's range
+  const int row = a.row0 + rrel;  // kv * L + l
+  const int cb = (pcb + 5 * ((prow * a.nblk) / a.ncu)) % a.nblk;
   const EncGroup eg = a.groups[grp];
   {
     const uint32_t* src = reinterpret_cast<const uint32_t*>(
@@ -217,13 +241,16 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
                                            (int)(kRowBytes * (uint32_t)a.swb), kBufRsrcWord3);
   o.woff = 4u * (uint32_t)lane;
   const uint32_t woff0 = o.woff + kRowBytes;  // the stream's first word
-  // raw anchors into the blob; coded anchors are coded from the input by
-  // k_anchor_encode instead (a wave-uniform choice)
+  // raw anchors into the blob, [ng][C] for this (kv, layer): the lane's
+  // channel is the vector offset, the group a scalar offset; coded anchors are
+  // coded from the input by k_anchor_encode instead (a wave-uniform choice)
   const bool raw_anchors = B.lay.off_anchor != 0;
-  int8_t* anchors = reinterpret_cast<int8_t*>(B.blob + B.lay.off_anchor) +
-                    ((size_t)kv * a.L + l) * B.ng * a.C + c;
-  RcEnc e = {0, 0u, 0xFFFFFFFFu, 0u, 0u};
-  uint32_t nonfinite = 0;
+  const __amdgpu_buffer_rsrc_t anc = __builtin_amdgcn_make_buffer_rsrc(
+      B.blob + B.lay.off_anchor + ((size_t)kv * a.L + l) * B.ng * a.C, 0,
+      (int)((uint32_t)B.ng * (uint32_t)a.C), kBufRsrcWord3);
+  RcEnc e = {0, 0u, 0xFFFFFFFFu, 0u, 0u, 0xFFFFFFFFu};
+  // sum of 0 x every input: zero unless some input is infinite or NaN
+  float nfacc = 0.0f;
 
   // a delta's table row as a byte offset: (level + 32) * 128 + the lane's
   // column, level + 32 = level_bits(u) - (kLevelBias - 32)
@@ -232,15 +259,16 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
 
   // one group from its tokens' binary16 bits: the anchor, then the deltas
   auto code_group = [&](int g, int n, auto half_of) {
-    const uint32_t ha = half_of(0);
-    nonfinite |= (ha & 0x7C00u) == 0x7C00u;
-    const int av = quant_anchor(half_bits_to_float(ha), inv_a);
-    if (raw_anchors) anchors[(size_t)g * a.C] = (int8_t)av;
-    const float ahat = anchor_value(av, scale_a);
+    const float x0 = half_bits_to_float(half_of(0));
+    nfacc = __builtin_fmaf(x0, 0.0f, nfacc);
+    const int32_t ab = anchor_bits(x0, inv_a);
+    if (raw_anchors)
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)ab, anc, (uint32_t)c, (uint32_t)g * (uint32_t)a.C, 0);
+    const float ahat = anchor_of_bits(ab) * scale_a;  // anchor_value of the code
     for (int j = 1; j < n; j++) {
-      const uint32_t hx = half_of(j);
-      nonfinite |= (hx & 0x7C00u) == 0x7C00u;
-      const uint32_t off = ((uint32_t)level_bits((half_bits_to_float(hx) - ahat) * inv_step) << 7) + row0;
+      const float xf = half_bits_to_float(half_of(j));
+      nfacc = __builtin_fmaf(xf, 0.0f, nfacc);
+      const uint32_t off = ((uint32_t)level_bits((xf - ahat) * inv_step) << 7) + row0;
       const uint32_t c0 = *reinterpret_cast<const uint16_t*>(tab8 + off);
       const uint32_t c1 = *reinterpret_cast<const uint16_t*>(tab8 + off + 2 * kLanes);
       rc_put(e, c0, c1 - c0, o);
@@ -289,7 +317,7 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
                [&](int j) { return ld_half(xin, lane_off, (uint32_t)(ta + j) * row_bytes); });
   }
   if (B.tc > B.ng) rc_finish(e, o);  // a stream without symbols stays empty
-  if (nonfinite) atomicOr(&B.status[2], 1u);
+  if (!(nfacc == 0.0f)) atomicOr(&B.status[2], 1u);
   const uint32_t nwords = o.woff > woff0 ? (o.woff - woff0) / kRowBytes : 0u;
   B.lens[(size_t)rrel * a.C + c] = nwords;
   reinterpret_cast<uint16_t*>(B.blob + B.lay.off_len)[pi] = (uint16_t)nwords;
@@ -349,7 +377,7 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_anchor_encode(EncodeA
                                            (int)(kRowBytes * (uint32_t)a.swb), kBufRsrcWord3);
   o.woff = 4u * (uint32_t)lane;
   const uint32_t woff0 = o.woff + kRowBytes;
-  RcEnc e = {0, 0u, 0xFFFFFFFFu, 0u, 0u};
+  RcEnc e = {0, 0u, 0xFFFFFFFFu, 0u, 0u, 0xFFFFFFFFu};
   const uint32_t gstep = (uint32_t)a.G * row_bytes;
   // anchor tokens in batches of kAB, loaded one batch ahead (a batch past the
   // last group re-reads the last group, inside the chunk)
