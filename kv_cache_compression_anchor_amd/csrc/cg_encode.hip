@@ -433,50 +433,64 @@ __global__ __launch_bounds__(256) void k_row_totals(EncodeArgs a) {
 }
 
 // per blob: offsets of the range's rows, continuing from the words of the rows
-// coded before; flags a blob whose words so far do not fit cap (the range's
-// packing is then skipped, and so is every later one); the launch that ends
-// the rows writes the header
-__global__ void k_row_scan(EncodeArgs a) {
-  if (threadIdx.x != 0) return;
+// coded before (a wavefront prefix sum, 64 rows at a time); flags a blob whose
+// words so far do not fit cap (the range's packing is then skipped, and so is
+// every later one); the launch that ends the rows writes the header and zeroes
+// the padding (the gap before the payload and the tail after it)
+__global__ __launch_bounds__(256) void k_row_scan(EncodeArgs a) {
+  __shared__ uint32_t s_words, s_fits;
   const EncBlob& B = a.b[blockIdx.x];
-  uint32_t* row_off = reinterpret_cast<uint32_t*>(B.blob + B.lay.off_rows);
-  uint64_t w = B.status[0];
-  for (int r = 0; r < a.nrows; r++) {
-    row_off[a.row0 + r] = (uint32_t)w;
-    w += B.row_words[r];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const bool last = a.row0 + a.nrows == a.rows_total;
+  if (tid < kLanes) {
+    uint32_t* row_off = reinterpret_cast<uint32_t*>(B.blob + B.lay.off_rows);
+    uint64_t w = B.status[0];
+    for (int r0 = 0; r0 < a.nrows; r0 += kLanes) {
+      const int r = r0 + lane;
+      const uint32_t rw = r < a.nrows ? B.row_words[r] : 0u;
+      uint64_t incl = rw;
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint64_t y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      if (r < a.nrows) row_off[a.row0 + r] = (uint32_t)(w + incl - rw);
+      w += __shfl(incl, 63);
+    }
+    if (lane == 0) {
+      const size_t total = blob_bytes(B.lay, w);
+      const bool fits = total <= B.cap && w <= 0x3FFFFFFFull;
+      B.status[0] = (uint32_t)w;
+      if (!fits) B.status[1] = 1u;
+      s_words = (uint32_t)w;
+      s_fits = fits && B.status[1] == 0u ? 1u : 0u;
+      if (last) {
+        uint32_t* h = reinterpret_cast<uint32_t*>(B.blob);
+        h[0] = kBlobMagic;
+        h[1] = B.lay.off_anchor ? kBlobVersion : kBlobVersionCoded;
+        h[2] = (uint32_t)a.L;
+        h[3] = (uint32_t)a.C;
+        h[4] = (uint32_t)a.T;
+        h[5] = (uint32_t)B.t0;
+        h[6] = (uint32_t)B.tc;
+        h[7] = (uint32_t)a.G;
+        h[8] = (uint32_t)B.ng;
+        h[9] = (uint32_t)B.q;
+        h[10] = (uint32_t)w;
+        h[11] = kProbBits;
+        h[12] = (uint32_t)a.tables_id;
+        h[13] = (uint32_t)(a.tables_id >> 32);
+        h[14] = 0;
+        h[15] = 0;
+      }
+    }
   }
-  const size_t total = blob_bytes(B.lay, w);
-  B.status[0] = (uint32_t)w;
-  if (total > B.cap || w > 0x3FFFFFFFull) B.status[1] = 1u;
-  if (a.row0 + a.nrows != a.rows_total) return;
-  uint32_t* h = reinterpret_cast<uint32_t*>(B.blob);
-  h[0] = kBlobMagic;
-  h[1] = B.lay.off_anchor ? kBlobVersion : kBlobVersionCoded;
-  h[2] = (uint32_t)a.L;
-  h[3] = (uint32_t)a.C;
-  h[4] = (uint32_t)a.T;
-  h[5] = (uint32_t)B.t0;
-  h[6] = (uint32_t)B.tc;
-  h[7] = (uint32_t)a.G;
-  h[8] = (uint32_t)B.ng;
-  h[9] = (uint32_t)B.q;
-  h[10] = (uint32_t)w;
-  h[11] = kProbBits;
-  h[12] = (uint32_t)a.tables_id;
-  h[13] = (uint32_t)(a.tables_id >> 32);
-  h[14] = 0;
-  h[15] = 0;
-}
-
-// zero the gap before the payload and the tail after it
-__global__ __launch_bounds__(256) void k_pad(EncodeArgs a) {
-  const EncBlob& B = a.b[blockIdx.x];
-  if (B.status[1]) return;
-  const size_t W = B.status[0];
+  __syncthreads();
+  if (!last || !s_fits) return;
+  const size_t W = s_words;
   const size_t gap0 = B.lay.off_len + 2 * (size_t)B.lay.rows * a.C, gap1 = B.lay.off_pay;
   const size_t tail0 = B.lay.off_pay + 4 * W, tail1 = blob_bytes(B.lay, W);
-  for (size_t j = gap0 + threadIdx.x; j < gap1; j += 256) B.blob[j] = 0;
-  for (size_t j = tail0 + threadIdx.x; j < tail1; j += 256) B.blob[j] = 0;
+  for (size_t j = gap0 + tid; j < gap1; j += 256) B.blob[j] = 0;
+  for (size_t j = tail0 + tid; j < tail1; j += 256) B.blob[j] = 0;
 }
 
 // Pack one 64-stream block into the payload layout: its payload offset is the
@@ -553,8 +567,7 @@ hipError_t launch_encode(const EncodeArgs& a, hipStream_t st) {
   else
     k_encode<0><<<blocks, kLanes * a.waves, 0, st>>>(a);
   k_row_totals<<<dim3(a.nrows, nb), 256, 0, st>>>(a);
-  k_row_scan<<<nb, 64, 0, st>>>(a);
-  if (a.row0 + a.nrows == a.rows_total) k_pad<<<nb, 256, 0, st>>>(a);
+  k_row_scan<<<nb, 256, 0, st>>>(a);
   k_pack<<<dim3(a.nrows * a.nblk, nb), 256, 0, st>>>(a);
   return hipGetLastError();
 }
