@@ -425,15 +425,16 @@ int check_encode_args(const cg_tables* h, const void* k_dev, const void* v_dev, 
   return CG_OK;
 }
 
-// Scratch words of one stream: its worst-case words plus the placeholder word
-// in front of them (every chunk of the tables fits the longest chunk's bound).
+// Scratch words of one stream: its worst-case words in whole 16-byte units
+// (every chunk of the tables fits the longest chunk's bound).
 size_t stream_scratch_words(const DevTables& t) {
-  return std::max<size_t>(stream_words_bound(t.CH - (t.CH + t.G - 1) / t.G), 1) + 1;
+  return (std::max<size_t>(stream_words_bound(t.CH - (t.CH + t.G - 1) / t.G), 1) + 3) & ~(size_t)3;
 }
 
 // the same for an anchor stream (one symbol per group), 0 without coded anchors
 size_t anchor_scratch_words(const DevTables& t) {
-  return coded_anchors(t) ? std::max<size_t>(stream_words_bound((t.CH + t.G - 1) / t.G), 1) + 1 : 0;
+  return coded_anchors(t) ? (std::max<size_t>(stream_words_bound((t.CH + t.G - 1) / t.G), 1) + 3) & ~(size_t)3
+                          : 0;
 }
 
 // The fields of one blob of an encode launch, but for its scratch buffers.
@@ -471,9 +472,12 @@ void init_enc_args(EncodeArgs& a, const cg_tables* h, const void* k_dev, const v
   a.rows_total = coded_anchors(t) ? 4 * t.L : 2 * t.L;
   a.afreq = coded_anchors(t) ? reinterpret_cast<const uint16_t*>(t.ser + t.lay.off_afreq) : nullptr;
   a.waves = 1;
-  int cus = 0;
+  int cus = 0, lds = 0;
   a.ncu = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->dev) == hipSuccess && cus > 0
               ? cus : 1;
+  a.lds_cu = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, h->dev) ==
+                     hipSuccess && lds > 0
+                 ? lds : 65536;
 }
 
 // out_lens[i] and the call's result from blob i's status words {payload words,

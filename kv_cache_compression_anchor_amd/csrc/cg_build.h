@@ -85,7 +85,7 @@ struct EncBlob {
   const uint16_t* img;       // cum images of quality q
   const float* inv_step;     // of quality q
   // per launch, for the launch's rows [row0, row0 + nrows) of the blob's payload rows:
-  uint32_t* scratch;         // per 64-stream block: [swb rows][64 lanes] words, row 0 placeholders
+  uint32_t* scratch;         // per 64-stream block: [swb / 4 units][64 lanes][4 words]
   uint32_t* lens;            // [nrows][C] words
   uint32_t* row_words;       // [nrows]
   uint32_t* block_words;     // [nrows][nblk] words of each 64-stream block
@@ -109,14 +109,15 @@ struct EncodeArgs {
   // one that ends at rows_total (2L, or 4L with coded anchors) also writes the
   // header and the padding
   int row0, nrows, rows_total;
-  size_t swb;                // scratch rows per stream of this launch's rows
+  size_t swb;                // scratch words per stream of this launch's rows (a multiple of 4)
   const uint16_t* afreq;     // [2][L][256] anchor tables (coded anchors), else null
   const float* scale_a;
   const float* inv_a;
   uint64_t tables_id;
   EncGroup groups[kEncMaxBlobs];
   EncBlob b[kEncMaxBlobs];
-  int ncu;  // compute units: workgroups ncu apart in launch order share one
+  int ncu;     // compute units: workgroups ncu apart in launch order share one
+  int lds_cu;  // LDS bytes of a compute unit
 };
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t st);
 // zeroes n words at p on st (a kernel, so that the clearing also works where

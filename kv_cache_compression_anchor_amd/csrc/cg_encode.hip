@@ -27,27 +27,105 @@ struct RcEnc {
   uint32_t Y;      // 0 while P != 0, else 0xFFFFFFFF
 };
 
-// A lane's output words, through a buffer resource over the wave's 64 streams,
-// which lie interleaved word by word ([row][lane]): the lanes of a wave emit at
-// similar rates, so the 64 streams' current words share a few cache lines
-// instead of holding 64 lines partly written.  `woff` is the byte offset of
-// W's slot; a word's successor is one row (256 bytes) further.
-constexpr uint32_t kRowBytes = 4u * kLanes;
+// A lane's output words go to a staging ring in LDS of RW = 4 or 8 words per
+// lane ([slot][64 lanes], RW x 256 bytes per wave and aligned to that, so slot
+// k of the lane is at base | 256 k and the lanes' words of one emission are
+// conflict-free), and each completed 16-byte unit (words 4u .. 4u + 3) is
+// written to the wave's scratch block, laid out [unit][64 lanes][4 words], with
+// one store: a quarter of the stores of writing words one by one, each lane's
+// 16 bytes in one cache line where single words of 64 lanes at different
+// positions touched up to 64 lines per store.  Word w of the stream is
+// emission w + 1 (emission 0 is the placeholder W starts as, which lands in
+// the ring's last slot and is never written out).
+constexpr uint32_t kUnitRowBytes = 16u * kLanes;  // one unit of each of the 64 streams
+template <int RW>
 struct Sink {
-  __amdgpu_buffer_rsrc_t rs;
-  uint32_t woff;
+  static_assert(RW == 4 || RW == 8, "a ring of one or two units");
+  static constexpr uint32_t smask = 256u * (RW - 1);     // the slot bits of sa
+  static constexpr uint32_t umask = 1024u * (RW / 4 - 1);  // the bit of uoff that is the unit's half of the ring
+  __amdgpu_buffer_rsrc_t rs;  // the wave's scratch block
+  uint32_t base;   // LDS byte address of the lane's slot 0
+  uint32_t sa;     // 256 (emissions + 7): the next slot is (sa >> 8) mod RW
+  uint32_t fnext;  // sa once the next unit to write out is complete: 256 (12 + 4 u)
+  uint32_t uoff;   // scratch byte offset of that unit: 1024 u + 16 lane
 };
 
-__device__ __forceinline__ void emit_word(Sink& o, uint32_t w) {
-  __builtin_amdgcn_raw_buffer_store_b32(w, o.rs, o.woff, 0, 0);
-  o.woff += kRowBytes;
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(3))) T* lds_ptr(uint32_t byte_addr) {
+  return reinterpret_cast<__attribute__((address_space(3))) T*>(static_cast<uintptr_t>(byte_addr));
 }
+
+// the next word into the ring
+template <class S>
+__device__ __forceinline__ void stage_word(S& o, uint32_t w) {
+  *lds_ptr<uint32_t>(o.base | (o.sa & S::smask)) = w;
+  asm("v_add_u32 %0, 0x100, %0" : "+v"(o.sa));  // in place, after the address is formed
+}
+
+// writes the unit at fnext out of the ring (with 8 slots, slot bit 2 of its
+// words is u & 1, which is bit 10 of uoff)
+template <class S>
+__device__ __forceinline__ void write_unit(S& o) {
+  const uint32_t a = o.base | (o.uoff & S::umask);
+  const uint32_t w0 = *lds_ptr<uint32_t>(a), w1 = *lds_ptr<uint32_t>(a + 256u);
+  const uint32_t w2 = *lds_ptr<uint32_t>(a + 512u), w3 = *lds_ptr<uint32_t>(a + 768u);
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = {w0, w1, w2, w3};
+  __builtin_amdgcn_raw_buffer_store_b128(v, o.rs, o.uoff, 0, 0);
+  o.uoff += kUnitRowBytes;
+  o.fnext += 1024u;
+}
+
+// the lanes whose next unit is complete write it out (at most one: callers
+// flush before more than RW - 3 words have been staged since the last flush)
+template <class S>
+__device__ __forceinline__ void flush_units(S& o) {
+  if (o.sa >= o.fnext) write_unit(o);
+}
+
+// one word of the general steps: staged and, once its unit is complete,
+// written out at once (they may take several words in one symbol)
+template <class S>
+__device__ __forceinline__ void emit_word(S& o, uint32_t w) {
+  stage_word(o, w);
+  flush_units(o);
+}
+
+// the last, partial unit (its other slots hold stale words, which nothing reads)
+template <class S>
+__device__ __forceinline__ void flush_tail(S& o) {
+  if (o.sa > o.fnext - 1024u) write_unit(o);
+}
+
+// words of the stream taken so far
+template <class S>
+__device__ __forceinline__ uint32_t sink_words(const S& o) {
+  return o.sa >= 2048u ? (o.sa >> 8) - 8u : 0u;
+}
+
+// a lane's sink over the wave's scratch block (swb words per stream) and its
+// column of the wave's ring (LDS byte address ring, RW x 256 aligned)
+template <int RW>
+__device__ __forceinline__ Sink<RW> make_sink(uint32_t* block, size_t swb, uint32_t ring, int lane) {
+  Sink<RW> o;
+  o.rs = __builtin_amdgcn_make_buffer_rsrc(block, 0, (int)(4u * kLanes * (uint32_t)swb), kBufRsrcWord3);
+  o.base = ring + 4u * (uint32_t)lane;
+  o.sa = 7u * 256u;
+  o.fnext = 12u * 256u;
+  o.uoff = 16u * (uint32_t)lane;
+  return o;
+}
+
+// LDS of the encode kernels, all dynamic so that it starts at address 0: the
+// waves' rings first (each aligned to its size), then the kernel's table
+extern __shared__ __attribute__((aligned(16))) uint8_t enc_lds[];
 
 // --- general steps: every case, used for the rare symbols and the flush ----
 
 // a carry reached an all-ones run: it wraps to zeros, W + 1 and all but the
 // last zero word are final, the last zero word stays open
-__device__ __forceinline__ void carry_into_run(RcEnc& e, Sink& o) {
+template <class S>
+__device__ __forceinline__ void carry_into_run(RcEnc& e, S& o) {
   emit_word(o, e.W + 1u);
   for (uint32_t j = 1; j < e.P; j++) emit_word(o, 0u);
   e.W = 0;
@@ -56,7 +134,8 @@ __device__ __forceinline__ void carry_into_run(RcEnc& e, Sink& o) {
 
 // the carry out of the held bytes after an addition to L: into W, or through
 // an all-ones run
-__device__ __forceinline__ void settle_carry(RcEnc& e, Sink& o) {
+template <class S>
+__device__ __forceinline__ void settle_carry(RcEnc& e, S& o) {
   const uint32_t hmask = (1u << e.kh) - 1u;
   uint32_t hi = (uint32_t)(e.L >> 32);
   const bool c = hi > hmask;
@@ -71,7 +150,8 @@ __device__ __forceinline__ void settle_carry(RcEnc& e, Sink& o) {
 
 // shift nb8 / 8 (0..2) bytes out of the window; a word leaves when four are
 // held after the shift: it is the four top bytes of L before it
-__device__ __forceinline__ void shift_bytes(RcEnc& e, uint32_t nb8, Sink& o) {
+template <class S>
+__device__ __forceinline__ void shift_bytes(RcEnc& e, uint32_t nb8, S& o) {
   const uint32_t lo = (uint32_t)e.L, hi = (uint32_t)(e.L >> 32);
   const uint32_t kh2 = e.kh + nb8;
   const bool ext = kh2 >= 32u;
@@ -99,7 +179,8 @@ __device__ __forceinline__ void shift_bytes(RcEnc& e, uint32_t nb8, Sink& o) {
 // its kh carries bit 6, so kh + nb8 >= 32 (shifts and bit-field widths read
 // only the low five bits of kh), and its Y is 0, so wn >= Y; then "a word
 // leaves and it is all ones, or a run is open" is one compare pair.
-__device__ __forceinline__ void rc_put(RcEnc& e, uint32_t c0, uint32_t freq, Sink& o) {
+template <class S>
+__device__ __forceinline__ void rc_put(RcEnc& e, uint32_t c0, uint32_t freq, S& o) {
   const RcEnc e0 = e;
   const uint32_t r = e.range >> kProbBits;
   const uint64_t L1 = e.L + (uint64_t)r * c0;  // one 32 x 32 -> 64 multiply-add
@@ -120,11 +201,7 @@ __device__ __forceinline__ void rc_put(RcEnc& e, uint32_t c0, uint32_t freq, Sin
   const bool rare = __builtin_amdgcn_inverse_ballot_w64(m_ext & m_ge);
   const uint32_t W1 = e.W + cy;
   const bool emit = __builtin_amdgcn_inverse_ballot_w64(m_ext & ~m_ge);
-  if (emit) {
-    __builtin_amdgcn_raw_buffer_store_b32(W1, o.rs, o.woff, 0, 0);
-    // the slot after it (in place, after the store has read the old offset)
-    asm("v_add_u32 %0, 0x100, %0" : "+v"(o.woff));
-  }
+  if (emit) stage_word(o, W1);
   e.W = emit ? wn : W1;
   // shifted by nb8, L keeps its low 32 + (kh2 mod 32) bits: without a word
   // leaving that is all of it less the carry; with one, the window's low kh
@@ -149,7 +226,8 @@ __device__ __forceinline__ void rc_put(RcEnc& e, uint32_t c0, uint32_t freq, Sin
 // Flush: the fewest bytes (one or two) that name an aligned block inside
 // [low, low + range), so the stream decodes whatever bytes follow it; then the
 // open words and the bytes still held, the last word padded with zero bytes.
-__device__ __forceinline__ void rc_finish(RcEnc& e, Sink& o) {
+template <class S>
+__device__ __forceinline__ void rc_finish(RcEnc& e, S& o) {
   e.kh &= 31u;
   const uint64_t win = e.L & 0xFFFFFFFFull;
   uint32_t nb8 = 8;
@@ -188,9 +266,13 @@ __device__ __forceinline__ uint32_t ld_half(__amdgpu_buffer_rsrc_t r, uint32_t l
 // GS: group size fixed at compile time (0 = the runtime a.G only).  With GS,
 // the input of full groups is loaded two groups ahead, so the wait for it
 // never includes the stores issued since (every group issues the same loads).
-template <int GS>
+// RW: ring words per lane (8 where the launch's workgroups fit a compute unit
+// with them, else 4); the ring of RW words holds RW - 3 staged words beyond a
+// partial unit, so the delta loop flushes every 3 symbols with 8 and every
+// symbol with 4.
+template <int GS, int RW>
 __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) {
-  __shared__ uint16_t tab[kImgRows * kLanes];
+  uint16_t* tab = reinterpret_cast<uint16_t*>(enc_lds + (size_t)a.waves * RW * 256u);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int per_grp = a.nrows * a.nblk;
   const int grp = blockIdx.x / per_grp, unit = blockIdx.x % per_grp;
@@ -207,7 +289,9 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
   const int rrel = prow >= half ? half + (a.nrows - 1 - prow) : prow;  // row within the launch's range
   const int row = a.row0 + rrel;  // kv * L + l
   const int cb = (pcb + 5 * ((prow * a.nblk) / a.ncu)) % a.nblk;
-  const EncGroup eg = a.groups[grp];
+  // (the group's blob indices read from the arguments, not copied to a local
+  // array: indexing that by wave would take it through private memory)
+  const EncGroup& eg = a.groups[grp];
   {
     const uint32_t* src = reinterpret_cast<const uint32_t*>(
         a.b[eg.blob[0]].img + ((size_t)row * a.nblk + cb) * kImgRows * kLanes);
@@ -233,14 +317,9 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
       (void*)((kv ? a.v : a.k) + ((size_t)l * a.T + B.t0) * a.C), 0,
       (int)((uint32_t)B.tc * row_bytes), kBufRsrcWord3);
   const uint32_t lane_off = 2u * (uint32_t)c;
-  // the wave's block of 64 streams in scratch, [swb rows][64 lanes], row 0
-  // holding the placeholders
-  Sink o;
+  // the wave's block of 64 streams in scratch, swb words each, as 16-byte units
   const size_t block = (size_t)rrel * a.nblk + cb;
-  o.rs = __builtin_amdgcn_make_buffer_rsrc(B.scratch + block * kLanes * a.swb, 0,
-                                           (int)(kRowBytes * (uint32_t)a.swb), kBufRsrcWord3);
-  o.woff = 4u * (uint32_t)lane;
-  const uint32_t woff0 = o.woff + kRowBytes;  // the stream's first word
+  Sink<RW> o = make_sink<RW>(B.scratch + block * kLanes * a.swb, a.swb, (uint32_t)wave * RW * 256u, lane);
   // raw anchors into the blob, [ng][C] for this (kv, layer): the lane's
   // channel is the vector offset, the group a scalar offset; coded anchors are
   // coded from the input by k_anchor_encode instead (a wave-uniform choice)
@@ -272,6 +351,8 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
       const uint32_t c0 = *reinterpret_cast<const uint16_t*>(tab8 + off);
       const uint32_t c1 = *reinterpret_cast<const uint16_t*>(tab8 + off + 2 * kLanes);
       rc_put(e, c0, c1 - c0, o);
+      // the common step stages at most one word
+      if (RW == 4 || j % 3 == 0 || j == n - 1) flush_units(o);
     }
   };
 
@@ -316,9 +397,12 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
     code_group(g, min(a.G, B.tc - ta),
                [&](int j) { return ld_half(xin, lane_off, (uint32_t)(ta + j) * row_bytes); });
   }
-  if (B.tc > B.ng) rc_finish(e, o);  // a stream without symbols stays empty
+  if (B.tc > B.ng) {  // a stream without symbols stays empty
+    rc_finish(e, o);
+    flush_tail(o);
+  }
   if (!(nfacc == 0.0f)) atomicOr(&B.status[2], 1u);
-  const uint32_t nwords = o.woff > woff0 ? (o.woff - woff0) / kRowBytes : 0u;
+  const uint32_t nwords = sink_words(o);
   B.lens[(size_t)rrel * a.C + c] = nwords;
   reinterpret_cast<uint16_t*>(B.blob + B.lay.off_len)[pi] = (uint16_t)nwords;
 }
@@ -331,8 +415,9 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_encode(EncodeArgs a) 
 // blog, section 2.1: the quantised anchor, then arithmetic coding), into the
 // same per-block scratch layout as the delta streams, so the same kernels pack
 // them.  Non-finite input is flagged by k_encode, which reads every token.
+template <int RW>
 __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_anchor_encode(EncodeArgs a) {
-  __shared__ uint32_t cum[kASym + 1];
+  uint32_t* cum = reinterpret_cast<uint32_t*>(enc_lds + (size_t)a.waves * RW * 256u);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int per_grp = a.nrows * a.nblk;
   const int grp = blockIdx.x / per_grp, unit = blockIdx.x % per_grp;
@@ -356,7 +441,7 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_anchor_encode(EncodeA
     if (lane == 63) cum[kASym] = incl;
   }
   __syncthreads();
-  const EncGroup eg = a.groups[grp];
+  const EncGroup& eg = a.groups[grp];
   const int bi = __builtin_amdgcn_readfirstlane(eg.blob[wave]);
   if (bi < 0) return;
   const EncBlob& B = a.b[bi];
@@ -371,12 +456,8 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_anchor_encode(EncodeA
       (void*)((kv ? a.v : a.k) + ((size_t)l * a.T + B.t0) * a.C), 0,
       (int)((uint32_t)B.tc * row_bytes), kBufRsrcWord3);
   const uint32_t lane_off = 2u * (uint32_t)c;
-  Sink o;
   const size_t block = (size_t)rrel * a.nblk + cb;
-  o.rs = __builtin_amdgcn_make_buffer_rsrc(B.scratch + block * kLanes * a.swb, 0,
-                                           (int)(kRowBytes * (uint32_t)a.swb), kBufRsrcWord3);
-  o.woff = 4u * (uint32_t)lane;
-  const uint32_t woff0 = o.woff + kRowBytes;
+  Sink<RW> o = make_sink<RW>(B.scratch + block * kLanes * a.swb, a.swb, (uint32_t)wave * RW * 256u, lane);
   RcEnc e = {0, 0u, 0xFFFFFFFFu, 0u, 0u, 0xFFFFFFFFu};
   const uint32_t gstep = (uint32_t)a.G * row_bytes;
   // anchor tokens in batches of kAB, loaded one batch ahead (a batch past the
@@ -394,6 +475,7 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_anchor_encode(EncodeA
       const uint32_t s = (uint32_t)(quant_anchor(half_bits_to_float(x[j]), inv_a) + 128);
       const uint32_t c0 = cum[s];
       rc_put(e, c0, cum[s + 1] - c0, o);
+      flush_units(o);
     }
   };
   load(xa, 0);
@@ -405,7 +487,8 @@ __global__ __launch_bounds__(kLanes * kEncMaxWaves) void k_anchor_encode(EncodeA
     load(xb, g0 + 3 * kAB);
   }
   rc_finish(e, o);  // every chunk has at least one group
-  const uint32_t nwords = (o.woff - woff0) / kRowBytes;
+  flush_tail(o);
+  const uint32_t nwords = sink_words(o);
   B.lens[(size_t)rrel * a.C + c] = nwords;
   reinterpret_cast<uint16_t*>(B.blob + B.lay.off_len)[(size_t)(a.row0 + rrel) * a.C + c] =
       (uint16_t)nwords;
@@ -497,15 +580,13 @@ __global__ __launch_bounds__(256) void k_row_scan(EncodeArgs a) {
 // row's offset plus the words of the row's earlier blocks; m = the fewest
 // whole 16-byte units any of its streams has; units 0 .. m-1 of its ns streams
 // first, unit by unit (unit u of stream j at word 4 (u ns + j)), then every
-// stream's remaining words, stream after stream.  The block's words are
-// [row][lane] in scratch (row 0 the placeholders): a unit of all streams is
-// four scratch rows, transposed through LDS into one contiguous run of 4 ns
-// words; the tails are read a row at a time (the lanes are the streams).
-constexpr int kPackPitch = kLanes + 1;
+// stream's remaining words, stream after stream.  The block's words are in
+// scratch as [unit][lane][4 words] already, so unit u of all its streams is one
+// contiguous 16 ns-byte run there as in the payload; the tails are read a word
+// at a time (the lanes are the streams).
 __global__ __launch_bounds__(256) void k_pack(EncodeArgs a) {
   const EncBlob& B = a.b[blockIdx.y];
   if (B.status[1]) return;
-  __shared__ uint32_t tile[4 * kPackPitch];
   __shared__ uint32_t toff[kLanes], slen[kLanes];
   __shared__ uint32_t s_base, s_units, s_maxlen;
   const int rrel = blockIdx.x / a.nblk, cb = blockIdx.x % a.nblk;
@@ -540,19 +621,21 @@ __global__ __launch_bounds__(256) void k_pack(EncodeArgs a) {
     }
   }
   __syncthreads();
-  const uint32_t* src = B.scratch + ((size_t)rrel * a.nblk + cb) * kLanes * a.swb + kLanes;  // row 1
+  // the block's scratch: unit u of stream j (its words 4u .. 4u + 3) is the
+  // 16 bytes at word 4 (64 u + j)
+  const uint32_t* src = B.scratch + ((size_t)rrel * a.nblk + cb) * kLanes * a.swb;
   uint32_t* pay = reinterpret_cast<uint32_t*>(B.blob + B.lay.off_pay) + s_base;
   const uint32_t m = s_units, mx = s_maxlen;
-  // interleaved units: scratch rows 4u .. 4u + 3 (wave w takes row 4u + w)
-  for (uint32_t u = 0; u < m; u++) {
-    if (lane < ns) tile[wave * kPackPitch + lane] = src[(size_t)(4u * u + wave) * kLanes + lane];
-    __syncthreads();
-    if (tid < 4 * ns) pay[4u * u * (uint32_t)ns + tid] = tile[(tid & 3) * kPackPitch + (tid >> 2)];
-    __syncthreads();
-  }
-  // tails: stream j's words 4m .. len_j - 1, one scratch row at a time
+  typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
+  // interleaved units: wave w copies unit u = w, w + 4, ... of every stream
+  if (lane < ns)
+    for (uint32_t u = (uint32_t)wave; u < m; u += 4u)
+      *reinterpret_cast<u32x4a*>(pay + 4u * (u * (uint32_t)ns + (uint32_t)lane)) =
+          *reinterpret_cast<const u32x4a*>(src + 4u * (u * kLanes + (uint32_t)lane));
+  // tails: stream j's words 4m .. len_j - 1
   for (uint32_t k = 4u * m + (uint32_t)wave; k < mx; k += 4u)
-    if (lane < ns && k < slen[lane]) pay[toff[lane] + (k - 4u * m)] = src[(size_t)k * kLanes + lane];
+    if (lane < ns && k < slen[lane])
+      pay[toff[lane] + (k - 4u * m)] = src[4u * ((k >> 2) * kLanes + (uint32_t)lane) + (k & 3u)];
 }
 
 }  // namespace
@@ -560,12 +643,23 @@ __global__ __launch_bounds__(256) void k_pack(EncodeArgs a) {
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t st) {
   const unsigned nb = (unsigned)a.nblobs;
   const unsigned blocks = (unsigned)(a.n_groups * a.nrows * a.nblk);
-  if (a.row0 >= 2 * a.L)
-    k_anchor_encode<<<blocks, kLanes * a.waves, 0, st>>>(a);
-  else if (a.G == 10)
-    k_encode<10><<<blocks, kLanes * a.waves, 0, st>>>(a);
-  else
-    k_encode<0><<<blocks, kLanes * a.waves, 0, st>>>(a);
+  // rings of 8 words where the launch's workgroups still fit their compute
+  // units at once with them, else of 4
+  const bool anc = a.row0 >= 2 * a.L;
+  const size_t fixed = anc ? 4u * (kASym + 1) : 2u * kImgRows * kLanes;
+  const size_t per_cu = (blocks + (unsigned)a.ncu - 1) / (unsigned)a.ncu;
+  const bool r8 = per_cu * (fixed + (size_t)a.waves * 8u * 256u) <= (size_t)a.lds_cu;
+  const size_t lds = fixed + (size_t)a.waves * (r8 ? 8u : 4u) * 256u;
+  if (anc) {
+    if (r8) k_anchor_encode<8><<<blocks, kLanes * a.waves, lds, st>>>(a);
+    else k_anchor_encode<4><<<blocks, kLanes * a.waves, lds, st>>>(a);
+  } else if (a.G == 10) {
+    if (r8) k_encode<10, 8><<<blocks, kLanes * a.waves, lds, st>>>(a);
+    else k_encode<10, 4><<<blocks, kLanes * a.waves, lds, st>>>(a);
+  } else {
+    if (r8) k_encode<0, 8><<<blocks, kLanes * a.waves, lds, st>>>(a);
+    else k_encode<0, 4><<<blocks, kLanes * a.waves, lds, st>>>(a);
+  }
   k_row_totals<<<dim3(a.nrows, nb), 256, 0, st>>>(a);
   k_row_scan<<<nb, 256, 0, st>>>(a);
   k_pack<<<dim3(a.nrows * a.nblk, nb), 256, 0, st>>>(a);
