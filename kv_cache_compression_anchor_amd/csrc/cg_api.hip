@@ -787,7 +787,30 @@ int cg_encode_batch(const cg_tables* ch, const void* k_dev, const void* v_dev, i
       1, std::min<size_t>({(size_t)kEncMaxBlobs, (size_t)n, kEncScratchBudget / (4 * slot_words)}));
   const size_t fit = std::max<size_t>(1, std::min(budget, cap / wpb));
   const bool one_round = (n + fit - 1) / fit <= (n + budget - 1) / budget + 1;
-  const int slots = (int)(one_round ? fit : budget);
+  int slots = (int)(one_round ? fit : budget);
+  // The encoder stages its output in rings of 8 words per lane, 2 KB a wave of
+  // LDS beside the workgroup's 8 KB table, where all the launch's workgroups
+  // fit their compute units with them (else it takes 4-word rings and checks
+  // for complete units every symbol).  When they would not with `slots` blobs
+  // but would with a smaller multiple of 4 (whole groups of one quality), take
+  // that.
+  {
+    int cus = 0, lds = 0;
+    if (slots > 4 && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->dev) == hipSuccess &&
+        hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, h->dev) == hipSuccess &&
+        cus > 0 && lds > 0) {
+      auto fits8 = [&](size_t b) {
+        const size_t wgs = (b + 3) / 4 * 2 * (size_t)t.L * t.nblk;
+        const size_t per_wg = 2u * kImgRows * kLanes + std::min<size_t>(4, b) * 8u * 256u;
+        return (wgs + (size_t)cus - 1) / (size_t)cus * per_wg <= (size_t)lds;
+      };
+      if (!fits8((size_t)slots)) {
+        size_t b = (size_t)slots / 4 * 4;
+        while (b >= 4 && !fits8(b)) b -= 4;
+        if (b >= 4) slots = (int)b;
+      }
+    }
+  }
   const size_t row_words_per_slot = (size_t)2 * t.L * (1 + t.nblk);
   if ((rc = reserve_dev(&ws->scratch, &ws->scratch_bytes, 4 * slot_words * slots)) ||
       (rc = reserve_dev(&ws->lens, &ws->lens_bytes, 4 * t.lay.n * slots)) ||
