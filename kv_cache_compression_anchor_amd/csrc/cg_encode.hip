@@ -2,8 +2,9 @@
 // of the other tokens of the group against it, layer-group step, arithmetic
 // coding).  One lane per stream (kv, layer, channel): a wave codes 64 channels
 // of one (kv, layer) row in lockstep, so every input row it reads is one
-// coalesced 128-byte segment.  Streams land in per-stream scratch, then a
-// wavefront prefix sum over the stream lengths packs them into the blob.
+// coalesced 128-byte segment.  Streams land in per-stream scratch, 16 bytes at
+// a time, then a wavefront prefix sum over the stream lengths packs them into
+// the blob.
 #include "cg_build.h"
 
 namespace cg {
@@ -17,7 +18,8 @@ namespace {
 // 0xFFFFFFFF words after it (`P`) stay open until no carry can reach them.
 // `W` always has a slot: before the first word is taken it is a placeholder
 // word in front of the stream, which the first emission fills and nothing reads
-// (no carry can reach past the first word).
+// (no carry can reach past the first word; it stays in the staging ring below
+// and is never written out).
 struct RcEnc {
   uint64_t L;      // window (bits 0..31) and the bytes above it (bits 32..32+kh-1)
   uint32_t kh;     // 8 * bytes above the window: 0..24; plus 64 while P != 0
